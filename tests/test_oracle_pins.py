@@ -1,0 +1,436 @@
+"""Pins that hold the float64 oracle to things other than itself: values the
+pages print, closed forms, invariants the pages state, pure-Python brute force
+on tiny inputs and central finite differences. CPU only."""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.ce import MEAN, SUM
+from synth import bf16_bits_from_f32, make_ce_inputs, config_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *rest = line.split()
+            vals[key] = [float(r) for r in rest]
+    return vals
+
+
+# ---------------------------------------------------------------- bits
+
+def test_decode_bf16_exact():
+    bits = np.array([0x3F80, 0xC000, 0x3E80, 0x0001, 0x7F80, 0x8000, 0x4049], dtype=np.uint16)
+    want = [1.0, -2.0, 0.25, 2.0 ** -133, math.inf, -0.0, 3.140625]
+    got = oracle.decode(bits, "bf16")
+    for g, w in zip(got, want):
+        assert g == w and math.copysign(1, g) == math.copysign(1, w)
+
+
+def test_generator_bf16_round_to_nearest_even():
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -1 - 2 ** -8, 1 + 2 ** -8 + 2 ** -20,
+                  np.nan], dtype=np.float32)
+    b = bf16_bits_from_f32(x)
+    assert list(b[:5]) == [0x3F80, 0x3F80, 0x3F82, 0xBF80, 0x3F81]
+    assert (b[5] & 0x7F80) == 0x7F80 and (b[5] & 0x7F) != 0
+
+
+# ---------------------------------------------------------------- geometry
+
+def test_geometry_boundaries():
+    ids = [0, 255, 256, 511, 512, 767, 768, 999, 1000, 1023, 1024, -1, -100]
+    own, loc = oracle.owner_and_local(ids, 1000, 1024, 4)
+    assert list(own) == [0, 0, 1, 1, 2, 2, 3, 3, -1, -1, -1, -1, -1]
+    assert list(loc) == [0, 255, 0, 255, 0, 255, 0, 231, 0, 0, 0, 0, 0]
+
+
+@pytest.mark.parametrize("V_real,V_pad,n", [(1000, 1024, 4), (50000, 50016, 8), (5, 8, 8),
+                                             (7, 8, 2), (24, 24, 3)])
+def test_geometry_exhaustive(V_real, V_pad, n):
+    ids = np.arange(-5, V_pad + 5)
+    own, loc = oracle.owner_and_local(ids, V_real, V_pad, n)
+    S = V_pad // n
+    for i, o, l in zip(ids, own, loc):
+        owners = [k for k in range(n) if k * S <= i < min((k + 1) * S, V_real)]
+        if 0 <= i < V_real:
+            assert owners == [o] and o * S + l == i and 0 <= l < S
+        else:
+            assert owners == [] and o == -1
+
+
+def test_geometry_rejects_uneven():
+    with pytest.raises(ValueError):
+        oracle.shard_size(1000, 3)
+
+
+# ---------------------------------------------------------------- embedding
+
+def test_gather_masked_sum_equals_direct():
+    inp = config_inputs("c1")
+    W = oracle.decode(inp.W, inp.dtype)
+    ids = np.concatenate([inp.ids, np.array([-1, 1000, 1023, 1024, 255, 256, 0, 999])])
+    a = oracle.gather_direct(ids, W, inp.V_real)
+    b = oracle.gather_masked_shards(ids, W, inp.V_real, inp.V_pad, inp.num_shards)
+    assert np.array_equal(a, b)
+    # every valid ID reproduces its own row; invalid IDs give zero rows
+    for t, i in enumerate(ids):
+        if 0 <= i < inp.V_real:
+            assert np.array_equal(a[t], W[i])
+        else:
+            assert not a[t].any()
+
+
+def test_gather_edge_ids():
+    W = np.arange(8 * 3, dtype=np.float64).reshape(8, 3) + 1.0
+    ids = [-(2 ** 31), -1, 0, 4, 5, 7, 8, 2 ** 31 - 1]
+    out = oracle.gather_direct(ids, W, 5)
+    assert np.array_equal(out[2], W[0]) and np.array_equal(out[3], W[4])
+    assert not out[[0, 1, 4, 5, 6, 7]].any()
+
+
+def test_scatter_add_bruteforce():
+    rng = np.random.default_rng(7)
+    V_real, V_pad, H = 11, 12, 5
+    ids = np.array([3, 3, 0, 10, 11, -1, 3, 12, 5, 0, 10, 7], dtype=np.int64)
+    dout = rng.standard_normal((ids.shape[0], H))
+    dW, count = oracle.scatter_add(ids, dout, V_real, V_pad)
+    want = [[0.0] * H for _ in range(V_pad)]
+    cnt = [0] * V_pad
+    for t, i in enumerate(ids):
+        if 0 <= i < V_real:
+            cnt[i] += 1
+            for j in range(H):
+                want[i][j] += float(dout[t, j])
+    assert list(count) == cnt
+    assert np.allclose(dW, np.array(want), rtol=0, atol=1e-15)
+    assert not dW[V_real:].any()
+
+
+# ---------------------------------------------------------------- CE forward
+
+def test_target_status_cases():
+    v, i, b = oracle.target_status([-100, -1, 0, 4, 5, 7, 2 ** 31 - 1], 5, -100)
+    assert list(v) == [False, False, True, True, False, False, False]
+    assert list(i) == [True, False, False, False, False, False, False]
+    assert list(b) == [False, True, False, False, True, True, True]
+
+
+def _bruteforce_ce(h, W, y, V_real, ignore_index, grad_loss, reduction):
+    """Pure-Python reference: math.fsum over explicit loops."""
+    T, H = len(h), len(h[0])
+    z = [[math.fsum(h[t][j] * W[v][j] for j in range(H)) for v in range(V_real)]
+         for t in range(T)]
+    lse = []
+    for t in range(T):
+        m = max(z[t])
+        lse.append(m + math.log(math.fsum(math.exp(zv - m) for zv in z[t])))
+    valid = [0 <= y[t] < V_real for t in range(T)]
+    loss = [lse[t] - z[t][y[t]] if valid[t] else 0.0 for t in range(T)]
+    nv = sum(valid)
+    scale = grad_loss / max(nv, 1) if reduction == MEAN else grad_loss
+    G = [[(math.exp(z[t][v] - lse[t]) - (1.0 if v == y[t] else 0.0)) * scale if valid[t] else 0.0
+          for v in range(V_real)] for t in range(T)]
+    dh = [[math.fsum(G[t][v] * W[v][j] for v in range(V_real)) for j in range(H)] for t in range(T)]
+    dW = [[math.fsum(G[t][v] * h[t][j] for t in range(T)) for j in range(H)] for v in range(V_real)]
+    return lse, loss, nv, dh, dW
+
+
+@pytest.mark.parametrize("V_real,V_pad,n", [(1, 2, 2), (3, 4, 4), (7, 8, 2), (9, 12, 3),
+                                             (16, 16, 1), (13, 16, 8)])
+def test_bruteforce_tiny(V_real, V_pad, n):
+    rng = np.random.default_rng(V_real * 100 + V_pad)
+    T, H = 6, 3
+    h = rng.standard_normal((T, H))
+    W = rng.standard_normal((V_pad, H))
+    W[V_real:] = np.nan                      # padded rows must never be read
+    y = rng.integers(0, V_real, T)
+    y[1] = -100
+    y[4] = V_real + (V_pad - V_real) // 2     # a padded row: bad target
+    for red in (MEAN, SUM):
+        r = oracle.cross_entropy(h, W, y, V_real, V_pad, n, -100, 0.7, red)
+        lse, loss, nv, dh, dW = _bruteforce_ce(h.tolist(), W.tolist(), y.tolist(), V_real,
+                                               -100, 0.7, red)
+        assert np.allclose(r["lse"], lse, rtol=1e-13, atol=1e-13)
+        assert np.allclose(r["loss"], loss, rtol=1e-13, atol=1e-13)
+        assert r["n_valid"] == nv and r["n_bad"] == 1
+        assert np.allclose(r["dh"], dh, rtol=1e-12, atol=1e-13)
+        assert np.allclose(r["dW"][:V_real], dW, rtol=1e-12, atol=1e-13)
+        assert not r["dW"][V_real:].any()
+
+
+def test_binomial_page_numbers():
+    g = _golden("binomial_softmax.txt")
+    w = g["weights"]
+    denom = g["denominator"][0]
+    assert sum(w) == denom
+    V_real, V_pad = 5, 8
+    W = np.zeros((V_pad, 1))
+    W[:5, 0] = [math.log(math.comb(4, k)) for k in range(5)]
+    for garbage in (8.0, np.nan, np.inf):
+        W[5:, 0] = garbage
+        h = np.ones((5, 1))
+        y = np.array([0, 1, 2, 3, 4])
+        for n in (1, 2, 4, 8):
+            r = oracle.cross_entropy(h, W, y, V_real, V_pad, n, -100, 1.0, SUM)
+            assert np.allclose(r["lse"], math.log(denom), rtol=0, atol=1e-14)
+            # loss of target k is -log(w_k / 16)
+            assert np.allclose(r["loss"], [-math.log(wk / denom) for wk in w], atol=1e-14)
+            # the gradient row of token t is p - onehot(t)
+            p = np.array(w) / denom
+            G = np.tile(p, (5, 1)) - np.eye(5)
+            assert np.allclose(r["dh"][:, 0], (G * W[:5, 0]).sum(axis=1), atol=1e-14)
+            m, s = r["shard_m"], r["shard_s"]
+            assert np.allclose(oracle.merge_shard_stats(m, s), math.log(denom), atol=1e-14)
+
+
+def test_padded_mass_page_demo():
+    g = _golden("padded_mass.txt")
+    V_real, V_pad = int(g["V_real"][0]), int(g["V_pad"][0])
+    rng = np.random.default_rng(3)
+    row = rng.standard_normal(V_pad)
+    row[V_real:] = g["pad_logit"][0]
+    # W = identity so that the logits of h = row are row itself
+    W = np.eye(V_pad)
+    h = row[None, :]
+    f = oracle.ce_forward(h, W, np.array([0]), V_real, V_pad, 1)
+    p_real = np.exp(row[:V_real] - f["lse"][0])
+    assert abs(p_real.sum() - g["masked_real_mass"][0]) < 1e-14
+    # without the mask the padded columns take almost all the mass
+    lse_unmasked = oracle.lse_rows(row[None, :])[0]
+    assert np.exp(row[:V_real] - lse_unmasked).sum() < g["unmasked_real_mass_below"][0]
+
+
+def test_lse_closed_forms():
+    # h = 0 gives equal logits over the real rows: lse = ln V_real exactly,
+    # and the gradient row is 1/V_real - onehot
+    V_real, V_pad, H = 1000, 1024, 64
+    rng = np.random.default_rng(11)
+    W = rng.standard_normal((V_pad, H)) * 0.02
+    W[V_real:] = 8.0
+    h = np.zeros((3, H))
+    y = np.array([5, 999, -100])
+    r = oracle.cross_entropy(h, W, y, V_real, V_pad, 4, -100, 1.0, SUM)
+    assert np.allclose(r["lse"], math.log(V_real), rtol=0, atol=1e-12)
+    assert abs(math.log(V_real) - math.log(V_pad)) > 0.02
+    # dW row v = sum_t G[t, v] h[t] = 0 since h = 0; dh[t] = sum_v (1/V - [v=y]) W[v]
+    want = W[:V_real].mean(axis=0) - W[5]
+    assert np.allclose(r["dh"][0], want, atol=1e-15)
+    assert not r["dh"][2].any()
+
+
+def test_max_shift_large_logits():
+    # logits of +-1000 overflow exp() without the shift; with it the
+    # normaliser is exactly 1000 + ln 2 when two logits share the top value
+    V_real, V_pad = 10, 16
+    W = np.zeros((V_pad, 2))
+    W[0] = [1000.0, 0.0]
+    W[1] = [1000.0, 0.0]
+    W[2] = [-1000.0, 0.0]
+    W[3:V_real] = [0.0, 1.0]
+    h = np.array([[1.0, 0.0]])
+    with np.errstate(over="ignore"):
+        assert not np.isfinite(np.log(np.exp(h @ W[:V_real].T).sum()))
+    f = oracle.ce_forward(h, W, np.array([0]), V_real, V_pad, 2)
+    assert abs(f["lse"][0] - (1000.0 + math.log(2.0))) < 1e-12
+    assert abs(f["loss"][0] - math.log(2.0)) < 1e-12
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8])
+def test_sharded_lse_equals_unsharded(n):
+    inp = config_inputs("c1")
+    h = oracle.decode(inp.h, inp.dtype)
+    W = oracle.decode(inp.W, inp.dtype)
+    z = oracle.logits(h, W, inp.V_real) * 40.0    # spread the logits out
+    ref = oracle.lse_rows(z)
+    a = oracle.lse_two_phase(z, inp.V_real, inp.V_pad, n)
+    m, s = oracle.shard_stats(z, inp.V_real, inp.V_pad, n)
+    b = oracle.merge_shard_stats(m, s)
+    assert np.allclose(a, ref, rtol=1e-12, atol=0)
+    assert np.allclose(b, ref, rtol=1e-12, atol=0)
+
+
+def test_empty_shard_stats():
+    # V_real = 5 of V_pad = 8 over 8 shards: shards 5..7 own no real row
+    z = np.arange(10, dtype=np.float64).reshape(2, 5)
+    m, s = oracle.shard_stats(z, 5, 8, 8)
+    assert np.all(m[5:] == -np.inf) and not s[5:].any()
+    assert np.allclose(oracle.merge_shard_stats(m, s), oracle.lse_rows(z), rtol=1e-14)
+
+
+def test_local_softmax_negative_control():
+    # a planted mistake: each shard normalises over its own rows only.
+    # The parity tolerance of the bf16 path (2e-3 relative on the loss) must reject it.
+    inp = config_inputs("c1")
+    h = oracle.decode(inp.h, inp.dtype)
+    W = oracle.decode(inp.W, inp.dtype)
+    f = oracle.ce_forward(h, W, inp.targets, inp.V_real, inp.V_pad, inp.num_shards)
+    S = inp.S
+    z = oracle.logits(h, W, inp.V_real)
+    wrong = 0.0
+    for t, y in enumerate(inp.targets):
+        if f["valid"][t]:
+            k = y // S
+            zk = z[t, k * S:min((k + 1) * S, inp.V_real)]
+            wrong += oracle.lse_rows(zk[None, :])[0] - z[t, y]
+    assert abs(wrong - f["loss_sum"]) / f["loss_sum"] > 2e-3
+
+
+def test_padded_rows_do_not_matter():
+    inp = make_ce_inputs(16, 8, 37, 40, 4, "f32", seed=5, ignore_frac=0.2)
+    h = oracle.decode(inp.h, "f32")
+    base = oracle.decode(inp.W, "f32")
+    outs = []
+    for fill in (0.0, 8.0, np.nan, -np.inf):
+        W = base.copy()
+        W[37:] = fill
+        outs.append(oracle.cross_entropy(h, W, inp.targets, 37, 40, 4))
+    for o in outs[1:]:
+        for key in ("lse", "loss", "dh", "dW"):
+            assert np.array_equal(o[key], outs[0][key])
+        assert not o["dW"][37:].any()
+
+
+# ---------------------------------------------------------------- CE backward
+
+def _loss_mean(h, W, y, V_real, V_pad, n):
+    f = oracle.ce_forward(h, W, y, V_real, V_pad, n)
+    return f["loss_sum"] / max(f["n_valid"], 1)
+
+
+def test_gradient_finite_difference():
+    rng = np.random.default_rng(1)
+    T, H, V_real, V_pad, n = 3, 4, 7, 8, 2
+    h = rng.standard_normal((T, H))
+    W = rng.standard_normal((V_pad, H))
+    y = np.array([6, -100, 3])
+    r = oracle.cross_entropy(h, W, y, V_real, V_pad, n)
+    eps = 1e-6
+    for t in range(T):
+        for j in range(H):
+            hp, hm = h.copy(), h.copy()
+            hp[t, j] += eps
+            hm[t, j] -= eps
+            num = (_loss_mean(hp, W, y, V_real, V_pad, n) - _loss_mean(hm, W, y, V_real, V_pad, n)) / (2 * eps)
+            assert abs(num - r["dh"][t, j]) < 1e-8
+    for v in range(V_pad):
+        for j in range(H):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[v, j] += eps
+            Wm[v, j] -= eps
+            num = (_loss_mean(h, Wp, y, V_real, V_pad, n) - _loss_mean(h, Wm, y, V_real, V_pad, n)) / (2 * eps)
+            assert abs(num - r["dW"][v, j]) < 1e-8
+    assert not r["dh"][1].any()
+
+
+def test_gradient_rows_sum_to_zero():
+    inp = config_inputs("c1")
+    h = oracle.decode(inp.h, inp.dtype)
+    W = oracle.decode(inp.W, inp.dtype)
+    r = oracle.cross_entropy(h, W, inp.targets, inp.V_real, inp.V_pad, inp.num_shards)
+    # each G row sums to zero, so the dW rows sum to zero
+    assert np.abs(r["dW"].sum(axis=0)).max() < 1e-12
+    assert not r["dW"][inp.V_real:].any()
+    ign = ~r["valid"]
+    assert ign.any() and not r["dh"][ign].any()
+    assert r["n_valid"] == int(np.sum((inp.targets >= 0) & (inp.targets < inp.V_real)))
+
+
+def test_mean_normalised_once_and_no_valid_tokens():
+    inp = make_ce_inputs(8, 8, 20, 24, 2, "f32", seed=2)
+    h = oracle.decode(inp.h, "f32")
+    W = oracle.decode(inp.W, "f32")
+    r_sum = oracle.cross_entropy(h, W, inp.targets, 20, 24, 2, grad_loss=1.0, reduction=SUM)
+    r_mean = oracle.cross_entropy(h, W, inp.targets, 20, 24, 2, grad_loss=1.0, reduction=MEAN)
+    assert r_mean["loss_reduced"] == pytest.approx(r_sum["loss_sum"] / 8, rel=1e-15)
+    assert np.allclose(r_mean["dh"] * 8, r_sum["dh"], rtol=1e-13, atol=1e-15)
+    none = np.full(8, -100)
+    r0 = oracle.cross_entropy(h, W, none, 20, 24, 2)
+    assert r0["loss_reduced"] == 0.0 and r0["n_valid"] == 0
+    assert not r0["dh"].any() and not r0["dW"].any()
+    assert np.all(np.isfinite(r0["lse"]))
+
+
+def test_c1_has_argmax_and_target_on_different_shards():
+    inp = config_inputs("c1")
+    h = oracle.decode(inp.h, inp.dtype)
+    W = oracle.decode(inp.W, inp.dtype)
+    z = oracle.logits(h, W, inp.V_real)
+    am = z.argmax(axis=1)
+    y = inp.targets
+    ok = (y >= 0) & (y < inp.V_real)
+    assert int(np.sum(ok & (am // inp.S != y // inp.S))) >= 4
+    for v in (255, 256, 511, 512, 990, 999):
+        assert v in set(y.tolist())
+
+
+# ---------------------------------------------------------------- tied step
+
+def test_tied_step_finite_difference():
+    rng = np.random.default_rng(4)
+    T, H, V_real, V_pad, n = 5, 3, 6, 8, 2
+    W = rng.standard_normal((V_pad, H))
+    ids = np.array([2, 2, 7, 5, -3])        # a repeat, a padded ID, an out-of-range ID
+    y = np.array([1, 5, -100, 2, 0])
+    r = oracle.tied_step(ids, y, W, V_real, V_pad, n)
+
+    def loss_of(Wx):
+        hx = oracle.gather_direct(ids, Wx, V_real)
+        return _loss_mean(hx, Wx, y, V_real, V_pad, n)
+
+    eps = 1e-6
+    for v in range(V_pad):
+        for j in range(H):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[v, j] += eps
+            Wm[v, j] -= eps
+            num = (loss_of(Wp) - loss_of(Wm)) / (2 * eps)
+            assert abs(num - r["dW"][v, j]) < 1e-8
+    assert list(r["count"]) == [0, 0, 2, 0, 0, 1, 0, 0]
+
+
+# ---------------------------------------------------------------- sampled softmax
+
+def test_candidates_bruteforce():
+    V, P = 20, 9
+    y = np.array([3, 3, 17, -100, 0, 17, 25, 8])
+    perm = np.random.default_rng(9).permutation(V)
+    cand, pos, nu = oracle.candidates(y, V, -100, perm, P)
+    U = sorted(set(int(v) for v in y if 0 <= v < V))
+    assert nu == len(U) and list(cand[:nu]) == U
+    negs = []
+    for v in perm:
+        if int(v) not in U and len(negs) < P - len(U):
+            negs.append(int(v))
+    assert list(cand[nu:]) == negs and len(cand) == P
+    assert len(set(cand.tolist())) == P
+    for t, v in enumerate(y):
+        if 0 <= v < V:
+            assert cand[pos[t]] == v
+        else:
+            assert pos[t] == v
+    # more unique targets than P: the candidates are the unique targets alone
+    cand2, _, nu2 = oracle.candidates(np.arange(12), V, -100, perm, 5)
+    assert nu2 == 12 and list(cand2) == list(range(12))
+
+
+def test_sampled_full_candidate_set_equals_full_ce():
+    inp = make_ce_inputs(12, 6, 30, 30, 1, "f32", seed=8, ignore_frac=0.2)
+    h = oracle.decode(inp.h, "f32")
+    W = oracle.decode(inp.W, "f32")
+    perm = np.random.default_rng(2).permutation(30)
+    s = oracle.sampled_step(h, W, inp.targets, perm, P=30)
+    f = oracle.cross_entropy(h, W, inp.targets, 30, 30, 1)
+    assert np.allclose(s["lse"], f["lse"], rtol=1e-13)
+    assert np.allclose(s["loss"], f["loss"], rtol=1e-13, atol=1e-15)
+    assert np.allclose(s["dh"], f["dh"], rtol=1e-12, atol=1e-15)
+    assert np.allclose(s["dW"], f["dW"], rtol=1e-12, atol=1e-15)
