@@ -1,0 +1,210 @@
+"""Throughput of the vocabulary-sharded LM-head cross-entropy + masked embedding path
+on one MI355X.
+
+One step = the tied embedding + LM-head step over one batch:
+    vemb_fwd (masked lookup of the input IDs)  ->  vce_fwd (fused logits GEMM +
+    per-shard online max/sum-exp + cross-shard merge)  ->  vce_bwd (logit
+    recompute, G = scale*(softmax - onehot), dh and dW GEMMs)  ->  vemb_bwd
+    (scatter-add of dh into the same dW).
+Default workload: T=16384 tokens, H=3072, V=201088 (GPT-OSS-20B's table), bf16,
+8 contiguous vocabulary shards, Zipf(1.1) tokens, 1% out-of-range IDs, 2%
+ignored targets; inputs are seeded, synthetic and already in HBM when the
+timed region starts.
+
+    python bench.py [--steps K] [--warmup W] [--workload c4|c3] [--no-cpu-baseline]
+
+Prints one JSON line. Only one GPU is used; --gpus above 1 is refused.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused LM-head CE fwd+bwd tokens/s (V=201088,H=3072,bf16); % MFMA peak"
+PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c4", choices=["c3", "c4"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=256,
+                    help="tokens in the oracle's CPU-baseline sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, n_tok: int):
+    """The float64 oracle as it stands, on the first n_tok tokens of the same
+    workload, on this host's cores. Returns tokens/s of the oracle step."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()
+                     if i.get("user_api") == "blas"] or [os.cpu_count() or 1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    W = oracle.decode(inp.W, inp.dtype)
+    t0 = time.perf_counter()
+    if inp.h is None:
+        oracle.tied_step(inp.ids[:n_tok], inp.targets[:n_tok], W, inp.V_real, inp.V_pad,
+                         inp.num_shards, inp.ignore_index)
+        what = "tied step (gather, CE fwd+bwd, scatter-add)"
+    else:
+        h = oracle.decode(inp.h[:n_tok], inp.dtype)
+        oracle.cross_entropy(h, W, inp.targets[:n_tok], inp.V_real, inp.V_pad, inp.num_shards,
+                             inp.ignore_index)
+        what = "CE fwd+bwd"
+    dt = time.perf_counter() - t0
+    del W
+    return dict(value=n_tok / dt, unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"float64 oracle {what} on the first {n_tok} tokens of the same "
+                       f"workload (full V={inp.V_real}, H={inp.H}); {dt:.1f} s wall",
+                seconds=dt)
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": a.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import vocab_embedding_softmax_amd as V
+    from synth import config_inputs
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {a.workload} inputs")
+    inp = config_inputs(a.workload)
+    T, H, Vr, Vp, n = inp.T, inp.H, inp.V_real, inp.V_pad, inp.num_shards
+    W = V.from_bits(inp.W, inp.dtype, dev)
+    tg = torch.from_numpy(inp.targets).to(dev)
+    tied = inp.h is None
+    if tied:
+        ids = torch.from_numpy(inp.ids).to(dev)
+        h = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    else:
+        h = V.from_bits(inp.h, inp.dtype, dev)
+    dt_code = V.VCE_BF16
+    ws = V.Workspaces(dev, fwd=V.vce_fwd_workspace_bytes(T, H, Vr, Vp, n, dt_code),
+                      bwd=V.vce_bwd_workspace_bytes(T, H, Vr, Vp, n, dt_code),
+                      emb=V.vemb_bwd_workspace_bytes(T, H, Vr, Vp))
+    f32 = dict(dtype=torch.float32, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    fo = V._lib.FwdOut(torch.empty(T, **f32), torch.empty(T, **f32), torch.empty(1, **f32),
+                       torch.empty(1, **i32), torch.empty(1, **i32), None)
+    dh = torch.empty(T, H, **f32)
+    dW = torch.empty(Vp, H, **f32)
+    nbad = torch.empty(1, **i32)
+    gl = torch.ones(1, **f32)
+    stream = torch.cuda.current_stream(dev)
+    EV = ["start", "emb_fwd", "ce_fwd", "ce_bwd", "emb_bwd"]
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        if tied:
+            V.vemb_fwd(ids, W, Vr, n, out=h, n_bad=nbad)
+        if evs is not None:
+            evs[1].record(stream)
+        V.vce_fwd(h, W, tg, Vr, n, inp.ignore_index, out=fo, ws=ws["fwd"])
+        if evs is not None:
+            evs[2].record(stream)
+        V.vce_bwd(h, W, tg, fo.lse, gl, fo.n_valid, Vr, n, inp.ignore_index, V.REDUCE_MEAN,
+                  dh=dh, dW=dW, accumulate_dW=False, ws=ws["bwd"])
+        if evs is not None:
+            evs[3].record(stream)
+        if tied:
+            V.vemb_bwd(ids, dh, Vr, Vp, n, dW=dW, accumulate=True, ws=ws["emb"])
+        if evs is not None:
+            evs[4].record(stream)
+
+    log(f"[bench] warmup {a.warmup}")
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in EV] for _ in range(a.steps)]
+    log(f"[bench] timing {a.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(a.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / a.steps
+    phase = {}
+    for i in range(1, len(EV)):
+        phase[EV[i]] = float(np.mean([e[i - 1].elapsed_time(e[i]) for e in evs]))
+    log(f"[bench] {ms_step:.3f} ms/step, phases {phase}")
+
+    flop_gemm = 2.0 * T * H * Vr           # one of the four GEMMs of the CE
+    ce_fwd_ms = phase["ce_fwd"]
+    ce_bwd_ms = phase["ce_bwd"]
+    # dominant call: the one that takes longest; its kernels' algorithmic work
+    if ce_bwd_ms / 3.0 >= ce_fwd_ms:
+        dom_name, dom_ms, dom_flop = "vce_bwd (recompute+G, dh, dW GEMMs)", ce_bwd_ms, 3 * flop_gemm
+    else:
+        dom_name, dom_ms, dom_flop = "vce_fwd (fused logits GEMM + online LSE)", ce_fwd_ms, flop_gemm
+    achieved = dom_flop / (dom_ms * 1e-3) / 1e12
+    path_frac = 8.0 * T * H * Vr / (ms_step * 1e-3) / PEAK_BF16
+    res = {
+        "metric": METRIC,
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("tied embedding + LM-head step" if tied else "LM-head CE fwd+bwd")
+                        + f": T={T}, H={H}, V_real={Vr}, V_pad={Vp}, {n} contiguous vocab shards, "
+                          "bf16 inputs, fp32 accumulation, Zipf(1.1) tokens",
+            "T": T, "H": H, "V_real": Vr, "V_pad": Vp, "num_shards": n,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": dom_name,
+            "achieved": achieved,
+            "peak": PEAK_BF16 / 1e12,
+            "unit": "TFLOP/s",
+            "frac": achieved / (PEAK_BF16 / 1e12),
+            "traffic": None,
+        },
+        "path_mfma_frac": path_frac,
+        "phases_ms": phase,
+    }
+    del ws, dh, dW, W, h
+    torch.cuda.empty_cache()
+    if not a.no_cpu_baseline:
+        log(f"[bench] CPU baseline: oracle on {a.cpu_tokens} tokens")
+        cb = cpu_baseline(inp, a.cpu_tokens)
+        cb.pop("seconds", None)
+        res["cpu_baseline"] = cb
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

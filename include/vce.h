@@ -1,0 +1,203 @@
+/*
+ * vce.h -- vocabulary-sharded LM-head cross-entropy and masked embedding
+ *          lookup over one tied table, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (page titles):
+ *   [VS]  "Vocabulary shards: look up locally and normalize globally"
+ *   [SP]  "Sequence-parallel normalization: shard tokens, retain their hidden features"
+ *   [PAD] "Training collapses when token embeddings are not padded to a multiple of 64"
+ *   [SS]  "Sampled Softmax with Over-Tokenized Transformer"
+ *   [TP]  "Tensor Parallelism (TP)" (vLLM on Neuron design notes)
+ *
+ * Problem statement. Hidden rows h[T,H]; one table W[V_pad,H] shared by the
+ * input embedding and the output projection; V_real <= V_pad real classes
+ * (rows V_real..V_pad-1 are padding and never classes); num_shards contiguous
+ * equal row ranges of S = V_pad / num_shards rows each ([TP] "Embedding"),
+ * shard k owning rows [k*S, (k+1)*S). On one GPU the shards are emulated:
+ * every shard computes only with its own rows and the results are merged on
+ * the device exactly as a cross-shard reduction would merge them.
+ *
+ * Conventions for every entry point:
+ *   - Every array argument is a DEVICE pointer owned by the caller, row-major
+ *     and contiguous. The library allocates no memory, never synchronises the
+ *     host, keeps no state between calls and may be called concurrently on
+ *     different streams with disjoint outputs and workspaces.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     All work is enqueued on it; outputs are valid once it has drained.
+ *   - Argument errors are detected on the host and returned BEFORE any HIP
+ *     call is made, so they can be tested without a GPU.
+ *   - Data-dependent faults are counted, never aborted on: an out-of-range
+ *     target or ID is counted in a device scalar and handled by rule.
+ *   - Element types: VCE_F32 = IEEE float32, VCE_BF16 = bfloat16 (raw 16-bit
+ *     patterns). IDs and targets are int32. Statistics, losses and gradients
+ *     are float32.
+ *   - Alignment: every array pointer must be 16-byte aligned and H must be a
+ *     multiple of 8 (rows are read in 16-byte pieces).
+ *   - T = 0 is valid: scalars are written (0), nothing else is touched.
+ */
+#ifndef VCE_H
+#define VCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VCE_OK = 0,
+  VCE_ERR_NULL = 1,      /* a required pointer is NULL                          */
+  VCE_ERR_SHAPE = 2,     /* T < 0, H <= 0, V_real not in [1, V_pad], ignore_index
+                            inside [0, V_real), P < 1, capacity too small, or a
+                            size too large for 32-bit indexing of one dimension  */
+  VCE_ERR_SHARD = 3,     /* num_shards < 1 or V_pad not a multiple of num_shards */
+  VCE_ERR_DTYPE = 4,     /* unknown element type or reduction                    */
+  VCE_ERR_ALIGN = 5,     /* a pointer not 16-byte aligned, or H % 8 != 0         */
+  VCE_ERR_WORKSPACE = 6, /* workspace NULL or smaller than the query returned    */
+  VCE_ERR_HIP = 7        /* a HIP launch failed (hipGetLastError != success)     */
+} vce_status;
+
+typedef enum { VCE_F32 = 0, VCE_BF16 = 1 } vce_dtype;
+
+typedef enum { VCE_REDUCE_MEAN = 0, VCE_REDUCE_SUM = 1 } vce_reduction;
+
+/* Version of this interface (changes when a signature changes). */
+int32_t vce_abi_version(void);
+
+/* Human-readable text of a status code (static string, never NULL). */
+const char* vce_strerror(vce_status s);
+
+/* ------------------------------------------------------------------------ *
+ * Cross-entropy forward.                                                    *
+ *                                                                           *
+ * [VS] paragraph 3: for every token the logits z[t,v] = h[t,:] . W[v,:] of  *
+ * the real rows v < V_real are normalised by one global log-sum-exp built   *
+ * from per-shard maxima and sums of exponentials; the target logit comes    *
+ * from the single shard that owns the target. [VS] paragraph 4 and [PAD]    *
+ * section 5: padded rows are excluded (as if their logits were -inf);       *
+ * a target equal to ignore_index contributes no loss. [VS] paragraph 5: the *
+ * full [T, V] logits are never stored.                                      *
+ *                                                                           *
+ * In:  h [T,H] dt, W [V_pad,H] dt, targets [T] int32.                       *
+ * Out: lse [T]          log-sum-exp over the real rows (also for ignored     *
+ *                       tokens, [SP] paragraph 5);                           *
+ *      loss [T]         lse - z[t, y_t] for valid targets, else 0;           *
+ *      loss_sum [1]     sum of loss in a fixed order (deterministic);        *
+ *      n_valid [1]      number of targets in [0, V_real);                    *
+ *      n_bad_target [1] number of targets outside [0, V_real) that are not   *
+ *                       ignore_index (treated as ignored);                   *
+ *      shard_stats      optional (NULL = not written): float [2][num_shards] *
+ *                       [T]: plane 0 the shard maxima m_k (-inf for a shard  *
+ *                       with no real row), plane 1 the sums s_k of           *
+ *                       exp(z - m_k) over the shard's real rows.             *
+ * Rows of W at or past V_real are never read; any bits there (NaN, Inf) do  *
+ * not change any output.                                                    *
+ * ws: device workspace of at least vce_fwd_workspace_bytes(...) bytes.      *
+ * ------------------------------------------------------------------------ */
+size_t vce_fwd_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                               int32_t num_shards, vce_dtype dt);
+
+vce_status vce_fwd(const void* h, const void* W, const int32_t* targets,
+                   int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                   int32_t num_shards, int32_t ignore_index, vce_dtype dt,
+                   float* lse, float* loss, float* loss_sum, int32_t* n_valid,
+                   int32_t* n_bad_target, float* shard_stats,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Cross-entropy backward.                                                   *
+ *                                                                           *
+ * [VS] paragraph 4: the gradient of a valid logit is its global probability *
+ * minus the target indicator, times the loss scaling. Logits are recomputed *
+ * tile by tile (never stored whole) to form                                 *
+ *   G[t,v] = scale * (exp(z[t,v] - lse[t]) - [v == y_t])                    *
+ * for valid targets and real rows, else exactly 0, and then                 *
+ *   dh = G W        (overwritten, [T,H] float32)                            *
+ *   dW = G^T h      (rows < V_real; [V_pad,H] float32)                      *
+ * scale = grad_loss[0] / max(n_valid[0], 1) for VCE_REDUCE_MEAN ([SP]       *
+ * paragraph 3: one average over the valid tokens) or grad_loss[0] for       *
+ * VCE_REDUCE_SUM; both scalars are read on the device (no host sync).       *
+ * accumulate_dW = 0: every row of dW is written (rows >= V_real get 0);     *
+ * accumulate_dW = 1: G^T h is added into rows < V_real, rows >= V_real are  *
+ * left unchanged. lse must be the forward's output for the same inputs.     *
+ * G is staged in the workspace in the input element type (bf16 rounded to  *
+ * nearest-even, or float32).                                                *
+ * ------------------------------------------------------------------------ */
+size_t vce_bwd_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                               int32_t num_shards, vce_dtype dt);
+
+vce_status vce_bwd(const void* h, const void* W, const int32_t* targets, const float* lse,
+                   const float* grad_loss, const int32_t* n_valid, vce_reduction red,
+                   int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                   int32_t num_shards, int32_t ignore_index, vce_dtype dt,
+                   float* dh, float* dW, int32_t accumulate_dW,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Masked embedding lookup.                                                  *
+ *                                                                           *
+ * [VS] paragraph 1: a shard tests whether an ID is in its row range, turns  *
+ * owned IDs into local indices and contributes the row; non-owners give     *
+ * zero and the sum over shards is the embedding. [VS] paragraph 2: the      *
+ * table is never indexed with an unmasked global ID. Rule for IDs outside   *
+ * [0, V_real) (negative, padded rows, >= V_pad): a zero row, counted in     *
+ * n_bad_id. Each output row is a bit-exact copy of its owner's row          *
+ * (the owner's row is selected, not added to zeros, so -0.0 is kept).       *
+ * In:  ids [T] int32, W [V_pad,H] dt.  Out: out [T,H] dt,                   *
+ *      n_bad_id [1] int32 (optional, NULL = not counted).                   *
+ * ------------------------------------------------------------------------ */
+vce_status vemb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H,
+                    int64_t V_real, int64_t V_pad, int32_t num_shards, vce_dtype dt,
+                    void* out, int32_t* n_bad_id, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Embedding backward (scatter-add).                                         *
+ *                                                                           *
+ * [VS] paragraph 2: repeated occurrences of one token add their gradients   *
+ * into the one row that owns it; with a tied table every contribution lands *
+ * in the same tensor. dW[v,:] (+)= sum of dout[t,:] over t with ids[t] == v, *
+ * for v < V_real, summed in float32 in increasing t (deterministic: one     *
+ * writer per row, fixed order). IDs outside [0, V_real) are dropped.        *
+ * accumulate = 1: add into the touched rows only (e.g. after vce_bwd wrote  *
+ * the LM-head part of a tied dW); accumulate = 0: the whole table is        *
+ * overwritten (untouched rows become 0).                                    *
+ * In: ids [T] int32, dout [T,H] of dout_dt.  Out: dW [V_pad,H] float32.     *
+ * ------------------------------------------------------------------------ */
+size_t vemb_bwd_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_pad);
+
+vce_status vemb_bwd(const int32_t* ids, const void* dout, vce_dtype dout_dt,
+                    int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                    int32_t num_shards, float* dW, int32_t accumulate,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Sampled-softmax candidates.                                               *
+ *                                                                           *
+ * [SS] Setup (the simplified loss): candidates are the unique targets of    *
+ * the batch followed by random negatives, P in all, and each token's        *
+ * cross-entropy target is its target's position among the candidates.      *
+ * U = the distinct targets in [0, V), ascending. The negatives are the first *
+ * P - |U| entries of perm (a caller-drawn random permutation of [0, V)) that *
+ * are not in U, so they are uniform without replacement over the rest of    *
+ * the vocabulary. cand = U followed by the negatives; n_cand = max(P, |U|). *
+ * pos[t] = index of targets[t] in U for targets in [0, V), else targets[t]  *
+ * unchanged (so ignore_index stays ignored, other values stay invalid).     *
+ * In:  targets [T], perm [V] int32.  Out: cand [cand_cap] int32 with        *
+ *      cand_cap >= max(P, min(T, V)); pos [T] int32; n_unique [1], n_cand   *
+ *      [1] int32. The candidate rows' gather, cross-entropy and scatter-back *
+ *      reuse vemb_fwd, vce_fwd/vce_bwd (V_real = V_pad = n_cand, one shard)  *
+ *      and vemb_bwd.                                                         *
+ * ------------------------------------------------------------------------ */
+size_t vss_candidates_workspace_bytes(int64_t T, int64_t V);
+
+vce_status vss_candidates(const int32_t* targets, int64_t T, int64_t V, int32_t ignore_index,
+                          const int32_t* perm, int64_t P, int32_t* cand, int64_t cand_cap,
+                          int32_t* pos, int32_t* n_unique, int32_t* n_cand,
+                          void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VCE_H */

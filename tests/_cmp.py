@@ -1,0 +1,60 @@
+"""Comparison helpers and GPU-run wrappers shared by the GPU parity tests.
+
+Tolerances:
+  bf16 inputs, fp32 accumulation: |d loss_sum| / |loss_sum| <= 2e-3,
+    max_t |d lse_t| <= 1e-2, rel-L2 <= 1e-2 on dh and dW (and on every
+    embedding-gradient tensor);
+  fp32 inputs: 1e-5 relative on loss, lse (per element) and the gradients (rel-L2).
+  Integer and byte results (gathers, counts, candidate lists): bit-exact.
+"""
+
+import numpy as np
+
+import oracle
+from oracle.ce import MEAN
+
+TOL = {
+    "bf16": dict(loss=2e-3, lse_abs=1e-2, lse_rel=None, grad=1e-2),
+    "f32": dict(loss=1e-5, lse_abs=None, lse_rel=1e-5, grad=1e-5),
+}
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    if nb == 0:
+        return float(np.linalg.norm(a))
+    return float(np.linalg.norm(a - b) / nb)
+
+
+def check_ce(gpu: dict, ref: dict, dtype: str, V_real: int, check_grads: bool = True):
+    tol = TOL[dtype]
+    assert gpu["n_valid"] == ref["n_valid"], (gpu["n_valid"], ref["n_valid"])
+    assert gpu["n_bad"] == ref["n_bad"], (gpu["n_bad"], ref["n_bad"])
+    if ref["n_valid"]:
+        dl = abs(gpu["loss_sum"] - ref["loss_sum"]) / abs(ref["loss_sum"])
+        assert dl <= tol["loss"], f"loss rel err {dl}"
+    lse_err = np.abs(gpu["lse"].astype(np.float64) - ref["lse"])
+    if tol["lse_abs"] is not None:
+        assert lse_err.max() <= tol["lse_abs"], f"lse abs err {lse_err.max()}"
+    else:
+        rel = (lse_err / np.maximum(np.abs(ref["lse"]), 1e-30)).max()
+        assert rel <= tol["lse_rel"], f"lse rel err {rel}"
+    valid = ref["valid"]
+    assert not gpu["loss"][~valid].any()
+    if check_grads:
+        e_dh = rel_l2(gpu["dh"], ref["dh"])
+        e_dw = rel_l2(gpu["dW"], ref["dW"])
+        assert e_dh <= tol["grad"], f"dh rel-L2 {e_dh}"
+        assert e_dw <= tol["grad"], f"dW rel-L2 {e_dw}"
+        assert not gpu["dW"][V_real:].any(), "padded dW rows must be exactly 0"
+        assert not gpu["dh"][~valid].any(), "ignored tokens must get dh = 0"
+
+
+def oracle_ce(inp, grad_loss=1.0, reduction=MEAN, num_shards=None):
+    h = oracle.decode(inp.h, inp.dtype)
+    W = oracle.decode(inp.W, inp.dtype)
+    n = inp.num_shards if num_shards is None else num_shards
+    return oracle.cross_entropy(h, W, inp.targets, inp.V_real, inp.V_pad, n,
+                                inp.ignore_index, grad_loss, reduction)

@@ -1,0 +1,124 @@
+"""Host-side tests of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any HIP call (so these run
+without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vce.h")
+
+vce = pytest.importorskip("vocab_embedding_softmax_amd._lib",
+                          reason="libvce.so not built (python -m vocab_embedding_softmax_amd.build)")
+lib = vce.lib
+
+OK, NULL, SHAPE, SHARD, DTYPE, ALIGN, WORKSPACE = 0, 1, 2, 3, 4, 5, 6
+
+# fake, never dereferenced device addresses (16-byte aligned unless stated)
+A = ctypes.c_void_p(0x10000)
+B = ctypes.c_void_p(0x20000)
+C = ctypes.c_void_p(0x30000)
+MIS = ctypes.c_void_p(0x10008)  # 8-byte aligned only
+NUL = None
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)) - {"defined"})
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) == 11, names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in vce.SIGNATURES, n
+
+
+def test_version_and_strerror():
+    assert lib.vce_abi_version() == 1
+    for s in range(8):
+        assert vce.strerror(s)
+    assert vce.strerror(99) == "unknown status"
+
+
+def _fwd(T=4, H=64, V_real=1000, V_pad=1024, n=4, ign=-100, dt=1, h=A, W=B, tg=C, lse=A,
+         loss=B, ls=C, nv=A, nb=B, ss=NUL, ws=A, wsb=1 << 40):
+    return lib.vce_fwd(h, W, tg, T, H, V_real, V_pad, n, ign, dt, lse, loss, ls, nv, nb, ss, ws,
+                       wsb, None)
+
+
+def test_fwd_argument_errors():
+    assert _fwd(n=3) == SHARD
+    assert _fwd(n=0) == SHARD
+    assert _fwd(V_real=0) == SHAPE
+    assert _fwd(V_real=1025) == SHAPE
+    assert _fwd(T=-1) == SHAPE
+    assert _fwd(H=0) == SHAPE
+    assert _fwd(ign=5) == SHAPE          # ignore_index must not be a real class
+    assert _fwd(dt=7) == DTYPE
+    assert _fwd(h=NUL) == NULL
+    assert _fwd(ls=NUL) == NULL
+    assert _fwd(H=60) == ALIGN
+    assert _fwd(W=MIS) == ALIGN
+    assert _fwd(ws=NUL) == WORKSPACE
+    need = lib.vce_fwd_workspace_bytes(4, 64, 1000, 1024, 4, 1)
+    assert need > 0
+    assert _fwd(wsb=need - 1) == WORKSPACE
+
+
+def _bwd(T=4, H=64, V_real=1000, V_pad=1024, n=4, ign=-100, dt=1, red=0, dh=A, dW=B, gl=C,
+         nv=A, ws=A, wsb=1 << 40, h=A):
+    return lib.vce_bwd(h, B, C, A, gl, nv, red, T, H, V_real, V_pad, n, ign, dt, dh, dW, 0, ws,
+                       wsb, None)
+
+
+def test_bwd_argument_errors():
+    assert _bwd(n=5) == SHARD
+    assert _bwd(red=2) == DTYPE
+    assert _bwd(dW=NUL) == NULL
+    assert _bwd(gl=NUL) == NULL
+    assert _bwd(nv=NUL) == NULL            # needed for the mean
+    assert _bwd(h=NUL) == NULL
+    assert _bwd(dh=MIS) == ALIGN
+    need = lib.vce_bwd_workspace_bytes(4, 64, 1000, 1024, 4, 1)
+    assert need > 0
+    assert _bwd(wsb=need - 1) == WORKSPACE
+    assert _bwd(ign=0) == SHAPE
+
+
+def test_emb_argument_errors():
+    assert lib.vemb_fwd(A, B, 4, 64, 1000, 1024, 3, 1, C, NUL, None) == SHARD
+    assert lib.vemb_fwd(A, B, 4, 64, 1000, 1024, 4, 9, C, NUL, None) == DTYPE
+    assert lib.vemb_fwd(NUL, B, 4, 64, 1000, 1024, 4, 1, C, NUL, None) == NULL
+    assert lib.vemb_fwd(A, B, 4, 12, 1000, 1024, 4, 1, C, NUL, None) == ALIGN
+    assert lib.vemb_fwd(A, MIS, 4, 64, 1000, 1024, 4, 1, C, NUL, None) == ALIGN
+    need = lib.vemb_bwd_workspace_bytes(4, 64, 1000, 1024)
+    assert need > 0
+    assert lib.vemb_bwd(A, B, 0, 4, 64, 1000, 1024, 4, C, 1, A, need - 1, None) == WORKSPACE
+    assert lib.vemb_bwd(A, B, 0, 4, 64, 1000, 1024, 4, NUL, 1, A, need, None) == NULL
+    assert lib.vemb_bwd(A, B, 0, 4, 64, 1001, 1000, 4, C, 1, A, need, None) == SHAPE
+
+
+def test_candidates_argument_errors():
+    need = lib.vss_candidates_workspace_bytes(8, 100)
+    assert need > 0
+    args = lambda P=10, cap=10, ws=A, wsb=need, ign=-100: lib.vss_candidates(
+        A, 8, 100, ign, B, P, C, cap, A, B, C, ws, wsb, None)
+    assert args(P=0) == SHAPE
+    assert args(cap=9) == SHAPE          # capacity below max(P, min(T, V))
+    assert args(ign=3) == SHAPE
+    assert args(wsb=need - 1) == WORKSPACE
+    assert args(ws=NUL) == WORKSPACE
+
+
+def test_workspace_queries_are_deterministic_and_reject_bad_shapes():
+    a = lib.vce_bwd_workspace_bytes(8192, 3072, 201088, 201088, 8, 1)
+    b = lib.vce_bwd_workspace_bytes(8192, 3072, 201088, 201088, 8, 1)
+    assert a == b and a > 2 * 8192 * 201088 * 2
+    assert lib.vce_fwd_workspace_bytes(8, 64, 100, 101, 2, 1) == 0  # 101 % 2 != 0
+    assert lib.vce_bwd_workspace_bytes(8, 64, 100, 128, 4, 3) == 0  # bad dtype

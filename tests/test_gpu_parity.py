@@ -1,0 +1,303 @@
+"""GPU parity: libvce (through its C ABI) against the float64 oracle on the
+same seeded inputs. Every test here needs an MI355X."""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.ce import MEAN, SUM
+from synth import config_inputs, make_ce_inputs, make_tied_inputs, make_sampled_inputs
+from tests._cmp import TOL, check_ce, oracle_ce, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def V():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vocab_embedding_softmax_amd as v
+    return v
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_ce(V, inp, grad_loss=1.0, reduction=MEAN, num_shards=None, W_override=None):
+    dev = "cuda"
+    n = inp.num_shards if num_shards is None else num_shards
+    h = V.from_bits(inp.h, inp.dtype, dev)
+    W = V.from_bits(inp.W if W_override is None else W_override, inp.dtype, dev)
+    tg = torch.from_numpy(inp.targets).to(dev)
+    gl = torch.tensor([grad_loss], dtype=torch.float32, device=dev)
+    r = V.ce_step(h, W, tg, inp.V_real, n, inp.ignore_index, grad_loss=gl,
+                  reduction=reduction, shard_stats=True)
+    torch.cuda.synchronize()
+    f = r.fwd
+    return dict(lse=f.lse.cpu().numpy(), loss=f.loss.cpu().numpy(),
+                loss_sum=float(f.loss_sum.item()), n_valid=int(f.n_valid.item()),
+                n_bad=int(f.n_bad.item()), shard=f.shard_stats.cpu().numpy(),
+                dh=r.dh.cpu().numpy(), dW=r.dW.cpu().numpy())
+
+
+# ------------------------------------------------------------------ cross-entropy
+
+def test_c1_ce_parity_fp32(V):
+    say("case c1 fp32 ce")
+    inp = config_inputs("c1")
+    for red, gl in ((MEAN, 1.0), (SUM, 0.5)):
+        g = gpu_ce(V, inp, gl, red)
+        ref = oracle_ce(inp, gl, red)
+        check_ce(g, ref, "f32", inp.V_real)
+        # per-shard statistics: what each emulated rank holds before the merge
+        m, s = g["shard"][0], g["shard"][1]
+        assert np.allclose(m, ref["shard_m"], rtol=1e-5, atol=1e-6)
+        assert np.allclose(s, ref["shard_s"], rtol=1e-5, atol=1e-6)
+
+
+def test_c2_ce_parity_bf16_garbage_pad_rows(V):
+    say("case c2 bf16 ce")
+    inp = config_inputs("c2")
+    g = gpu_ce(V, inp)
+    ref = oracle_ce(inp)
+    check_ce(g, ref, "bf16", inp.V_real)
+    m, s = g["shard"][0], g["shard"][1]
+    assert np.abs(m - ref["shard_m"]).max() < 1e-3
+    assert np.allclose(s, ref["shard_s"], rtol=2e-3)
+
+
+def test_c2_pad_rows_do_not_change_any_bit(V):
+    say("case c2 pad rows +8 vs NaN vs 0")
+    inp = config_inputs("c2", T=512)
+    base = gpu_ce(V, inp)
+    for fill in (0x7FC0, 0x0000, 0xFF80):  # NaN, +0, -inf
+        W2 = inp.W.copy()
+        W2[inp.V_real:] = fill
+        g = gpu_ce(V, inp, W_override=W2)
+        for k in ("lse", "loss", "dh", "dW", "shard"):
+            assert np.array_equal(g[k].view(np.uint32), base[k].view(np.uint32)), k
+        assert g["loss_sum"] == base["loss_sum"]
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8])
+def test_num_shards_invariance(V, n):
+    say(f"case c2-recipe T=384 shards={n}")
+    inp = config_inputs("c2", T=384)
+    g = gpu_ce(V, inp, num_shards=n)
+    ref = oracle_ce(inp, num_shards=n)
+    check_ce(g, ref, "bf16", inp.V_real)
+    assert np.abs(g["lse"] - ref["lse"]).max() < 1e-4
+
+
+RAGGED = [
+    # T, H, V_real, V_pad, n, dtype
+    (1, 8, 1, 8, 8, "f32"),
+    (5, 8, 13, 16, 4, "bf16"),
+    (300, 72, 1001, 1002, 2, "bf16"),    # V_pad not a multiple of 8, H not of 64
+    (257, 64, 777, 800, 5, "f32"),
+    (513, 136, 2500, 2560, 10, "bf16"),
+    (64, 64, 1000, 1024, 4, "bf16"),
+    (40, 1024, 300, 300, 3, "f32"),
+]
+
+
+@pytest.mark.parametrize("T,H,Vr,Vp,n,dt", RAGGED)
+def test_ragged_shapes(V, T, H, Vr, Vp, n, dt):
+    say(f"case ragged T={T} H={H} V_real={Vr} V_pad={Vp} n={n} {dt}")
+    inp = make_ce_inputs(T, H, Vr, Vp, n, dt, seed=T * 7 + H, ignore_frac=0.1,
+                         pad_fill=float("nan"))
+    inp.targets[0] = Vr - 1
+    if T > 2:
+        inp.targets[1] = Vr + 1 if Vr + 1 < 2**31 else -5   # a bad target
+    g = gpu_ce(V, inp)
+    ref = oracle_ce(inp)
+    check_ce(g, ref, dt, Vr)
+
+
+def test_zero_tokens(V):
+    say("case T=0")
+    inp = make_ce_inputs(0, 64, 100, 128, 2, "bf16", seed=1)
+    dev = "cuda"
+    h = torch.empty(0, 64, dtype=torch.bfloat16, device=dev)
+    W = V.from_bits(inp.W, "bf16", dev)
+    tg = torch.empty(0, dtype=torch.int32, device=dev)
+    dW = torch.full((128, 64), 7.0, device=dev)
+    r = V.ce_step(h, W, tg, 100, 2, dW=dW)
+    torch.cuda.synchronize()
+    assert r.fwd.loss_sum.item() == 0.0 and r.fwd.n_valid.item() == 0
+    assert not r.dW.any()
+
+
+def test_all_targets_ignored(V):
+    say("case all ignored")
+    inp = make_ce_inputs(70, 64, 500, 512, 4, "bf16", seed=3)
+    inp.targets[:] = -100
+    g = gpu_ce(V, inp)
+    assert g["n_valid"] == 0 and g["loss_sum"] == 0.0
+    assert not g["dh"].any() and not g["dW"].any()
+    ref = oracle_ce(inp)
+    assert np.abs(g["lse"] - ref["lse"]).max() < 1e-2
+
+
+def test_rerun_is_bitwise_identical(V):
+    say("case determinism c2 T=1024")
+    inp = config_inputs("c2", T=1024)
+    a = gpu_ce(V, inp)
+    b = gpu_ce(V, inp)
+    for k in ("lse", "loss", "dh", "dW"):
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+    assert a["loss_sum"] == b["loss_sum"]
+
+
+# ------------------------------------------------------------------ embedding
+
+def _bits(t):
+    a = t.cpu()
+    if a.dtype == torch.bfloat16:
+        return a.view(torch.int16).numpy()
+    return a.view(torch.int32).numpy()
+
+
+@pytest.mark.parametrize("cfg", ["c1", "c2"])
+def test_embedding_gather_bit_exact(V, cfg):
+    say(f"case gather {cfg}")
+    inp = config_inputs(cfg)
+    dev = "cuda"
+    edge = np.array([-1, inp.V_real, inp.V_pad - 1, inp.V_pad, -(2**31), 2**31 - 1, 0,
+                     inp.V_real - 1, inp.S - 1, inp.S], dtype=np.int32)
+    ids = np.concatenate([inp.ids, edge]).astype(np.int32)
+    W = V.from_bits(inp.W, inp.dtype, dev)
+    out, nbad = V.vemb_fwd(torch.from_numpy(ids).to(dev), W, inp.V_real, inp.num_shards)
+    torch.cuda.synchronize()
+    got = _bits(out)
+    Wb = inp.W.view(np.int16) if inp.dtype == "bf16" else inp.W.view(np.int32)
+    ok = (ids >= 0) & (ids < inp.V_real)
+    want = np.zeros_like(got)
+    want[ok] = Wb[ids[ok]]
+    assert np.array_equal(got, want)
+    assert int(nbad.item()) == int((~ok).sum())
+    # and the masked per-shard sum (the sharded form) agrees in value
+    Wf = oracle.decode(inp.W, inp.dtype)
+    ms = oracle.gather_masked_shards(ids, Wf, inp.V_real, inp.V_pad, inp.num_shards)
+    assert np.array_equal(oracle.decode(got.view(np.uint16) if inp.dtype == "bf16" else
+                                        got.view(np.float32), inp.dtype), ms)
+
+
+def _dout(T, H, seed, dtype):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    if dtype == "bf16":
+        from synth import bf16_bits_from_f32
+        return bf16_bits_from_f32(x)
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("cfg", ["c1", "c2"])
+def test_scatter_add_parity(V, cfg, dtype):
+    say(f"case scatter {cfg} dout={dtype}")
+    inp = config_inputs(cfg)
+    dev = "cuda"
+    T, H = inp.ids.shape[0], inp.H
+    dout = _dout(T, H, 5, dtype)
+    ids_t = torch.from_numpy(inp.ids).to(dev)
+    d = V.from_bits(dout, dtype, dev)
+    ref, count = oracle.scatter_add(inp.ids, oracle.decode(dout, dtype), inp.V_real, inp.V_pad)
+    # overwrite mode
+    got = V.vemb_bwd(ids_t, d, inp.V_real, inp.V_pad, inp.num_shards).cpu().numpy()
+    torch.cuda.synchronize()
+    assert rel_l2(got, ref) <= 1e-6
+    assert not got[count == 0].any()
+    once = count == 1
+    assert np.array_equal(got[once], ref[once].astype(np.float32))
+    # accumulate mode adds into the rows the IDs touch and leaves the others
+    base = np.random.default_rng(1).standard_normal((inp.V_pad, H)).astype(np.float32)
+    dW = torch.from_numpy(base).to(dev)
+    V.vemb_bwd(ids_t, d, inp.V_real, inp.V_pad, inp.num_shards, dW=dW, accumulate=True)
+    got2 = dW.cpu().numpy()
+    assert np.array_equal(got2[count == 0], base[count == 0])
+    assert rel_l2(got2 - base, ref) <= 1e-5
+
+
+def test_scatter_add_heavy_repeats(V):
+    say("case scatter heavy repeats")
+    dev = "cuda"
+    rng = np.random.default_rng(3)
+    T, H, Vr = 5000, 264, 300
+    ids = np.where(rng.random(T) < 0.6, 7, rng.integers(-5, Vr + 5, T)).astype(np.int32)
+    dout = rng.standard_normal((T, H)).astype(np.float32)
+    ref, count = oracle.scatter_add(ids, dout, Vr, Vr)
+    got = V.vemb_bwd(torch.from_numpy(ids).to(dev), torch.from_numpy(dout).to(dev), Vr, Vr,
+                     1).cpu().numpy()
+    assert count[7] > 2500
+    assert rel_l2(got, ref) <= 1e-6
+    # fixed summation order: a second run gives the same bits
+    got_b = V.vemb_bwd(torch.from_numpy(ids).to(dev), torch.from_numpy(dout).to(dev), Vr, Vr,
+                       1).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), got_b.view(np.uint32))
+
+
+# ------------------------------------------------------------------ tied step
+
+def test_tied_step_small(V):
+    say("case tied step T=1024 H=256 V=8192")
+    inp = make_tied_inputs(1024, 256, 8000, 8192, 8, "bf16", seed=44)
+    dev = "cuda"
+    W = V.from_bits(inp.W, "bf16", dev)
+    r = V.tied_step(torch.from_numpy(inp.ids).to(dev), torch.from_numpy(inp.targets).to(dev),
+                    W, inp.V_real, inp.num_shards)
+    torch.cuda.synchronize()
+    ref = oracle.tied_step(inp.ids, inp.targets, oracle.decode(inp.W, "bf16"), inp.V_real,
+                           inp.V_pad, inp.num_shards)
+    h_bits = _bits(r.extra["h"])
+    ok = (inp.ids >= 0) & (inp.ids < inp.V_real)
+    want = np.zeros_like(h_bits)
+    want[ok] = inp.W.view(np.int16)[inp.ids[ok]]
+    assert np.array_equal(h_bits, want)
+    assert int(r.extra["n_bad_id"].item()) == int((~ok).sum())
+    g = dict(lse=r.fwd.lse.cpu().numpy(), loss=r.fwd.loss.cpu().numpy(),
+             loss_sum=float(r.fwd.loss_sum.item()), n_valid=int(r.fwd.n_valid.item()),
+             n_bad=int(r.fwd.n_bad.item()), dh=r.dh.cpu().numpy(), dW=r.dW.cpu().numpy())
+    check_ce(g, ref, "bf16", inp.V_real)
+
+
+# ------------------------------------------------------------------ sampled softmax
+
+def test_candidates_bit_exact(V):
+    say("case candidates")
+    dev = "cuda"
+    inp = make_sampled_inputs(3000, 64, 20000, 2048, "bf16", seed=9, ignore_frac=0.03)
+    inp.targets[5] = 25000  # out of range: keeps its value as position
+    c = V.vss_candidates(torch.from_numpy(inp.targets).to(dev), inp.V_real,
+                         torch.from_numpy(inp.perm).to(dev), inp.P)
+    torch.cuda.synchronize()
+    cand, pos, nu = oracle.candidates(inp.targets, inp.V_real, -100, inp.perm, inp.P)
+    assert int(c.n_unique.item()) == nu
+    assert int(c.n_cand.item()) == cand.shape[0]
+    assert np.array_equal(c.cand.cpu().numpy()[:cand.shape[0]], cand.astype(np.int32))
+    assert np.array_equal(c.pos.cpu().numpy(), pos.astype(np.int32))
+
+
+def test_sampled_step_small(V):
+    say("case sampled step T=1024 H=128 V=16384 P=2048")
+    dev = "cuda"
+    inp = make_sampled_inputs(1024, 128, 16384, 2048, "bf16", seed=12)
+    h = V.from_bits(inp.h, "bf16", dev)
+    W = V.from_bits(inp.W, "bf16", dev)
+    r = V.sampled_step(h, W, torch.from_numpy(inp.targets).to(dev),
+                       torch.from_numpy(inp.perm).to(dev), inp.P)
+    torch.cuda.synchronize()
+    ref = oracle.sampled_step(oracle.decode(inp.h, "bf16"), oracle.decode(inp.W, "bf16"),
+                              inp.targets, inp.perm, inp.P)
+    assert int(r.extra["n_cand"].item()) == inp.P
+    assert np.array_equal(r.extra["cand"].cpu().numpy()[:inp.P], ref["cand"].astype(np.int32))
+    g = dict(lse=r.fwd.lse.cpu().numpy(), loss=r.fwd.loss.cpu().numpy(),
+             loss_sum=float(r.fwd.loss_sum.item()), n_valid=int(r.fwd.n_valid.item()),
+             n_bad=int(r.fwd.n_bad.item()), dh=r.dh.cpu().numpy(), dW=r.dW.cpu().numpy())
+    check_ce(g, ref, "bf16", inp.V_real)

@@ -1,0 +1,268 @@
+"""ctypes binding of libvce (include/vce.h).
+
+Argument marshalling only: every function here takes torch tensors that live
+on the GPU, checks their dtype/shape/contiguity, allocates outputs and
+workspaces with torch when the caller did not pass them, and calls the C entry
+point of the same name on the current torch stream. All arithmetic happens in
+the library's HIP kernels. Importing this module fails loudly when the library
+has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from collections import namedtuple
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvce.so")
+
+VCE_F32, VCE_BF16 = 0, 1
+REDUCE_MEAN, REDUCE_SUM = 0, 1
+
+STATUS = {0: "VCE_OK", 1: "VCE_ERR_NULL", 2: "VCE_ERR_SHAPE", 3: "VCE_ERR_SHARD",
+          4: "VCE_ERR_DTYPE", 5: "VCE_ERR_ALIGN", 6: "VCE_ERR_WORKSPACE", 7: "VCE_ERR_HIP"}
+
+# every symbol include/vce.h declares, with its C signature
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+SIGNATURES = {
+    "vce_abi_version": (_I32, []),
+    "vce_strerror": (ctypes.c_char_p, [_I32]),
+    "vce_fwd_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32, _I32]),
+    "vce_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32,
+                       _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "vce_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32, _I32]),
+    "vce_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _I32, _I32, _I32,
+                       _P, _P, _I32, _P, _SZ, _P]),
+    "vemb_fwd": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P, _P, _P]),
+    "vemb_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
+    "vemb_bwd": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _I64, _I32, _P, _I32, _P, _SZ, _P]),
+    "vss_candidates_workspace_bytes": (_SZ, [_I64, _I64]),
+    "vss_candidates": (_I32, [_P, _I64, _I64, _I32, _P, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _P]),
+}
+
+
+class VceError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}: {strerror(status)}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          f"`python -m vocab_embedding_softmax_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def strerror(status: int) -> str:
+    return lib.vce_strerror(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise VceError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return VCE_BF16
+    if t.dtype == torch.float32:
+        return VCE_F32
+    raise TypeError(f"element type must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None:
+        return ws
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ sizes
+
+def vce_fwd_workspace_bytes(T, H, V_real, V_pad, num_shards, dtype=VCE_BF16) -> int:
+    return int(lib.vce_fwd_workspace_bytes(T, H, V_real, V_pad, num_shards, dtype))
+
+
+def vce_bwd_workspace_bytes(T, H, V_real, V_pad, num_shards, dtype=VCE_BF16) -> int:
+    return int(lib.vce_bwd_workspace_bytes(T, H, V_real, V_pad, num_shards, dtype))
+
+
+def vemb_bwd_workspace_bytes(T, H, V_real, V_pad) -> int:
+    return int(lib.vemb_bwd_workspace_bytes(T, H, V_real, V_pad))
+
+
+def vss_candidates_workspace_bytes(T, V) -> int:
+    return int(lib.vss_candidates_workspace_bytes(T, V))
+
+
+# ------------------------------------------------------------------ entry points
+
+FwdOut = namedtuple("FwdOut", "lse loss loss_sum n_valid n_bad shard_stats")
+
+
+def vce_fwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, V_real: int,
+            num_shards: int, ignore_index: int = -100, *, shard_stats: bool = False,
+            out: Optional[FwdOut] = None, ws: Optional[torch.Tensor] = None,
+            stream=None) -> FwdOut:
+    """Cross-entropy forward. h [T,H], W [V_pad,H] (same dtype), targets [T] int32."""
+    T, H = h.shape
+    V_pad = W.shape[0]
+    dt = _dt(h)
+    _need(h, "h")
+    _need(W, "W", h.dtype, (V_pad, H))
+    _need(targets, "targets", torch.int32, (T,))
+    dev = h.device
+    if out is None:
+        f = dict(dtype=torch.float32, device=dev)
+        i = dict(dtype=torch.int32, device=dev)
+        out = FwdOut(torch.empty(T, **f), torch.empty(T, **f), torch.empty(1, **f),
+                     torch.empty(1, **i), torch.empty(1, **i),
+                     torch.empty(2, num_shards, T, **f) if shard_stats else None)
+    need = vce_fwd_workspace_bytes(T, H, V_real, V_pad, num_shards, dt)
+    ws = _workspace(need, dev, ws)
+    st = lib.vce_fwd(_ptr(h), _ptr(W), _ptr(targets), T, H, V_real, V_pad, num_shards,
+                     ignore_index, dt, _ptr(out.lse), _ptr(out.loss), _ptr(out.loss_sum),
+                     _ptr(out.n_valid), _ptr(out.n_bad), _ptr(out.shard_stats), _ptr(ws),
+                     ws.numel(), _stream(stream, dev))
+    _check("vce_fwd", st)
+    return out
+
+
+BwdOut = namedtuple("BwdOut", "dh dW")
+
+
+def vce_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor,
+            grad_loss: torch.Tensor, n_valid: torch.Tensor, V_real: int, num_shards: int,
+            ignore_index: int = -100, reduction: int = REDUCE_MEAN, *,
+            dh: Optional[torch.Tensor] = None, dW: Optional[torch.Tensor] = None,
+            accumulate_dW: bool = False, ws: Optional[torch.Tensor] = None,
+            stream=None) -> BwdOut:
+    """Cross-entropy backward: dh [T,H] and dW [V_pad,H] (float32)."""
+    T, H = h.shape
+    V_pad = W.shape[0]
+    dt = _dt(h)
+    _need(h, "h")
+    _need(W, "W", h.dtype, (V_pad, H))
+    _need(targets, "targets", torch.int32, (T,))
+    _need(lse, "lse", torch.float32, (T,))
+    _need(grad_loss, "grad_loss", torch.float32)
+    _need(n_valid, "n_valid", torch.int32)
+    dev = h.device
+    if dh is None:
+        dh = torch.empty(T, H, dtype=torch.float32, device=dev)
+    if dW is None:
+        dW = torch.empty(V_pad, H, dtype=torch.float32, device=dev)
+    _need(dh, "dh", torch.float32, (T, H))
+    _need(dW, "dW", torch.float32, (V_pad, H))
+    need = vce_bwd_workspace_bytes(T, H, V_real, V_pad, num_shards, dt)
+    ws = _workspace(need, dev, ws)
+    st = lib.vce_bwd(_ptr(h), _ptr(W), _ptr(targets), _ptr(lse), _ptr(grad_loss), _ptr(n_valid),
+                     reduction, T, H, V_real, V_pad, num_shards, ignore_index, dt, _ptr(dh),
+                     _ptr(dW), 1 if accumulate_dW else 0, _ptr(ws), ws.numel(),
+                     _stream(stream, dev))
+    _check("vce_bwd", st)
+    return BwdOut(dh, dW)
+
+
+def vemb_fwd(ids: torch.Tensor, W: torch.Tensor, V_real: int, num_shards: int, *,
+             out: Optional[torch.Tensor] = None, n_bad: Optional[torch.Tensor] = None,
+             count_bad: bool = True, stream=None):
+    """Masked lookup: returns (out [T,H] in W's dtype, n_bad [1] int32 or None)."""
+    T = ids.shape[0]
+    V_pad, H = W.shape
+    dt = _dt(W)
+    _need(ids, "ids", torch.int32, (T,))
+    _need(W, "W")
+    dev = W.device
+    if out is None:
+        out = torch.empty(T, H, dtype=W.dtype, device=dev)
+    _need(out, "out", W.dtype, (T, H))
+    if count_bad and n_bad is None:
+        n_bad = torch.empty(1, dtype=torch.int32, device=dev)
+    st = lib.vemb_fwd(_ptr(ids), _ptr(W), T, H, V_real, V_pad, num_shards, dt, _ptr(out),
+                      _ptr(n_bad) if count_bad else None, _stream(stream, dev))
+    _check("vemb_fwd", st)
+    return out, n_bad
+
+
+def vemb_bwd(ids: torch.Tensor, dout: torch.Tensor, V_real: int, V_pad: int, num_shards: int,
+             *, dW: Optional[torch.Tensor] = None, accumulate: bool = False,
+             ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Scatter-add of dout rows into dW [V_pad, H] (float32) by ID."""
+    T, H = dout.shape
+    dt = _dt(dout)
+    _need(ids, "ids", torch.int32, (T,))
+    _need(dout, "dout")
+    dev = dout.device
+    if dW is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs dW")
+        dW = torch.empty(V_pad, H, dtype=torch.float32, device=dev)
+    _need(dW, "dW", torch.float32, (V_pad, H))
+    need = vemb_bwd_workspace_bytes(T, H, V_real, V_pad)
+    ws = _workspace(need, dev, ws)
+    st = lib.vemb_bwd(_ptr(ids), _ptr(dout), dt, T, H, V_real, V_pad, num_shards, _ptr(dW),
+                      1 if accumulate else 0, _ptr(ws), ws.numel(), _stream(stream, dev))
+    _check("vemb_bwd", st)
+    return dW
+
+
+CandOut = namedtuple("CandOut", "cand pos n_unique n_cand")
+
+
+def vss_candidates(targets: torch.Tensor, V: int, perm: torch.Tensor, P: int,
+                   ignore_index: int = -100, *, out: Optional[CandOut] = None,
+                   ws: Optional[torch.Tensor] = None, stream=None) -> CandOut:
+    """Sampled-softmax candidates: cand [cap], pos [T], n_unique [1], n_cand [1] (int32)."""
+    T = targets.shape[0]
+    _need(targets, "targets", torch.int32, (T,))
+    _need(perm, "perm", torch.int32, (V,))
+    dev = targets.device
+    cap = max(P, min(T, V))
+    if out is None:
+        i = dict(dtype=torch.int32, device=dev)
+        out = CandOut(torch.empty(cap, **i), torch.empty(T, **i), torch.empty(1, **i),
+                      torch.empty(1, **i))
+    need = vss_candidates_workspace_bytes(T, V)
+    ws = _workspace(need, dev, ws)
+    st = lib.vss_candidates(_ptr(targets), T, V, ignore_index, _ptr(perm), P, _ptr(out.cand),
+                            out.cand.numel(), _ptr(out.pos), _ptr(out.n_unique), _ptr(out.n_cand),
+                            _ptr(ws), ws.numel(), _stream(stream, dev))
+    _check("vss_candidates", st)
+    return out

@@ -1,0 +1,179 @@
+// C entry points of libvce: argument checks (all on the host, before any HIP
+// call), workspace sizing, then the launchers.
+#include "../../include/vce.h"
+
+#include <hip/hip_runtime.h>
+
+#include "vce_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+size_t esize_of(vce_dtype dt) { return dt == VCE_BF16 ? 2 : 4; }
+bool dtype_ok(int dt) { return dt == VCE_F32 || dt == VCE_BF16; }
+
+// Shape / shard checks shared by the table-based entry points.
+vce_status check_table(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n) {
+  if (T < 0 || H <= 0 || V_real < 1 || V_real > V_pad) return VCE_ERR_SHAPE;
+  if (T > kMaxDim || H > kMaxDim || V_pad > kMaxDim) return VCE_ERR_SHAPE;
+  if (n < 1 || V_pad % n != 0) return VCE_ERR_SHARD;
+  return VCE_OK;
+}
+
+vce_status check_ignore(int32_t ignore_index, int64_t V_real) {
+  return (ignore_index >= 0 && ignore_index < V_real) ? VCE_ERR_SHAPE : VCE_OK;
+}
+
+vce_status hip_status(hipError_t e) { return e == hipSuccess ? VCE_OK : VCE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t vce_abi_version(void) { return 1; }
+
+const char* vce_strerror(vce_status s) {
+  switch (s) {
+    case VCE_OK: return "ok";
+    case VCE_ERR_NULL: return "a required pointer is NULL";
+    case VCE_ERR_SHAPE: return "invalid size argument (T, H, V_real, V_pad, P, capacity or ignore_index)";
+    case VCE_ERR_SHARD: return "num_shards must be >= 1 and divide V_pad";
+    case VCE_ERR_DTYPE: return "unknown element type or reduction";
+    case VCE_ERR_ALIGN: return "pointers must be 16-byte aligned and H a multiple of 8";
+    case VCE_ERR_WORKSPACE: return "workspace missing or smaller than the size query";
+    case VCE_ERR_HIP: return "a HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t vce_fwd_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                               int32_t num_shards, vce_dtype dt) {
+  if (check_table(T, H, V_real, V_pad, num_shards) != VCE_OK || !dtype_ok(dt)) return 0;
+  return vce::plan_fwd(T, H, V_real, V_pad, num_shards, nullptr).bytes;
+}
+
+size_t vce_bwd_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                               int32_t num_shards, vce_dtype dt) {
+  if (check_table(T, H, V_real, V_pad, num_shards) != VCE_OK || !dtype_ok(dt)) return 0;
+  return vce::plan_bwd(T, H, V_real, V_pad, num_shards, esize_of(dt), nullptr).bytes;
+}
+
+size_t vemb_bwd_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_pad) {
+  if (check_table(T, H, V_real, V_pad, 1) != VCE_OK) return 0;
+  return vce::plan_emb_bwd(T, H, V_real, nullptr).bytes;
+}
+
+size_t vss_candidates_workspace_bytes(int64_t T, int64_t V) {
+  if (T < 0 || V < 1 || T > kMaxDim || V > kMaxDim) return 0;
+  return vce::plan_cand(T, V, nullptr).bytes;
+}
+
+vce_status vce_fwd(const void* h, const void* W, const int32_t* targets, int64_t T, int64_t H,
+                   int64_t V_real, int64_t V_pad, int32_t num_shards, int32_t ignore_index,
+                   vce_dtype dt, float* lse, float* loss, float* loss_sum, int32_t* n_valid,
+                   int32_t* n_bad_target, float* shard_stats, void* ws, size_t ws_bytes,
+                   void* stream) {
+  if (!dtype_ok(dt)) return VCE_ERR_DTYPE;
+  vce_status st = check_table(T, H, V_real, V_pad, num_shards);
+  if (st != VCE_OK) return st;
+  if ((st = check_ignore(ignore_index, V_real)) != VCE_OK) return st;
+  if (!loss_sum || !n_valid || !n_bad_target) return VCE_ERR_NULL;
+  if (T > 0 && (!h || !W || !targets || !lse || !loss)) return VCE_ERR_NULL;
+  if (H % 8 != 0) return VCE_ERR_ALIGN;
+  if (T > 0 && (!aligned16(h) || !aligned16(W) || !aligned4(targets) || !aligned4(lse) ||
+                !aligned4(loss) || (shard_stats && !aligned4(shard_stats))))
+    return VCE_ERR_ALIGN;
+  if (!aligned4(loss_sum) || !aligned4(n_valid) || !aligned4(n_bad_target)) return VCE_ERR_ALIGN;
+  const vce::FwdPlan probe = vce::plan_fwd(T, H, V_real, V_pad, num_shards, nullptr);
+  if (T > 0 && (!ws || ws_bytes < probe.bytes)) return VCE_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return VCE_ERR_ALIGN;
+  const vce::FwdPlan p = vce::plan_fwd(T, H, V_real, V_pad, num_shards, ws);
+  return hip_status(vce::run_ce_fwd(h, W, targets, T, H, V_real, V_pad, num_shards, ignore_index,
+                                    dt == VCE_BF16, lse, loss, loss_sum, n_valid, n_bad_target,
+                                    shard_stats, p, static_cast<hipStream_t>(stream)));
+}
+
+vce_status vce_bwd(const void* h, const void* W, const int32_t* targets, const float* lse,
+                   const float* grad_loss, const int32_t* n_valid, vce_reduction red, int64_t T,
+                   int64_t H, int64_t V_real, int64_t V_pad, int32_t num_shards,
+                   int32_t ignore_index, vce_dtype dt, float* dh, float* dW,
+                   int32_t accumulate_dW, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dt) || (red != VCE_REDUCE_MEAN && red != VCE_REDUCE_SUM)) return VCE_ERR_DTYPE;
+  vce_status st = check_table(T, H, V_real, V_pad, num_shards);
+  if (st != VCE_OK) return st;
+  if ((st = check_ignore(ignore_index, V_real)) != VCE_OK) return st;
+  if (!dW || !grad_loss || (red == VCE_REDUCE_MEAN && !n_valid)) return VCE_ERR_NULL;
+  if (T > 0 && (!h || !W || !targets || !lse || !dh)) return VCE_ERR_NULL;
+  if (H % 8 != 0) return VCE_ERR_ALIGN;
+  if (!aligned16(dW) || !aligned4(grad_loss) || (n_valid && !aligned4(n_valid)))
+    return VCE_ERR_ALIGN;
+  if (T > 0 && (!aligned16(h) || !aligned16(W) || !aligned4(targets) || !aligned4(lse) ||
+                !aligned16(dh)))
+    return VCE_ERR_ALIGN;
+  const vce::BwdPlan probe = vce::plan_bwd(T, H, V_real, V_pad, num_shards, esize_of(dt), nullptr);
+  if (T > 0 && (!ws || ws_bytes < probe.bytes)) return VCE_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return VCE_ERR_ALIGN;
+  const vce::BwdPlan p = vce::plan_bwd(T, H, V_real, V_pad, num_shards, esize_of(dt), ws);
+  return hip_status(vce::run_ce_bwd(h, W, targets, lse, grad_loss, n_valid, red, T, H, V_real,
+                                    V_pad, num_shards, dt == VCE_BF16, dh, dW, accumulate_dW ? 1 : 0,
+                                    p, static_cast<hipStream_t>(stream)));
+}
+
+vce_status vemb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, int64_t V_real,
+                    int64_t V_pad, int32_t num_shards, vce_dtype dt, void* out, int32_t* n_bad_id,
+                    void* stream) {
+  if (!dtype_ok(dt)) return VCE_ERR_DTYPE;
+  vce_status st = check_table(T, H, V_real, V_pad, num_shards);
+  if (st != VCE_OK) return st;
+  if (T > 0 && (!ids || !W || !out)) return VCE_ERR_NULL;
+  if (H % 8 != 0) return VCE_ERR_ALIGN;
+  if (T > 0 && (!aligned4(ids) || !aligned16(W) || !aligned16(out))) return VCE_ERR_ALIGN;
+  if (n_bad_id && !aligned4(n_bad_id)) return VCE_ERR_ALIGN;
+  return hip_status(vce::run_emb_fwd(ids, W, T, H, V_real, V_pad, num_shards, esize_of(dt), out,
+                                     n_bad_id, static_cast<hipStream_t>(stream)));
+}
+
+vce_status vemb_bwd(const int32_t* ids, const void* dout, vce_dtype dout_dt, int64_t T, int64_t H,
+                    int64_t V_real, int64_t V_pad, int32_t num_shards, float* dW,
+                    int32_t accumulate, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dout_dt)) return VCE_ERR_DTYPE;
+  vce_status st = check_table(T, H, V_real, V_pad, num_shards);
+  if (st != VCE_OK) return st;
+  if (!dW) return VCE_ERR_NULL;
+  if (T > 0 && (!ids || !dout)) return VCE_ERR_NULL;
+  if (H % 8 != 0) return VCE_ERR_ALIGN;
+  if (!aligned16(dW)) return VCE_ERR_ALIGN;
+  if (T > 0 && (!aligned4(ids) || !aligned16(dout))) return VCE_ERR_ALIGN;
+  const vce::EmbBwdPlan probe = vce::plan_emb_bwd(T, H, V_real, nullptr);
+  if (T > 0 && (!ws || ws_bytes < probe.bytes)) return VCE_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return VCE_ERR_ALIGN;
+  const vce::EmbBwdPlan p = vce::plan_emb_bwd(T, H, V_real, ws);
+  return hip_status(vce::run_emb_bwd(ids, dout, dout_dt == VCE_BF16, T, H, V_real, V_pad, dW,
+                                     accumulate ? 1 : 0, p, static_cast<hipStream_t>(stream)));
+}
+
+vce_status vss_candidates(const int32_t* targets, int64_t T, int64_t V, int32_t ignore_index,
+                          const int32_t* perm, int64_t P, int32_t* cand, int64_t cand_cap,
+                          int32_t* pos, int32_t* n_unique, int32_t* n_cand, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (T < 0 || V < 1 || P < 1 || T > kMaxDim || V > kMaxDim || P > kMaxDim) return VCE_ERR_SHAPE;
+  if (check_ignore(ignore_index, V) != VCE_OK) return VCE_ERR_SHAPE;
+  const int64_t need_cap = P > (T < V ? T : V) ? P : (T < V ? T : V);
+  if (cand_cap < need_cap) return VCE_ERR_SHAPE;
+  if (!perm || !cand || !n_unique || !n_cand) return VCE_ERR_NULL;
+  if (T > 0 && (!targets || !pos)) return VCE_ERR_NULL;
+  if (!aligned4(perm) || !aligned4(cand) || !aligned4(n_unique) || !aligned4(n_cand))
+    return VCE_ERR_ALIGN;
+  if (T > 0 && (!aligned4(targets) || !aligned4(pos))) return VCE_ERR_ALIGN;
+  const vce::CandPlan probe = vce::plan_cand(T, V, nullptr);
+  if (!ws || ws_bytes < probe.bytes) return VCE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return VCE_ERR_ALIGN;
+  const vce::CandPlan p = vce::plan_cand(T, V, ws);
+  return hip_status(vce::run_candidates(targets, T, V, perm, P, cand, pos, n_unique, n_cand, p,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,427 @@
+// Cross-entropy forward and backward over a vocabulary-sharded LM head.
+//
+// Forward ("Vocabulary shards: look up locally and normalize globally", ¶3-4):
+//   1. k_gemm_tn<EPI_FWD>: every vocabulary tile of every shard computes its
+//      logits h W_tile^T with MFMA and reduces them at once to per-token
+//      (max, sum exp) over its real rows; the tile that owns a token's target
+//      stores that logit. Logits never leave registers.
+//   2. k_ce_merge: per token, the tiles of each shard are merged into the
+//      shard's (m_k, s_k) (the quantities one rank would hold), then the
+//      shards are merged into the global log-sum-exp, in a fixed order.
+//   3. k_ce_finalize: fixed-order sum of the loss and the token counts.
+// Backward (same page, ¶4): logits are recomputed tile by tile to form
+//   G = scale * (softmax - onehot), staged as bf16 (or f32) in both layouts;
+//   dh = G W and dW = G^T h are then plain MFMA GEMMs over the staged G.
+#include "gemm_tn.hpp"
+#include "vce_internal.hpp"
+
+namespace vce {
+
+// ------------------------------------------------------------------ planning
+
+static int64_t tiles_per_shard(int64_t S) { return cdiv(S, kTileM); }
+
+FwdPlan plan_fwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, void* ws) {
+  (void)H;
+  (void)V_real;
+  FwdPlan p{};
+  p.S = V_pad / n;
+  p.tiles_per_seg = tiles_per_shard(p.S);
+  p.tiles_m = p.tiles_per_seg * n;
+  p.tiles_n = cdiv(T, kTileN);
+  p.merge_blocks = cdiv(T, 256);
+  Carve c(ws);
+  p.stats = c.take<float2>(static_cast<size_t>(p.tiles_m * T));
+  p.zt = c.take<float>(static_cast<size_t>(T));
+  p.part_loss = c.take<float>(static_cast<size_t>(p.merge_blocks + 1));
+  p.part_nv = c.take<int32_t>(static_cast<size_t>(p.merge_blocks + 1));
+  p.part_nb = c.take<int32_t>(static_cast<size_t>(p.merge_blocks + 1));
+  p.bytes = c.used;
+  return p;
+}
+
+static int32_t pick_dh_splits(int64_t T, int64_t H, int64_t Kv) {
+  const int64_t tiles = cdiv(T, kTileN) * cdiv(H, kTileN);
+  int64_t s = 1;
+  while (tiles * s < 512 && s < 8 && Kv / (2 * s) >= 4 * 64) s *= 2;
+  return static_cast<int32_t>(s);
+}
+
+BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, size_t esize,
+                 void* ws) {
+  BwdPlan p{};
+  p.S = V_pad / n;
+  p.tiles_per_seg = tiles_per_shard(p.S);
+  p.tiles_m = p.tiles_per_seg * n;
+  p.tiles_n = cdiv(T, kTileN);
+  p.ldV = round_up(V_pad, 8);
+  p.ldT = round_up(T, 8);
+  p.Kv = round_up(V_real, 8);
+  p.esize = esize;
+  const int64_t slice = (esize == 2) ? 64 : 32;
+  p.dh_splits = pick_dh_splits(T, H, p.Kv);
+  p.dh_k_per_split = round_up(cdiv(p.Kv, p.dh_splits), slice);
+  Carve c(ws);
+  p.G = c.take<char>(static_cast<size_t>(T * p.ldV) * esize);
+  p.GT = c.take<char>(static_cast<size_t>(V_pad * p.ldT) * esize);
+  p.WT = c.take<char>(static_cast<size_t>(H * p.ldV) * esize);
+  p.hT = c.take<char>(static_cast<size_t>(H * p.ldT) * esize);
+  p.dh_part = (p.dh_splits > 1) ? c.take<float>(static_cast<size_t>(p.dh_splits * T * H)) : nullptr;
+  p.bytes = c.used;
+  return p;
+}
+
+// ------------------------------------------------------------------ kernels
+
+// Per token: merge the tile statistics of each shard into (m_k, s_k), then
+// the shards into the global log-sum-exp; loss = lse - target logit for
+// valid targets. Block partial sums of the loss and counts follow in a fixed
+// tree order.
+__global__ __launch_bounds__(256) void k_ce_merge(
+    const float2* __restrict__ stats, const float* __restrict__ zt,
+    const int32_t* __restrict__ targets, int64_t T, int64_t V_real, int32_t ignore_index,
+    int32_t n_seg, int64_t tiles_per_seg, float* __restrict__ lse, float* __restrict__ loss,
+    float* __restrict__ shard_stats, float* __restrict__ part_loss,
+    int32_t* __restrict__ part_nv, int32_t* __restrict__ part_nb) {
+  __shared__ float s_l[256];
+  __shared__ int32_t s_v[256], s_b[256];
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  float l = 0.0f;
+  int32_t nv = 0, nb = 0;
+  if (t < T) {
+    float M = -INFINITY, Ssum = 0.0f;
+    for (int32_t k = 0; k < n_seg; ++k) {
+      float mk = -INFINITY, sk = 0.0f;
+      const float2* st = stats + (static_cast<int64_t>(k) * tiles_per_seg) * T + t;
+      for (int64_t j = 0; j < tiles_per_seg; ++j) {
+        const float2 v = st[j * T];
+        lse_merge(mk, sk, v.x, v.y);
+      }
+      if (shard_stats) {
+        shard_stats[static_cast<int64_t>(k) * T + t] = mk;
+        shard_stats[static_cast<int64_t>(n_seg + k) * T + t] = sk;
+      }
+      lse_merge(M, Ssum, mk, sk);
+    }
+    const float L = M + logf(Ssum);
+    lse[t] = L;
+    const int64_t y = targets[t];
+    const bool valid = (y >= 0) && (y < V_real);
+    const bool bad = !valid && (y != ignore_index);
+    l = valid ? (L - zt[t]) : 0.0f;
+    loss[t] = l;
+    nv = valid ? 1 : 0;
+    nb = bad ? 1 : 0;
+  }
+  s_l[threadIdx.x] = l;
+  s_v[threadIdx.x] = nv;
+  s_b[threadIdx.x] = nb;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (static_cast<int>(threadIdx.x) < w) {
+      s_l[threadIdx.x] += s_l[threadIdx.x + w];
+      s_v[threadIdx.x] += s_v[threadIdx.x + w];
+      s_b[threadIdx.x] += s_b[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    part_loss[blockIdx.x] = s_l[0];
+    part_nv[blockIdx.x] = s_v[0];
+    part_nb[blockIdx.x] = s_b[0];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_ce_finalize(const float* __restrict__ part_loss,
+                                                     const int32_t* __restrict__ part_nv,
+                                                     const int32_t* __restrict__ part_nb,
+                                                     int64_t nparts, float* loss_sum,
+                                                     int32_t* n_valid, int32_t* n_bad) {
+  __shared__ float s_l[256];
+  __shared__ int32_t s_v[256], s_b[256];
+  float l = 0.0f;
+  int32_t nv = 0, nb = 0;
+  for (int64_t i = threadIdx.x; i < nparts; i += 256) {
+    l += part_loss[i];
+    nv += part_nv[i];
+    nb += part_nb[i];
+  }
+  s_l[threadIdx.x] = l;
+  s_v[threadIdx.x] = nv;
+  s_b[threadIdx.x] = nb;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (static_cast<int>(threadIdx.x) < w) {
+      s_l[threadIdx.x] += s_l[threadIdx.x + w];
+      s_v[threadIdx.x] += s_v[threadIdx.x + w];
+      s_b[threadIdx.x] += s_b[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    *loss_sum = s_l[0];
+    *n_valid = s_v[0];
+    *n_bad = s_b[0];
+  }
+}
+
+__global__ void k_fill_scalars(float* f0, int32_t* i0, int32_t* i1) {
+  if (threadIdx.x == 0) {
+    if (f0) *f0 = 0.0f;
+    if (i0) *i0 = 0;
+    if (i1) *i1 = 0;
+  }
+}
+
+// dst[c][r] = (r < R_valid) ? src[r][c] : 0   for c < C, r < ldR.
+// 64 x 64 tile through LDS.
+template <typename E>
+__global__ __launch_bounds__(256) void k_transpose(const E* __restrict__ src, int64_t R_valid,
+                                                   int64_t C, int64_t ld_src, E* __restrict__ dst,
+                                                   int64_t ldR) {
+  __shared__ E tile[64][65];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.y) * 64;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int rl = ty + 4 * k;
+    const int64_t r = r0 + rl, c = c0 + tx;
+    E v = E(0);
+    if (r < R_valid && c < C) v = src[r * ld_src + c];
+    tile[rl][tx] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int cl = ty + 4 * k;
+    const int64_t c = c0 + cl, r = r0 + tx;
+    if (c < C && r < ldR) dst[c * ldR + r] = tile[tx][cl];
+  }
+}
+
+// G[t][v] = 0 for v in [c0, c1) (columns past V_pad in the staged G)
+template <typename E>
+__global__ void k_zero_cols(E* G, int64_t rows, int64_t ld, int64_t c0, int64_t c1) {
+  const int64_t w = c1 - c0;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < rows * w) G[(i / w) * ld + c0 + i % w] = E(0);
+}
+
+__global__ __launch_bounds__(256) void k_zero_f4(float4* __restrict__ p, int64_t n4) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// out[i] = sum over s of part[s][i], s in increasing order
+__global__ __launch_bounds__(256) void k_splitk_sum(const float4* __restrict__ part, int64_t n4,
+                                                    int32_t splits, float4* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float4 a = part[i];
+  for (int32_t s = 1; s < splits; ++s) {
+    const float4 b = part[static_cast<int64_t>(s) * n4 + i];
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+  }
+  out[i] = a;
+}
+
+// ------------------------------------------------------------------ launchers
+
+template <typename E, int MODE>
+static hipError_t launch_gemm(const GemmShape& g, const EpiArgs& e, hipStream_t s) {
+  const int64_t blocks = static_cast<int64_t>(g.n_seg) * g.tiles_per_seg * g.tiles_n * g.k_splits;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gemm_tn<E, MODE, kTileM, kTileN>), dim3(static_cast<uint32_t>(blocks)),
+                     dim3(256), 0, s, g, e);
+  return hipGetLastError();
+}
+
+hipError_t run_fill_scalars(float* f0, int32_t* i0, int32_t* i1, hipStream_t s) {
+  hipLaunchKernelGGL(k_fill_scalars, dim3(1), dim3(64), 0, s, f0, i0, i1);
+  return hipGetLastError();
+}
+
+hipError_t run_ce_fwd(const void* h, const void* W, const int32_t* targets, int64_t T, int64_t H,
+                      int64_t V_real, int64_t V_pad, int32_t n, int32_t ignore_index, bool bf16,
+                      float* lse, float* loss, float* loss_sum, int32_t* n_valid, int32_t* n_bad,
+                      float* shard_stats, const FwdPlan& p, hipStream_t s) {
+  if (T == 0) return run_fill_scalars(loss_sum, n_valid, n_bad, s);
+  GemmShape g{};
+  g.A = W;
+  g.lda = H;
+  g.B = h;
+  g.ldb = H;
+  g.seg_len = p.S;
+  g.n_seg = n;
+  g.tiles_per_seg = static_cast<int32_t>(p.tiles_per_seg);
+  g.m_total = V_pad;
+  g.m_load_end = V_real;
+  g.n_total = T;
+  g.tiles_n = static_cast<int32_t>(p.tiles_n);
+  g.k_splits = 1;
+  g.k_total = H;
+  g.k_per_split = round_up(H, bf16 ? 64 : 32);
+  g.group_m = 8;
+  EpiArgs e{};
+  e.fwd.targets = targets;
+  e.fwd.T = T;
+  e.fwd.V_real = V_real;
+  e.fwd.stats = p.stats;
+  e.fwd.zt = p.zt;
+  hipError_t err = bf16 ? launch_gemm<uint16_t, EPI_FWD>(g, e, s) : launch_gemm<float, EPI_FWD>(g, e, s);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_ce_merge, dim3(static_cast<uint32_t>(p.merge_blocks)), dim3(256), 0, s,
+                     p.stats, p.zt, targets, T, V_real, ignore_index, n, p.tiles_per_seg, lse,
+                     loss, shard_stats, p.part_loss, p.part_nv, p.part_nb);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(k_ce_finalize, dim3(1), dim3(256), 0, s, p.part_loss, p.part_nv, p.part_nb,
+                     p.merge_blocks, loss_sum, n_valid, n_bad);
+  return hipGetLastError();
+}
+
+template <typename E>
+static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targets,
+                              const float* lse, const float* grad_loss, const int32_t* n_valid,
+                              int32_t reduction, int64_t T, int64_t H, int64_t V_real,
+                              int64_t V_pad, int32_t n, float* dh, float* dW, int32_t accumulate,
+                              const BwdPlan& p, hipStream_t s) {
+  hipError_t err;
+  constexpr int64_t slice = Elem<E>::kSlice;
+  if (T == 0) {
+    // no token: dh is empty; dW gets zeros (or is left as it is when accumulating)
+    if (!accumulate) {
+      const int64_t n4 = V_pad * H / 4;
+      hipLaunchKernelGGL(k_zero_f4, dim3(static_cast<uint32_t>(cdiv(n4, 256))), dim3(256), 0, s,
+                         reinterpret_cast<float4*>(dW), n4);
+      return hipGetLastError();
+    }
+    return hipSuccess;
+  }
+  // 1. W^T [H][ldV] with rows >= V_real zeroed, h^T [H][ldT] with tokens >= T zeroed
+  hipLaunchKernelGGL(k_transpose<E>, dim3(static_cast<uint32_t>(cdiv(p.ldV, 64)),
+                                          static_cast<uint32_t>(cdiv(H, 64))),
+                     dim3(256), 0, s, static_cast<const E*>(W), V_real, H, H,
+                     static_cast<E*>(p.WT), p.ldV);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(k_transpose<E>, dim3(static_cast<uint32_t>(cdiv(p.ldT, 64)),
+                                          static_cast<uint32_t>(cdiv(H, 64))),
+                     dim3(256), 0, s, static_cast<const E*>(h), T, H, H, static_cast<E*>(p.hT),
+                     p.ldT);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (p.ldV > V_pad) {
+    const int64_t cnt = T * (p.ldV - V_pad);
+    hipLaunchKernelGGL(k_zero_cols<E>, dim3(static_cast<uint32_t>(cdiv(cnt, 256))), dim3(256), 0,
+                       s, static_cast<E*>(p.G), T, p.ldV, V_pad, p.ldV);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  // 2. recompute logits per tile -> G, G^T
+  {
+    GemmShape g{};
+    g.A = W;
+    g.lda = H;
+    g.B = h;
+    g.ldb = H;
+    g.seg_len = p.S;
+    g.n_seg = n;
+    g.tiles_per_seg = static_cast<int32_t>(p.tiles_per_seg);
+    g.m_total = V_pad;
+    g.m_load_end = V_real;
+    g.n_total = T;
+    g.tiles_n = static_cast<int32_t>(cdiv(p.ldT, kTileN));
+    g.k_splits = 1;
+    g.k_total = H;
+    g.k_per_split = round_up(H, slice);
+    g.group_m = 8;
+    EpiArgs e{};
+    e.grad.targets = targets;
+    e.grad.lse = lse;
+    e.grad.T = T;
+    e.grad.V_real = V_real;
+    e.grad.grad_loss = grad_loss;
+    e.grad.n_valid = n_valid;
+    e.grad.reduction = reduction;
+    e.grad.vec_store = (n == 1 || p.S % 4 == 0) ? 1 : 0;
+    e.grad.G = p.G;
+    e.grad.ldG = p.ldV;
+    e.grad.GT = p.GT;
+    e.grad.ldGT = p.ldT;
+    if ((err = launch_gemm<E, EPI_GRAD>(g, e, s)) != hipSuccess) return err;
+  }
+  // 3. dh = G W  (K = real vocabulary, split into fixed partial planes)
+  {
+    GemmShape g{};
+    g.A = p.G;
+    g.lda = p.ldV;
+    g.B = p.WT;
+    g.ldb = p.ldV;
+    g.seg_len = T;
+    g.n_seg = 1;
+    g.tiles_per_seg = static_cast<int32_t>(cdiv(T, kTileM));
+    g.m_total = T;
+    g.m_load_end = T;
+    g.n_total = H;
+    g.tiles_n = static_cast<int32_t>(cdiv(H, kTileN));
+    g.k_splits = p.dh_splits;
+    g.k_total = p.Kv;
+    g.k_per_split = p.dh_k_per_split;
+    g.group_m = 8;
+    EpiArgs e{};
+    e.store.C = (p.dh_splits > 1) ? p.dh_part : dh;
+    e.store.ldc = H;
+    e.store.split_stride = T * H;
+    e.store.accumulate = 0;
+    e.store.m_zero_from = T;
+    if ((err = launch_gemm<E, EPI_STORE>(g, e, s)) != hipSuccess) return err;
+    if (p.dh_splits > 1) {
+      const int64_t n4 = T * H / 4;
+      hipLaunchKernelGGL(k_splitk_sum, dim3(static_cast<uint32_t>(cdiv(n4, 256))), dim3(256), 0,
+                         s, reinterpret_cast<const float4*>(p.dh_part), n4, p.dh_splits,
+                         reinterpret_cast<float4*>(dh));
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+  }
+  // 4. dW = G^T h  (K = tokens); rows >= V_real are 0 (or untouched when accumulating)
+  {
+    GemmShape g{};
+    g.A = p.GT;
+    g.lda = p.ldT;
+    g.B = p.hT;
+    g.ldb = p.ldT;
+    g.seg_len = V_pad;
+    g.n_seg = 1;
+    g.tiles_per_seg = static_cast<int32_t>(cdiv(V_pad, kTileM));
+    g.m_total = V_pad;
+    g.m_load_end = V_real;
+    g.n_total = H;
+    g.tiles_n = static_cast<int32_t>(cdiv(H, kTileN));
+    g.k_splits = 1;
+    g.k_total = p.ldT;
+    g.k_per_split = round_up(p.ldT, slice);
+    g.group_m = 8;
+    EpiArgs e{};
+    e.store.C = dW;
+    e.store.ldc = H;
+    e.store.split_stride = 0;
+    e.store.accumulate = accumulate;
+    e.store.m_zero_from = V_real;
+    if ((err = launch_gemm<E, EPI_STORE>(g, e, s)) != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+hipError_t run_ce_bwd(const void* h, const void* W, const int32_t* targets, const float* lse,
+                      const float* grad_loss, const int32_t* n_valid, int32_t reduction,
+                      int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, bool bf16,
+                      float* dh, float* dW, int32_t accumulate, const BwdPlan& p, hipStream_t s) {
+  if (bf16)
+    return ce_bwd_impl<uint16_t>(h, W, targets, lse, grad_loss, n_valid, reduction, T, H, V_real,
+                                 V_pad, n, dh, dW, accumulate, p, s);
+  return ce_bwd_impl<float>(h, W, targets, lse, grad_loss, n_valid, reduction, T, H, V_real, V_pad,
+                            n, dh, dW, accumulate, p, s);
+}
+
+}  // namespace vce

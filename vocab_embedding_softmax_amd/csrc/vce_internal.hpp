@@ -1,0 +1,115 @@
+// Host-side planning shared by the launchers and the C entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vce {
+
+constexpr int kTileM = 256;   // GEMM tile rows (M side)
+constexpr int kTileN = 256;   // GEMM tile columns (N side)
+constexpr int kAlign = 256;   // workspace region alignment (bytes)
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// Bump allocator over a caller-supplied workspace (or a null base, for sizing).
+struct Carve {
+  char* base;
+  size_t used = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    used = static_cast<size_t>(round_up(static_cast<int64_t>(used), kAlign));
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += count * sizeof(T);
+    return p;
+  }
+};
+
+// Forward cross-entropy plan: vocabulary tiles per shard, token tiles.
+struct FwdPlan {
+  int64_t S, tiles_per_seg, tiles_m, tiles_n, merge_blocks;
+  float2* stats;
+  float* zt;
+  float* part_loss;
+  int32_t* part_nv;
+  int32_t* part_nb;
+  size_t bytes;
+};
+FwdPlan plan_fwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, void* ws);
+
+// Backward plan: staged G (both layouts), transposed W and h, dh partials.
+struct BwdPlan {
+  int64_t S, tiles_per_seg, tiles_m, tiles_n, ldV, ldT, Kv;
+  int32_t dh_splits;
+  int64_t dh_k_per_split;
+  size_t esize;
+  void* G;
+  void* GT;
+  void* WT;
+  void* hT;
+  float* dh_part;
+  size_t bytes;
+};
+BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, size_t esize,
+                 void* ws);
+
+// Embedding backward plan (sort by ID, then segment sums).
+struct EmbBwdPlan {
+  int64_t nchunks, nslices, scan_blocks;
+  int32_t* counts;   // [V_real] occurrences of each ID
+  int32_t* offs;     // [V_real + 1] exclusive prefix of counts (offs[V_real] = total)
+  int32_t* cursor;   // [V_real] placement cursors
+  int32_t* perm;     // [T] token indices grouped by ID
+  int32_t* sorted;   // [T] token indices sorted by (ID, token)
+  int32_t* scan_tmp; // [scan_blocks + 1]
+  float* partial;    // [nchunks][2][H]
+  size_t bytes;
+};
+EmbBwdPlan plan_emb_bwd(int64_t T, int64_t H, int64_t V_real, void* ws);
+
+struct CandPlan {
+  int64_t scan_blocks_v;
+  int32_t* flags;    // [V]
+  int32_t* uidx;     // [V + 1]
+  int32_t* notin;    // [V]
+  int32_t* nidx;     // [V + 1]
+  int32_t* scan_tmp; // [scan_blocks + 1]
+  size_t bytes;
+};
+CandPlan plan_cand(int64_t T, int64_t V, void* ws);
+
+// Launchers (all enqueue on `s`; return the first launch error).
+hipError_t run_ce_fwd(const void* h, const void* W, const int32_t* targets, int64_t T, int64_t H,
+                      int64_t V_real, int64_t V_pad, int32_t n, int32_t ignore_index, bool bf16,
+                      float* lse, float* loss, float* loss_sum, int32_t* n_valid, int32_t* n_bad,
+                      float* shard_stats, const FwdPlan& p, hipStream_t s);
+
+hipError_t run_ce_bwd(const void* h, const void* W, const int32_t* targets, const float* lse,
+                      const float* grad_loss, const int32_t* n_valid, int32_t reduction,
+                      int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, bool bf16,
+                      float* dh, float* dW, int32_t accumulate, const BwdPlan& p, hipStream_t s);
+
+hipError_t run_emb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, int64_t V_real,
+                       int64_t V_pad, int32_t n, size_t esize, void* out, int32_t* n_bad,
+                       hipStream_t s);
+
+hipError_t run_emb_bwd(const int32_t* ids, const void* dout, bool dout_bf16, int64_t T, int64_t H,
+                       int64_t V_real, int64_t V_pad, float* dW, int32_t accumulate,
+                       const EmbBwdPlan& p, hipStream_t s);
+
+hipError_t run_candidates(const int32_t* targets, int64_t T, int64_t V, const int32_t* perm,
+                          int64_t P, int32_t* cand, int32_t* pos, int32_t* n_unique,
+                          int32_t* n_cand, const CandPlan& p, hipStream_t s);
+
+hipError_t run_fill_scalars(float* f0, int32_t* i0, int32_t* i1, hipStream_t s);
+
+// Exclusive scan of n int32 values: y[i] = sum x[0..i), y[n] = total.
+// tmp holds scan_blocks(n) + 1 ints.
+int64_t scan_blocks(int64_t n);
+hipError_t run_scan(const int32_t* x, int64_t n, int32_t* y, int32_t* y_copy, int32_t* tmp,
+                    hipStream_t s);
+
+}  // namespace vce

@@ -1,0 +1,95 @@
+"""Whole steps of the path as sequences of library calls (no arithmetic here).
+
+ce_step       cross-entropy forward + backward on (h, W, targets)
+tied_step     lookup -> cross-entropy forward/backward -> scatter-add of dh
+              into the same dW ("Vocabulary shards: look up locally and
+              normalize globally", ¶2: one tied table, all contributions)
+sampled_step  candidates -> lookup of the candidate rows -> cross-entropy over
+              them -> scatter of their gradients into the full table
+              ("Sampled Softmax with Over-Tokenized Transformer", Setup)
+"""
+
+from __future__ import annotations
+
+from collections import namedtuple
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+StepOut = namedtuple("StepOut", "fwd dh dW extra")
+
+
+def from_bits(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Host array -> GPU tensor holding the same bits (uint16 bf16 bits or float32)."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    raise ValueError(dtype)
+
+
+class Workspaces:
+    """Device workspaces sized once for a step shape and reused by every call."""
+
+    def __init__(self, device, **sizes):
+        self.buf = {k: torch.empty(max(int(v), 16), dtype=torch.uint8, device=device)
+                    for k, v in sizes.items()}
+
+    def __getitem__(self, k):
+        return self.buf[k]
+
+
+def ce_step(h, W, targets, V_real, num_shards, ignore_index=-100, *, grad_loss=None,
+            reduction=L.REDUCE_MEAN, ws: Optional[Workspaces] = None, dh=None, dW=None,
+            shard_stats=False, stream=None) -> StepOut:
+    dev = h.device
+    if grad_loss is None:
+        grad_loss = torch.ones(1, dtype=torch.float32, device=dev)
+    f = L.vce_fwd(h, W, targets, V_real, num_shards, ignore_index, shard_stats=shard_stats,
+                  ws=None if ws is None else ws["fwd"], stream=stream)
+    b = L.vce_bwd(h, W, targets, f.lse, grad_loss, f.n_valid, V_real, num_shards, ignore_index,
+                  reduction, dh=dh, dW=dW, ws=None if ws is None else ws["bwd"], stream=stream)
+    return StepOut(f, b.dh, b.dW, None)
+
+
+def tied_step(ids, targets, W, V_real, num_shards, ignore_index=-100, *, grad_loss=None,
+              reduction=L.REDUCE_MEAN, ws: Optional[Workspaces] = None, h=None, dh=None,
+              dW=None, stream=None) -> StepOut:
+    dev = W.device
+    if grad_loss is None:
+        grad_loss = torch.ones(1, dtype=torch.float32, device=dev)
+    h, n_bad_id = L.vemb_fwd(ids, W, V_real, num_shards, out=h, stream=stream)
+    f = L.vce_fwd(h, W, targets, V_real, num_shards, ignore_index,
+                  ws=None if ws is None else ws["fwd"], stream=stream)
+    b = L.vce_bwd(h, W, targets, f.lse, grad_loss, f.n_valid, V_real, num_shards, ignore_index,
+                  reduction, dh=dh, dW=dW, accumulate_dW=False,
+                  ws=None if ws is None else ws["bwd"], stream=stream)
+    L.vemb_bwd(ids, b.dh, V_real, W.shape[0], num_shards, dW=b.dW, accumulate=True,
+               ws=None if ws is None else ws["emb"], stream=stream)
+    return StepOut(f, b.dh, b.dW, dict(h=h, n_bad_id=n_bad_id))
+
+
+def sampled_step(h, W, targets, perm, P, ignore_index=-100, *, grad_loss=None,
+                 reduction=L.REDUCE_MEAN, ws: Optional[Workspaces] = None, dW=None,
+                 stream=None) -> StepOut:
+    """Assumes the batch has at most P distinct targets (then n_cand == P); the
+    caller can check extra['n_cand'] afterwards."""
+    dev = h.device
+    V, H = W.shape
+    if grad_loss is None:
+        grad_loss = torch.ones(1, dtype=torch.float32, device=dev)
+    c = L.vss_candidates(targets, V, perm, P, ignore_index,
+                         ws=None if ws is None else ws["cand"], stream=stream)
+    cand = c.cand[:P]
+    Wc, _ = L.vemb_fwd(cand, W, V, 1, count_bad=False, stream=stream)
+    f = L.vce_fwd(h, Wc, c.pos, P, 1, ignore_index, ws=None if ws is None else ws["fwd"],
+                  stream=stream)
+    b = L.vce_bwd(h, Wc, c.pos, f.lse, grad_loss, f.n_valid, P, 1, ignore_index, reduction,
+                  ws=None if ws is None else ws["bwd"], stream=stream)
+    dW = L.vemb_bwd(cand, b.dW, V, V, 1, dW=dW, accumulate=False,
+                    ws=None if ws is None else ws["emb"], stream=stream)
+    return StepOut(f, b.dh, dW, dict(cand=c.cand, pos=c.pos, n_unique=c.n_unique,
+                                     n_cand=c.n_cand, Wc=Wc, dWc=b.dW))
