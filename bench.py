@@ -43,8 +43,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4", choices=["c3", "c4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=256,
+    ap.add_argument("--cpu-tokens", type=int, default=512,
                     help="tokens in the oracle's CPU-baseline sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one elementwise pass over 1 GiB (read 1 GiB, write 1 GiB): "
+                         "the reference kernel that calibrates FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -196,6 +199,14 @@ def main():
         "path_mfma_frac": path_frac,
         "phases_ms": phase,
     }
+    if a.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        res["copy_probe_bytes"] = src.numel() * 4
+        del src, dst
     del ws, dh, dW, W, h
     torch.cuda.empty_cache()
     if not a.no_cpu_baseline:

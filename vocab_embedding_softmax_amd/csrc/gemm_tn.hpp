@@ -7,17 +7,23 @@
 //             (token-major and vocabulary-major) in the input element type
 //   EPI_STORE plain float32 store / accumulate (dh and dW)
 //
-// Workgroup: 256 threads = 4 waves in a 2 x 2 grid over a BM x BN tile; each
-// wave owns a (BM/2) x (BN/2) sub-tile made of 32 x 32 MFMA blocks. K advances
-// in 128-byte slices (64 bf16 or 32 float), staged in LDS by direct
+// Workgroup: WAVES_M x WAVES_N waves over a BM x BN tile; each wave owns a
+// (BM/WAVES_M) x (BN/WAVES_N) sub-tile made of 32 x 32 MFMA blocks. K
+// advances in 128-byte slices (64 bf16 or 32 float), staged in LDS by direct
 // global->LDS loads (global_load_lds_dwordx4), two stages deep. Each LDS row
-// holds one 128-byte K slice of one operand row, its 16-byte chunks permuted
-// by an XOR of the row index so that the fragment reads of 32 consecutive
-// rows spread over all banks.
+// holds one 128-byte K slice of one operand row, its eight 16-byte chunks
+// permuted by ((row >> 1) & 7): the 16 lanes that one LDS cycle serves read 16
+// consecutive rows, which then cover all 64 banks exactly once.
+//
+// Operand rows past the valid range are loaded from a clamped (valid) row and
+// their results are discarded by the epilogues; only a K slice that runs past
+// K reads zeros for the missing chunks, so garbage never enters a valid sum.
 //
 // The M side can be cut into equal segments (the vocabulary shards): tiles
 // never cross a segment end, so every tile computes with one shard's rows.
 #pragma once
+
+#include <type_traits>
 
 #include "vce_device.hpp"
 
@@ -34,7 +40,7 @@ struct GemmShape {
   int32_t n_seg;        // number of M segments
   int32_t tiles_per_seg;
   int64_t m_total;      // tile ends are clipped to this
-  int64_t m_load_end;   // A rows at or past this are never read (loaded as zeros)
+  int64_t m_load_end;   // A rows at or past this are never read
   int64_t n_total;      // B rows at or past this are never read
   int32_t tiles_n;
   int32_t k_splits;     // split of K into independent partial products
@@ -80,7 +86,7 @@ struct EpiArgs {
   StoreArgs store;
 };
 
-// 16 zero bytes: the source of every masked chunk (rows or K past the end)
+// 16 zero bytes: the source of the chunks of a K slice that lie past K
 static __device__ __attribute__((aligned(64))) const uint32_t g_zero_chunk[16] = {0};
 
 template <typename E>
@@ -96,8 +102,20 @@ struct Elem<float> {
   static constexpr int kChunk = 4;
 };
 
-// chunk permutation of LDS row `row`
-__device__ __forceinline__ int lds_swz(int row) { return row & 7; }
+// Chunk permutation of LDS row `row` for rows of RB bytes (8 or 4 chunks):
+// the 16 lanes of one LDS cycle read 16 consecutive rows at one logical
+// chunk, and the permutation spreads them over all 64 banks.
+template <int RB>
+__device__ __forceinline__ int lds_swz(int row) {
+  return RB == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
+
+// s_waitcnt vmcnt(N) with the other counters left free (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 template <typename E>
 __device__ __forceinline__ void mma_chunk(f32x16& acc, const u32x4& a, const u32x4& b);
@@ -122,274 +140,451 @@ __device__ __forceinline__ void mma_chunk<float>(f32x16& acc, const u32x4& a, co
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Stage ROWS operand rows x one 128-byte K slice into LDS at `dst`.
-// Wave w moves rows [(q*4 + w)*8, +8) for q = 0..ROWS/32-1: lane l brings the
-// 16-byte chunk (l & 7) ^ swz(row) of row (l >> 3), written to LDS at
-// dst + row*128 + (l & 7)*16 (the LDS side of these loads is lane-linear).
-template <typename E, int ROWS>
-__device__ __forceinline__ void stage_rows(char* dst, const E* src, int64_t ld, int64_t row0,
-                                           int64_t row_end, int64_t k, int64_t k_end,
-                                           int wave, int lane) {
-  constexpr int EPC = Elem<E>::kChunk;
+// Per-lane byte offsets (relative to the tile's first row and current K) of
+// the chunks this lane brings into LDS for ROWS operand rows of RB-byte K
+// slices. One wave-wide load moves 1 KB = RPI rows: wave w, load q moves tile
+// rows [(q*NW + w)*RPI, +RPI); lane l brings chunk (l % CPR) ^ swz(row) of row
+// l / CPR, landing at LDS row*RB + (l % CPR)*16 (lane-linear).
+template <int ROWS, int NW, int RB>
+struct RowLoads {
+  static constexpr int CPR = RB / 16;     // chunks per row
+  static constexpr int RPI = 64 / CPR;    // rows per wave-wide load
+  static constexpr int Q = ROWS / (RPI * NW);
+  static_assert(ROWS % (RPI * NW) == 0, "load split");
+  uint32_t off[Q];     // byte offset of the chunk in global memory
+  uint32_t kchunk[Q];  // element offset of the chunk inside the K slice
+
+  template <int EPC>
+  __device__ __forceinline__ void init(int64_t row0, int64_t row_end, int64_t ld, int wave,
+                                       int lane, int esize) {
 #pragma unroll
-  for (int q = 0; q < ROWS / 32; ++q) {
-    const int r0 = (q * 4 + wave) * 8;
-    const int row = r0 + (lane >> 3);
-    const int lch = (lane & 7) ^ lds_swz(row);
-    const int64_t grow = row0 + row;
-    const int64_t gk = k + static_cast<int64_t>(lch) * EPC;
-    const void* p = (grow < row_end && gk < k_end)
-                        ? static_cast<const void*>(src + grow * ld + gk)
-                        : static_cast<const void*>(g_zero_chunk);
-    __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(dst + r0 * 128), 16, 0, 0);
+    for (int q = 0; q < Q; ++q) {
+      const int r = (q * NW + wave) * RPI + lane / CPR;
+      const int lch = (lane % CPR) ^ lds_swz<RB>(r);
+      int64_t gr = row0 + r;
+      if (gr >= row_end) gr = row_end - 1;  // clamp: the result of this row is discarded
+      off[q] = static_cast<uint32_t>(((gr - row0) * ld + lch * EPC) * esize);
+      kchunk[q] = static_cast<uint32_t>(lch * EPC);
+    }
+  }
+
+  // stage one K slice: `base` points at (row0, k); `kleft` = K elements left
+  // from k (only consulted for a slice that runs past K)
+  template <int Q0 = 0, int Q1 = Q>
+  __device__ __forceinline__ void issue(char* lds, const char* base, int64_t kleft,
+                                        int wave) const {
+#pragma unroll
+    for (int q = Q0; q < (Q1 < Q ? Q1 : Q); ++q) {
+      const void* p = base + off[q];
+      if (static_cast<int64_t>(kchunk[q]) >= kleft) p = g_zero_chunk;
+      __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(lds + (q * NW + wave) * RPI * RB), 16, 0,
+                                       0);
+    }
+  }
+};
+
+// Compile-time loop: f(integral_constant<int, I>) for I in [I0, N)
+template <int I0, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I0 < N) {
+    f(std::integral_constant<int, I0>{});
+    static_for<I0 + 1, N>(f);
   }
 }
 
-template <typename E, int MODE, int BM, int BN>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void k_gemm_tn(GemmShape g, EpiArgs e) {
-  constexpr int BK = Elem<E>::kSlice;
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int MI = WM / 32, NI = WN / 32;
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile sizes");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+// Geometry of one output tile.
+struct TileGeom {
+  int64_t tm;      // tile index along M (segment-major)
+  int64_t ks;      // K split
+  int64_t m0, m_end, m_load, n0, n_end, k_beg, k_end;
+  __device__ __forceinline__ bool active() const {
+    return m_load > m0 && n_end > n0 && k_end > k_beg;
+  }
+};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int half = lane >> 5, l32 = lane & 31;
-
-  // ---- which tile
+// Logical tile L -> tile: K split outermost, then groups of group_m tiles
+// along M, each group walking all tiles along N.
+template <int BM, int BN>
+__device__ __forceinline__ TileGeom decode_tile(const GemmShape& g, int64_t L) {
   const int64_t tiles_m = static_cast<int64_t>(g.n_seg) * g.tiles_per_seg;
   const int64_t per_split = tiles_m * g.tiles_n;
-  const int64_t total = per_split * g.k_splits;
-  const int64_t L = xcd_logical_block(blockIdx.x, total);
-  const int64_t ks = L / per_split;
-  const int64_t rem = L - ks * per_split;
+  TileGeom t;
+  t.ks = L / per_split;
+  const int64_t rem = L - t.ks * per_split;
   const int64_t in_group = static_cast<int64_t>(g.group_m) * g.tiles_n;
   const int64_t grp = rem / in_group;
   const int64_t first_m = grp * g.group_m;
   const int64_t gsz = min(static_cast<int64_t>(g.group_m), tiles_m - first_m);
   const int64_t r_in = rem - grp * in_group;
-  const int64_t tm = first_m + r_in % gsz;
+  t.tm = first_m + r_in % gsz;
   const int64_t tn = r_in / gsz;
-  const int64_t seg = tm / g.tiles_per_seg;
-  const int64_t tj = tm - seg * g.tiles_per_seg;
-  const int64_t m0 = seg * g.seg_len + tj * BM;
-  const int64_t m_end = min(min(m0 + BM, (seg + 1) * g.seg_len), g.m_total);
-  const int64_t m_load = min(m_end, g.m_load_end);
-  const int64_t n0 = tn * BN;
-  const int64_t n_end = min(n0 + static_cast<int64_t>(BN), g.n_total);
-  const int64_t k_beg = ks * g.k_per_split;
-  const int64_t k_end = min(k_beg + g.k_per_split, g.k_total);
+  const int64_t seg = t.tm / g.tiles_per_seg;
+  const int64_t tj = t.tm - seg * g.tiles_per_seg;
+  t.m0 = seg * g.seg_len + tj * BM;
+  t.m_end = min(min(t.m0 + BM, (seg + 1) * g.seg_len), g.m_total);
+  t.m_load = min(t.m_end, g.m_load_end);
+  t.n0 = tn * BN;
+  t.n_end = min(t.n0 + static_cast<int64_t>(BN), g.n_total);
+  t.k_beg = t.ks * g.k_per_split;
+  t.k_end = min(t.k_beg + g.k_per_split, g.k_total);
+  return t;
+}
+
+// Persistent GEMM: the grid holds a multiple of 8 workgroups (one per CU).
+// Workgroups are handed to the 8 XCDs round-robin, so the workgroups of one
+// XCD (blockIdx % 8 equal) take one contiguous range of logical tiles and walk
+// it together, sharing operand tiles in that XCD's L2. While a tile's
+// epilogue runs, the first K slices of the workgroup's next tile are already
+// on their way into LDS.
+template <typename E, int MODE, int BM, int BN, int WAVES_M, int WAVES_N, int RB, int NS, int OCC>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N,
+                                                      64 * WAVES_M * WAVES_N),
+                          amdgpu_waves_per_eu(OCC, OCC)))
+void k_gemm_tn(GemmShape g, EpiArgs e) {
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int NT = 64 * NW;
+  constexpr int ES = sizeof(E);
+  constexpr int BK = RB / ES;              // K elements per slice
+  constexpr int EPC = Elem<E>::kChunk;
+  constexpr int SS = RB / 32;              // sub-steps per slice (two chunks each)
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int MI = WM / 32, NI = WN / 32;
+  constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
+  static_assert(NS >= 2, "stages");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+  __shared__ float2 red[MODE == EPI_FWD ? WAVES_M * BN : 1];
+
+  using LA = RowLoads<BM, NW, RB>;
+  using LB = RowLoads<BN, NW, RB>;
+  constexpr int LOADS = LA::Q + LB::Q;  // VMEM instructions per slice per wave
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int half = lane >> 5, l32 = lane & 31;
+
+  // ---- this workgroup's tiles: L = start + wi, start + wi + per_xcd, ... < end
+  const int64_t tiles_m = static_cast<int64_t>(g.n_seg) * g.tiles_per_seg;
+  const int64_t total = tiles_m * g.tiles_n * g.k_splits;
+  const int64_t xcd = blockIdx.x & 7;
+  const int64_t wi = blockIdx.x >> 3;
+  const int64_t per_xcd = gridDim.x >> 3;
+  const int64_t q8 = total >> 3, r8 = total & 7;
+  const int64_t start = xcd * q8 + min(xcd, r8);
+  const int64_t end = start + q8 + (xcd < r8 ? 1 : 0);
+  int64_t L = start + wi;
+  if (L >= end) return;
+
+  // per-tile load state
+  LA la;
+  LB lb;
+  const char* Ab = nullptr;
+  const char* Bb = nullptr;
+  int64_t klen = 0;
+  int nk = 0;
+  auto setup = [&](const TileGeom& t) {
+    la.template init<EPC>(t.m0, t.m_load, g.lda, wave, lane, ES);
+    lb.template init<EPC>(t.n0, t.n_end, g.ldb, wave, lane, ES);
+    Ab = static_cast<const char*>(g.A) + (t.m0 * g.lda + t.k_beg) * ES;
+    Bb = static_cast<const char*>(g.B) + (t.n0 * g.ldb + t.k_beg) * ES;
+    klen = t.k_end - t.k_beg;
+    nk = t.active() ? static_cast<int>((klen + BK - 1) / BK) : 0;
+  };
+  auto issue = [&](int kt) {
+    char* st = smem + (kt % NS) * STAGE;
+    const int64_t kleft = klen - static_cast<int64_t>(kt) * BK;
+    const char* a = Ab + static_cast<int64_t>(kt) * BK * ES;
+    const char* b = Bb + static_cast<int64_t>(kt) * BK * ES;
+    la.issue(st, a, kleft, wave);
+    lb.issue(st + A_BYTES, b, kleft, wave);
+  };
+  auto prologue = [&]() {
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+      if (p < nk) issue(p);
+    asm volatile("" ::"r"(smem) : "memory");
+  };
+
+
+  // fragment rows of this lane inside a stage; the chunk depends on the sub-step
+  const int rowA = (wm * WM + l32) * RB;
+  const int rowB = A_BYTES + (wn * WN + l32) * RB;
+  const int swz = lds_swz<RB>(l32);
+
+  TileGeom cur = decode_tile<BM, BN>(g, L);
+  setup(cur);
+  prologue();
 
   f32x16 acc[MI][NI];
+  while (true) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
+      for (int j = 0; j < NI; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const E* Ap = static_cast<const E*>(g.A);
-  const E* Bp = static_cast<const E*>(g.B);
-
-  if (m_load > m0 && k_end > k_beg) {
-    const int nk = static_cast<int>((k_end - k_beg + BK - 1) / BK);
-    stage_rows<E, BM>(smem, Ap, g.lda, m0, m_load, k_beg, k_end, wave, lane);
-    stage_rows<E, BN>(smem + A_BYTES, Bp, g.ldb, n0, n_end, k_beg, k_end, wave, lane);
-    asm volatile("" ::"r"(smem) : "memory");
-    for (int kt = 0; kt < nk; ++kt) {
-      __syncthreads();  // stage kt has landed; nobody still reads stage kt+1
-      if (kt + 1 < nk) {
-        char* nxt = smem + ((kt + 1) & 1) * STAGE;
-        const int64_t kk = k_beg + static_cast<int64_t>(kt + 1) * BK;
-        stage_rows<E, BM>(nxt, Ap, g.lda, m0, m_load, kk, k_end, wave, lane);
-        stage_rows<E, BN>(nxt + A_BYTES, Bp, g.ldb, n0, n_end, kk, k_end, wave, lane);
-      }
+    // One K slice: wait for it, queue slice kt + NS - 1 (unless past the end),
+    // then run the slice's MFMAs interleaved one-for-one with the next
+    // sub-step's fragment reads.
+    auto kstep = [&](int kt, auto issue_next) {
+      constexpr bool ISSUE = decltype(issue_next)::value;
+      if constexpr (ISSUE)
+        wait_vmcnt<(NS - 2) * LOADS>();
+      else
+        wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();  // every wave's part of slice kt is in; slice kt-1 is free
       asm volatile("" ::"r"(smem) : "memory");
-      const char* sA = smem + (kt & 1) * STAGE + wm * WM * 128;
-      const char* sB = smem + (kt & 1) * STAGE + A_BYTES + wn * WN * 128;
+      if constexpr (ISSUE) issue(kt + NS - 1);
+      asm volatile("" ::"r"(smem) : "memory");
+      const char* st = smem + (kt % NS) * STAGE;
+      u32x4 fa[2][MI], fb[2][NI];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int ch = ((2 * s + half) ^ lds_swz(l32)) * 16;
-        u32x4 a[MI], b[NI];
+      for (int s = 0; s < SS; ++s) {
+        const int cb = s & 1;
+        if (s == 0) {
+          const int ch = (half ^ swz) * 16;
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            fa[0][i] = *reinterpret_cast<const u32x4*>(st + rowA + i * 32 * RB + ch);
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+            fb[0][j] = *reinterpret_cast<const u32x4*>(st + rowB + j * 32 * RB + ch);
+        }
+        if (s + 1 < SS) {  // next sub-step's fragments, in flight during this one's MFMAs
+          const int chn = ((2 * (s + 1) + half) ^ swz) * 16;
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            fa[cb ^ 1][i] = *reinterpret_cast<const u32x4*>(st + rowA + i * 32 * RB + chn);
+#pragma unroll
+          for (int j = 0; j < NI; ++j)
+            fb[cb ^ 1][j] = *reinterpret_cast<const u32x4*>(st + rowB + j * 32 * RB + chn);
+        }
 #pragma unroll
         for (int i = 0; i < MI; ++i)
-          a[i] = *reinterpret_cast<const u32x4*>(sA + (i * 32 + l32) * 128 + ch);
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
-          b[j] = *reinterpret_cast<const u32x4*>(sB + (j * 32 + l32) * 128 + ch);
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NI; ++j) mma_chunk<E>(acc[i][j], a[i], b[j]);
+          for (int j = 0; j < NI; ++j) mma_chunk<E>(acc[i][j], fa[cb][i], fb[cb][j]);
       }
+      constexpr int NF = MI + NI;                              // fragment reads per sub-step
+      constexpr int NMF = MI * NI * (sizeof(E) == 2 ? 1 : 4);  // MFMAs per sub-step
+      __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
+#pragma unroll
+      for (int s = 0; s + 1 < SS; ++s) {
+#pragma unroll
+        for (int k = 0; k < NF; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF - NF, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+    };
+
+    if (nk > 0) {
+      int kt = 0;
+      for (; kt + NS - 1 < nk; ++kt) kstep(kt, std::true_type{});
+      for (; kt < nk; ++kt) kstep(kt, std::false_type{});
     }
-  }
 
-  // Row of accumulator element r of block i (relative to the wave tile):
-  //   i*32 + 8*(r/4) + 4*half + r%4 ;  its column: j*32 + l32.
-  const int64_t vbase = m0 + wm * WM;
-
-  if constexpr (MODE == EPI_FWD) {
-    const FwdArgs& f = e.fwd;
-    const int64_t vend = m_load;  // real rows of this tile end here (m_load_end = V_real)
-    const bool full = vbase + WM <= vend;
-    __syncthreads();  // all waves are done with the operand stages
-    float2* red = reinterpret_cast<float2*>(smem);  // [2][BN]
+    // Per-token epilogue inputs of the finished tile, fetched before the next
+    // tile's loads are queued (vector loads complete in issue order).
+    int32_t yv[NI];
+    float lv[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      float m = -INFINITY;
+      const int64_t tt = cur.n0 + wn * WN + j * 32 + l32;
+      yv[j] = -1;
+      lv[j] = 0.0f;
+      if constexpr (MODE == EPI_FWD) {
+        if (tt < e.fwd.T) yv[j] = e.fwd.targets[tt];
+      } else if constexpr (MODE == EPI_GRAD) {
+        if (tt < e.grad.T) {
+          yv[j] = e.grad.targets[tt];
+          lv[j] = e.grad.lse[tt];
+        }
+      }
+    }
+
+    // every wave is done with the stage buffers: start the next tile's loads
+    __syncthreads();
+    const int64_t Ln = L + per_xcd;
+    const bool has_next = Ln < end;
+    const TileGeom t = cur;
+    if (has_next) {
+      cur = decode_tile<BM, BN>(g, Ln);
+      setup(cur);
+      prologue();
+    }
+
+    // ---------------------------------------------------------------- epilogue
+    // Row of accumulator element r of block i (relative to the wave tile):
+    //   i*32 + 8*(r/4) + 4*half + r%4 ;  its column: j*32 + l32.
+    const int64_t vbase = t.m0 + wm * WM;
+
+    if constexpr (MODE == EPI_FWD) {
+      const FwdArgs& f = e.fwd;
+      // real rows of this wave's sub-tile: local rows [0, lim)  (m_load_end = V_real)
+      const int lim = static_cast<int>(max(min(t.m_load - vbase, static_cast<int64_t>(WM)),
+                                           static_cast<int64_t>(0)));
+      const bool full = lim == WM;
+      if (!full) {  // rows past the real vocabulary (or the shard) take no part
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (i * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= lim) acc[i][j][r] = -INFINITY;
+      }
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[i][j][r]);
+        m = fmaxf(m, __shfl_xor(m, 32));
+        float s = 0.0f;
+        if (m != -INFINITY) {
+          const float mb = m * kLog2e;
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s += fast_exp2(fmaf(acc[i][j][r], kLog2e, -mb));
+        }
+        s += __shfl_xor(s, 32);
+        const int col = wn * WN + j * 32 + l32;
+        if (half == 0) red[wm * BN + col] = make_float2(m, s);
+
+        // the owning tile stores the target logit
+        const int64_t dy = static_cast<int64_t>(yv[j]) - vbase;
+        const bool mine = yv[j] >= 0 && dy >= 0 && dy < lim;
+        if (__any(mine)) {
+          const int loc = static_cast<int>(mine ? dy : 0);
+          float val = 0.0f;
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              val = (i * 32 + 8 * (r >> 2) + 4 * half + (r & 3) == loc) ? acc[i][j][r] : val;
+          if (mine && ((loc >> 2) & 1) == half) f.zt[t.n0 + col] = val;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+      for (int c = tid; c < BN; c += NT) {
+        const int64_t tt = t.n0 + c;
+        if (tt < f.T) {
+          float2 a = red[c];
+#pragma unroll
+          for (int w = 1; w < WAVES_M; ++w) {
+            const float2 b = red[w * BN + c];
+            lse_merge(a.x, a.y, b.x, b.y);
+          }
+          f.stats[t.tm * f.T + tt] = a;
+        }
+      }
+      __syncthreads();  // red is reused by the next tile
+    } else if constexpr (MODE == EPI_GRAD) {
+      const GradArgs& gr = e.grad;
+      const float scale = (gr.reduction == 0)
+                              ? gr.grad_loss[0] / static_cast<float>(max(gr.n_valid[0], 1))
+                              : gr.grad_loss[0];
+      const int64_t vreal_end = min(t.m_end, gr.V_real);
+      E* Gp = static_cast<E*>(gr.G);
+      E* GTp = static_cast<E*>(gr.GT);
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int64_t tt = t.n0 + wn * WN + j * 32 + l32;
+        const bool tin = tt < gr.T;
+        const int64_t y = yv[j];
+        const bool valid = tin && y >= 0 && y < gr.V_real;
+        const float nl = lv[j] * kLog2e;
+        const bool t_gt = tt < gr.ldGT;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t v0 = vbase + i * 32 + 8 * q + 4 * half;
+            float gv[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const int64_t v = v0 + c;
+              const float p = fast_exp2(fmaf(acc[i][j][4 * q + c], kLog2e, -nl));
+              const float oh = (v == y) ? 1.0f : 0.0f;
+              // select, never multiply, so a non-finite p of a discarded entry cannot leak
+              gv[c] = (valid && v < vreal_end) ? scale * (p - oh) : 0.0f;
+            }
+            if constexpr (sizeof(E) == 2) {
+              uint16_t hb[4];
+#pragma unroll
+              for (int c = 0; c < 4; ++c) hb[c] = f32_to_bf16(gv[c]);
+              if (tin) {
+                if (gr.vec_store && v0 + 3 < t.m_end) {
+                  u32x2 pk;
+                  pk.x = static_cast<uint32_t>(hb[0]) | (static_cast<uint32_t>(hb[1]) << 16);
+                  pk.y = static_cast<uint32_t>(hb[2]) | (static_cast<uint32_t>(hb[3]) << 16);
+                  *reinterpret_cast<u32x2*>(Gp + tt * gr.ldG + v0) = pk;
+                } else {
+#pragma unroll
+                  for (int c = 0; c < 4; ++c)
+                    if (v0 + c < t.m_end) Gp[tt * gr.ldG + v0 + c] = hb[c];
+                }
+              }
+              if (t_gt) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                  if (v0 + c < t.m_end) GTp[(v0 + c) * gr.ldGT + tt] = hb[c];
+              }
+            } else {
+              if (tin) {
+                if (gr.vec_store && v0 + 3 < t.m_end) {
+                  f32x4 pk = {gv[0], gv[1], gv[2], gv[3]};
+                  *reinterpret_cast<f32x4*>(Gp + tt * gr.ldG + v0) = pk;
+                } else {
+#pragma unroll
+                  for (int c = 0; c < 4; ++c)
+                    if (v0 + c < t.m_end) Gp[tt * gr.ldG + v0 + c] = gv[c];
+                }
+              }
+              if (t_gt) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                  if (v0 + c < t.m_end) GTp[(v0 + c) * gr.ldGT + tt] = gv[c];
+              }
+            }
+          }
+      }
+    } else {  // EPI_STORE
+      const StoreArgs& st = e.store;
+      float* Cp = st.C + t.ks * st.split_stride;
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t v = vbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (full || v < vend) m = fmaxf(m, acc[i][j][r]);
-        }
-      m = fmaxf(m, __shfl_xor(m, 32));
-      float s = 0.0f;
-      if (m != -INFINITY) {
-        const float mb = m * kLog2e;
+          const int64_t m = vbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (m >= t.m_end) continue;
+          const bool zero_row = m >= st.m_zero_from;
+          if (zero_row && st.accumulate) continue;
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t v = vbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (full || v < vend) s += fast_exp2(fmaf(acc[i][j][r], kLog2e, -mb));
+          for (int j = 0; j < NI; ++j) {
+            const int64_t n = t.n0 + wn * WN + j * 32 + l32;
+            if (n >= t.n_end) continue;
+            float* dst = Cp + m * st.ldc + n;
+            const float v = zero_row ? 0.0f : acc[i][j][r];
+            if (st.accumulate)
+              *dst += v;
+            else
+              *dst = v;
           }
-      }
-      s += __shfl_xor(s, 32);
-      const int col = wn * WN + j * 32 + l32;
-      if (half == 0) red[wm * BN + col] = make_float2(m, s);
+        }
+    }
 
-      // the owning tile stores the target logit
-      const int64_t t = n0 + col;
-      const int64_t y = (t < f.T) ? static_cast<int64_t>(f.targets[t]) : -1;
-      const bool mine = (y >= vbase) && (y < vbase + WM) && (y < vend);
-      if (__any(mine)) {
-        const int64_t loc = y - vbase;
-        float val = 0.0f;
-        bool hit = false;
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int lr = i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (mine && loc == lr) {
-              val = acc[i][j][r];
-              hit = true;
-            }
-          }
-        if (hit) f.zt[t] = val;
-      }
-    }
-    __syncthreads();
-    if (tid < BN) {
-      const int64_t t = n0 + tid;
-      if (t < f.T) {
-        float2 a = red[tid];
-        const float2 b = red[BN + tid];
-        lse_merge(a.x, a.y, b.x, b.y);
-        f.stats[tm * f.T + t] = a;
-      }
-    }
-  } else if constexpr (MODE == EPI_GRAD) {
-    const GradArgs& gr = e.grad;
-    const float scale = (gr.reduction == 0)
-                            ? gr.grad_loss[0] / static_cast<float>(max(gr.n_valid[0], 1))
-                            : gr.grad_loss[0];
-    const int64_t vreal_end = min(m_end, gr.V_real);
-    E* Gp = static_cast<E*>(gr.G);
-    E* GTp = static_cast<E*>(gr.GT);
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int64_t t = n0 + wn * WN + j * 32 + l32;
-      const bool tin = t < gr.T;
-      const int64_t y = tin ? static_cast<int64_t>(gr.targets[t]) : -1;
-      const bool valid = tin && y >= 0 && y < gr.V_real;
-      const float coef = valid ? scale : 0.0f;
-      const float nl = tin ? gr.lse[t] * kLog2e : 0.0f;
-      const bool t_gt = t < gr.ldGT;
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t v0 = vbase + i * 32 + 8 * q + 4 * half;
-          float gv[4];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int64_t v = v0 + c;
-            const float p = fast_exp2(fmaf(acc[i][j][4 * q + c], kLog2e, -nl));
-            const float oh = (v == y) ? 1.0f : 0.0f;
-            gv[c] = (v < vreal_end) ? coef * (p - oh) : 0.0f;
-          }
-          if constexpr (sizeof(E) == 2) {
-            uint16_t hb[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) hb[c] = f32_to_bf16(gv[c]);
-            if (tin) {
-              if (gr.vec_store && v0 + 3 < m_end) {
-                u32x2 pk;
-                pk.x = static_cast<uint32_t>(hb[0]) | (static_cast<uint32_t>(hb[1]) << 16);
-                pk.y = static_cast<uint32_t>(hb[2]) | (static_cast<uint32_t>(hb[3]) << 16);
-                *reinterpret_cast<u32x2*>(Gp + t * gr.ldG + v0) = pk;
-              } else {
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                  if (v0 + c < m_end) Gp[t * gr.ldG + v0 + c] = hb[c];
-              }
-            }
-            if (t_gt) {
-#pragma unroll
-              for (int c = 0; c < 4; ++c)
-                if (v0 + c < m_end) GTp[(v0 + c) * gr.ldGT + t] = hb[c];
-            }
-          } else {
-            if (tin) {
-              if (gr.vec_store && v0 + 3 < m_end) {
-                f32x4 pk = {gv[0], gv[1], gv[2], gv[3]};
-                *reinterpret_cast<f32x4*>(Gp + t * gr.ldG + v0) = pk;
-              } else {
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                  if (v0 + c < m_end) Gp[t * gr.ldG + v0 + c] = gv[c];
-              }
-            }
-            if (t_gt) {
-#pragma unroll
-              for (int c = 0; c < 4; ++c)
-                if (v0 + c < m_end) GTp[(v0 + c) * gr.ldGT + t] = gv[c];
-            }
-          }
-        }
-    }
-  } else {  // EPI_STORE
-    const StoreArgs& st = e.store;
-    float* Cp = st.C + ks * st.split_stride;
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = vbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (m >= m_end) continue;
-        const bool zero_row = m >= st.m_zero_from;
-        if (zero_row && st.accumulate) continue;
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-          const int64_t n = n0 + wn * WN + j * 32 + l32;
-          if (n >= n_end) continue;
-          float* dst = Cp + m * st.ldc + n;
-          const float v = zero_row ? 0.0f : acc[i][j][r];
-          if (st.accumulate)
-            *dst += v;
-          else
-            *dst = v;
-        }
-      }
+    if (!has_next) break;
+    L = Ln;
   }
 }
 

@@ -29,7 +29,7 @@ FwdPlan plan_fwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
   p.tiles_per_seg = tiles_per_shard(p.S);
   p.tiles_m = p.tiles_per_seg * n;
   p.tiles_n = cdiv(T, kTileN);
-  p.merge_blocks = cdiv(T, 256);
+  p.merge_blocks = cdiv(T, kMergeTok);
   Carve c(ws);
   p.stats = c.take<float2>(static_cast<size_t>(p.tiles_m * T));
   p.zt = c.take<float>(static_cast<size_t>(T));
@@ -41,9 +41,9 @@ FwdPlan plan_fwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
 }
 
 static int32_t pick_dh_splits(int64_t T, int64_t H, int64_t Kv) {
-  const int64_t tiles = cdiv(T, kTileN) * cdiv(H, kTileN);
+  const int64_t tiles = cdiv(T, kTileM) * cdiv(H, kTileN);
   int64_t s = 1;
-  while (tiles * s < 512 && s < 8 && Kv / (2 * s) >= 4 * 64) s *= 2;
+  while (tiles * s < 256 * 4 && s < 8 && Kv / (2 * s) >= 4 * kPadK) s *= 2;
   return static_cast<int32_t>(s);
 }
 
@@ -54,13 +54,12 @@ BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
   p.tiles_per_seg = tiles_per_shard(p.S);
   p.tiles_m = p.tiles_per_seg * n;
   p.tiles_n = cdiv(T, kTileN);
-  p.ldV = round_up(V_pad, 8);
-  p.ldT = round_up(T, 8);
-  p.Kv = round_up(V_real, 8);
+  p.ldV = round_up(V_pad, kPadK);
+  p.ldT = round_up(T, kPadK);
+  p.Kv = round_up(V_real, kPadK);
   p.esize = esize;
-  const int64_t slice = (esize == 2) ? 64 : 32;
   p.dh_splits = pick_dh_splits(T, H, p.Kv);
-  p.dh_k_per_split = round_up(cdiv(p.Kv, p.dh_splits), slice);
+  p.dh_k_per_split = round_up(cdiv(p.Kv, p.dh_splits), kPadK);
   Carve c(ws);
   p.G = c.take<char>(static_cast<size_t>(T * p.ldV) * esize);
   p.GT = c.take<char>(static_cast<size_t>(V_pad * p.ldT) * esize);
@@ -75,34 +74,61 @@ BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
 
 // Per token: merge the tile statistics of each shard into (m_k, s_k), then
 // the shards into the global log-sum-exp; loss = lse - target logit for
-// valid targets. Block partial sums of the loss and counts follow in a fixed
-// tree order.
+// valid targets. A workgroup takes 32 tokens; 8 lane groups each merge every
+// 8th tile of a shard, and the 8 partial pairs are merged in group order, so
+// the result does not depend on scheduling. Block partial sums of the loss
+// and the counts follow in a fixed shuffle-tree order.
 __global__ __launch_bounds__(256) void k_ce_merge(
     const float2* __restrict__ stats, const float* __restrict__ zt,
     const int32_t* __restrict__ targets, int64_t T, int64_t V_real, int32_t ignore_index,
     int32_t n_seg, int64_t tiles_per_seg, float* __restrict__ lse, float* __restrict__ loss,
     float* __restrict__ shard_stats, float* __restrict__ part_loss,
     int32_t* __restrict__ part_nv, int32_t* __restrict__ part_nb) {
-  __shared__ float s_l[256];
-  __shared__ int32_t s_v[256], s_b[256];
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  float l = 0.0f;
-  int32_t nv = 0, nb = 0;
-  if (t < T) {
-    float M = -INFINITY, Ssum = 0.0f;
-    for (int32_t k = 0; k < n_seg; ++k) {
-      float mk = -INFINITY, sk = 0.0f;
+  constexpr int NSUB = 256 / kMergeTok;
+  __shared__ float2 red[NSUB][kMergeTok];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tok = lane & (kMergeTok - 1);
+  const int sub = wave * 2 + (lane >> 5);
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kMergeTok + tok;
+  const bool tin = t < T;
+  float M = -INFINITY, Ssum = 0.0f;
+  for (int32_t k = 0; k < n_seg; ++k) {
+    float mk = -INFINITY, sk = 0.0f;
+    if (tin) {
       const float2* st = stats + (static_cast<int64_t>(k) * tiles_per_seg) * T + t;
-      for (int64_t j = 0; j < tiles_per_seg; ++j) {
+      int64_t j = sub;
+      for (; j + 3 * NSUB < tiles_per_seg; j += 4 * NSUB) {
+        const float2 v0 = st[j * T];
+        const float2 v1 = st[(j + NSUB) * T];
+        const float2 v2 = st[(j + 2 * NSUB) * T];
+        const float2 v3 = st[(j + 3 * NSUB) * T];
+        lse_merge(mk, sk, v0.x, v0.y);
+        lse_merge(mk, sk, v1.x, v1.y);
+        lse_merge(mk, sk, v2.x, v2.y);
+        lse_merge(mk, sk, v3.x, v3.y);
+      }
+      for (; j < tiles_per_seg; j += NSUB) {
         const float2 v = st[j * T];
         lse_merge(mk, sk, v.x, v.y);
       }
+    }
+    red[sub][tok] = make_float2(mk, sk);
+    __syncthreads();
+    if (sub == 0 && tin) {
+#pragma unroll
+      for (int w = 1; w < NSUB; ++w) lse_merge(mk, sk, red[w][tok].x, red[w][tok].y);
       if (shard_stats) {
         shard_stats[static_cast<int64_t>(k) * T + t] = mk;
         shard_stats[static_cast<int64_t>(n_seg + k) * T + t] = sk;
       }
       lse_merge(M, Ssum, mk, sk);
     }
+    __syncthreads();
+  }
+  if (sub != 0) return;  // lanes 0..31 of wave 0 finish the tokens
+  float l = 0.0f;
+  int32_t nv = 0, nb = 0;
+  if (tin) {
     const float L = M + logf(Ssum);
     lse[t] = L;
     const int64_t y = targets[t];
@@ -113,22 +139,16 @@ __global__ __launch_bounds__(256) void k_ce_merge(
     nv = valid ? 1 : 0;
     nb = bad ? 1 : 0;
   }
-  s_l[threadIdx.x] = l;
-  s_v[threadIdx.x] = nv;
-  s_b[threadIdx.x] = nb;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (static_cast<int>(threadIdx.x) < w) {
-      s_l[threadIdx.x] += s_l[threadIdx.x + w];
-      s_v[threadIdx.x] += s_v[threadIdx.x + w];
-      s_b[threadIdx.x] += s_b[threadIdx.x + w];
-    }
-    __syncthreads();
+#pragma unroll
+  for (int o = kMergeTok / 2; o > 0; o >>= 1) {
+    l += __shfl_xor(l, o);
+    nv += __shfl_xor(nv, o);
+    nb += __shfl_xor(nb, o);
   }
-  if (threadIdx.x == 0) {
-    part_loss[blockIdx.x] = s_l[0];
-    part_nv[blockIdx.x] = s_v[0];
-    part_nb[blockIdx.x] = s_b[0];
+  if (lane == 0) {
+    part_loss[blockIdx.x] = l;
+    part_nv[blockIdx.x] = nv;
+    part_nb[blockIdx.x] = nb;
   }
 }
 
@@ -231,12 +251,25 @@ __global__ __launch_bounds__(256) void k_splitk_sum(const float4* __restrict__ p
 
 // ------------------------------------------------------------------ launchers
 
+// Persistent launch: one workgroup per CU (a multiple of 8, one group of
+// workgroups per XCD), never more than there are tiles (rounded up to 8).
+static int64_t persistent_blocks(int64_t tiles) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 8)
+    cus = 256;
+  const int64_t grid = static_cast<int64_t>(cus / 8) * 8 * kOcc;
+  return min(grid, round_up(tiles, 8));
+}
+
 template <typename E, int MODE>
 static hipError_t launch_gemm(const GemmShape& g, const EpiArgs& e, hipStream_t s) {
-  const int64_t blocks = static_cast<int64_t>(g.n_seg) * g.tiles_per_seg * g.tiles_n * g.k_splits;
-  if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_tn<E, MODE, kTileM, kTileN>), dim3(static_cast<uint32_t>(blocks)),
-                     dim3(256), 0, s, g, e);
+  const int64_t tiles = static_cast<int64_t>(g.n_seg) * g.tiles_per_seg * g.tiles_n * g.k_splits;
+  if (tiles <= 0) return hipSuccess;
+  const int64_t blocks = persistent_blocks(tiles);
+  hipLaunchKernelGGL((k_gemm_tn<E, MODE, kTileM, kTileN, kWavesM, kWavesN, kRowBytes, kStages, kOcc>),
+                     dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWavesM * kWavesN), 0, s, g, e);
   return hipGetLastError();
 }
 
@@ -264,7 +297,7 @@ hipError_t run_ce_fwd(const void* h, const void* W, const int32_t* targets, int6
   g.tiles_n = static_cast<int32_t>(p.tiles_n);
   g.k_splits = 1;
   g.k_total = H;
-  g.k_per_split = round_up(H, bf16 ? 64 : 32);
+  g.k_per_split = round_up(H, kPadK);
   g.group_m = 8;
   EpiArgs e{};
   e.fwd.targets = targets;
@@ -290,7 +323,6 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
                               int64_t V_pad, int32_t n, float* dh, float* dW, int32_t accumulate,
                               const BwdPlan& p, hipStream_t s) {
   hipError_t err;
-  constexpr int64_t slice = Elem<E>::kSlice;
   if (T == 0) {
     // no token: dh is empty; dW gets zeros (or is left as it is when accumulating)
     if (!accumulate) {
@@ -334,7 +366,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
     g.tiles_n = static_cast<int32_t>(cdiv(p.ldT, kTileN));
     g.k_splits = 1;
     g.k_total = H;
-    g.k_per_split = round_up(H, slice);
+    g.k_per_split = round_up(H, kPadK);
     g.group_m = 8;
     EpiArgs e{};
     e.grad.targets = targets;
@@ -400,7 +432,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
     g.tiles_n = static_cast<int32_t>(cdiv(H, kTileN));
     g.k_splits = 1;
     g.k_total = p.ldT;
-    g.k_per_split = round_up(p.ldT, slice);
+    g.k_per_split = round_up(p.ldT, kPadK);
     g.group_m = 8;
     EpiArgs e{};
     e.store.C = dW;

@@ -7,8 +7,36 @@
 
 namespace vce {
 
-constexpr int kTileM = 256;   // GEMM tile rows (M side)
-constexpr int kTileN = 256;   // GEMM tile columns (N side)
+#ifndef VCE_WAVES_M
+#define VCE_WAVES_M 2
+#endif
+#ifndef VCE_WAVES_N
+#define VCE_WAVES_N 4
+#endif
+#ifndef VCE_TILE_M
+#define VCE_TILE_M 256
+#endif
+#ifndef VCE_TILE_N
+#define VCE_TILE_N 256
+#endif
+#ifndef VCE_OCC
+#define VCE_OCC 1
+#endif
+constexpr int kTileM = VCE_TILE_M;  // GEMM tile rows (M side)
+constexpr int kTileN = VCE_TILE_N;  // GEMM tile columns (N side)
+constexpr int kOcc = VCE_OCC;       // workgroups resident per CU (waves per SIMD)
+#ifndef VCE_ROW_BYTES
+#define VCE_ROW_BYTES 128
+#endif
+#ifndef VCE_STAGES
+#define VCE_STAGES 2
+#endif
+constexpr int kRowBytes = VCE_ROW_BYTES;  // bytes of one operand row per K slice in LDS
+constexpr int kStages = VCE_STAGES;       // K slices in flight + the one being consumed
+constexpr int kWavesM = VCE_WAVES_M;  // waves per workgroup along M
+constexpr int kWavesN = VCE_WAVES_N;  // waves per workgroup along N
+constexpr int kPadK = 64;     // staged operands are padded to this many K elements
+constexpr int kMergeTok = 32; // tokens per workgroup of the statistics merge
 constexpr int kAlign = 256;   // workspace region alignment (bytes)
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
