@@ -4,7 +4,7 @@ on one MI355X.
 One step = the tied embedding + LM-head step over one batch:
     vemb_fwd (masked lookup of the input IDs)  ->  vce_fwd (fused logits GEMM +
     per-shard online max/sum-exp + cross-shard merge)  ->  vce_bwd (logit
-    recompute, G = scale*(softmax - onehot), dh and dW GEMMs)  ->  vemb_bwd
+    recompute into G = scale*(softmax - onehot), dh and dW GEMMs)  ->  vemb_bwd
     (scatter-add of dh into the same dW).
 Default workload: T=16384 tokens, H=3072, V=201088 (GPT-OSS-20B's table), bf16,
 8 contiguous vocabulary shards, Zipf(1.1) tokens, 1% out-of-range IDs, 2%
@@ -19,6 +19,7 @@ Prints one JSON line. Only one GPU is used; --gpus above 1 is refused.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +31,8 @@ sys.path.insert(0, ROOT)
 METRIC = "fused LM-head CE fwd+bwd tokens/s (V=201088,H=3072,bf16); % MFMA peak"
 PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
+CSRC = os.path.join(ROOT, "vocab_embedding_softmax_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_grad_gemm_c4.txt")
 
 
 def log(*a):
@@ -43,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4", choices=["c3", "c4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=512,
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens in the oracle's CPU-baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one elementwise pass over 1 GiB (read 1 GiB, write 1 GiB): "
@@ -51,10 +54,41 @@ def parse():
     return ap.parse_args()
 
 
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gradient GEMM from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, each scaled by the same counter's reading
+    for a copy of known size; None when absent or taken on other kernel sources."""
+    try:
+        vals = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if line.startswith("#") or not line.strip():
+                    continue
+                k, v = line.split(None, 1)
+                vals[k] = v.strip()
+        if vals.get("source_hash") != kernel_source_hash():
+            return None
+        copy_bytes = float(vals["copy_bytes"])
+        f_scale = copy_bytes / (float(vals["copy_fetch_kib"]) * 1024.0)
+        w_scale = copy_bytes / (float(vals["copy_write_kib"]) * 1024.0)
+        return (float(vals["kernel_fetch_kib"]) * 1024.0 * f_scale +
+                float(vals["kernel_write_kib"]) * 1024.0 * w_scale)
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(inp, n_tok: int):
     """The float64 oracle as it stands, on the first n_tok tokens of the same
     workload, on this host's cores. Returns tokens/s of the oracle step."""
-    import numpy as np
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -77,8 +111,7 @@ def cpu_baseline(inp, n_tok: int):
     del W
     return dict(value=n_tok / dt, unit="tokens/s", cores=int(cores), kind="oracle",
                 sample=f"float64 oracle {what} on the first {n_tok} tokens of the same "
-                       f"workload (full V={inp.V_real}, H={inp.H}); {dt:.1f} s wall",
-                seconds=dt)
+                       f"workload (full V={inp.V_real}, H={inp.H}); {dt:.1f} s wall")
 
 
 def main():
@@ -119,32 +152,34 @@ def main():
     nbad = torch.empty(1, **i32)
     gl = torch.ones(1, **f32)
     stream = torch.cuda.current_stream(dev)
-    EV = ["start", "emb_fwd", "ce_fwd", "ce_bwd", "emb_bwd"]
 
-    def step(evs=None):
-        if evs is not None:
-            evs[0].record(stream)
+    # events: 0 start | 1 after lookup | 2 after forward | 3..7 backward stages | 8 after scatter
+    def new_events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(9)]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
         if tied:
             V.vemb_fwd(ids, W, Vr, n, out=h, n_bad=nbad)
-        if evs is not None:
-            evs[1].record(stream)
+        if ev is not None:
+            ev[1].record(stream)
         V.vce_fwd(h, W, tg, Vr, n, inp.ignore_index, out=fo, ws=ws["fwd"])
-        if evs is not None:
-            evs[2].record(stream)
+        if ev is not None:
+            ev[2].record(stream)
         V.vce_bwd(h, W, tg, fo.lse, gl, fo.n_valid, Vr, n, inp.ignore_index, V.REDUCE_MEAN,
-                  dh=dh, dW=dW, accumulate_dW=False, ws=ws["bwd"])
-        if evs is not None:
-            evs[3].record(stream)
+                  dh=dh, dW=dW, accumulate_dW=False, ws=ws["bwd"],
+                  events=None if ev is None else ev[3:8])
         if tied:
             V.vemb_bwd(ids, dh, Vr, Vp, n, dW=dW, accumulate=True, ws=ws["emb"])
-        if evs is not None:
-            evs[4].record(stream)
+        if ev is not None:
+            ev[8].record(stream)
 
     log(f"[bench] warmup {a.warmup}")
     for _ in range(a.warmup):
-        step()
+        step(new_events())
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in EV] for _ in range(a.steps)]
+    evs = [new_events() for _ in range(a.steps)]
     log(f"[bench] timing {a.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -153,20 +188,33 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / a.steps
-    phase = {}
-    for i in range(1, len(EV)):
-        phase[EV[i]] = float(np.mean([e[i - 1].elapsed_time(e[i]) for e in evs]))
-    log(f"[bench] {ms_step:.3f} ms/step, phases {phase}")
 
-    flop_gemm = 2.0 * T * H * Vr           # one of the four GEMMs of the CE
-    ce_fwd_ms = phase["ce_fwd"]
-    ce_bwd_ms = phase["ce_bwd"]
-    # dominant call: the one that takes longest; its kernels' algorithmic work
-    if ce_bwd_ms / 3.0 >= ce_fwd_ms:
-        dom_name, dom_ms, dom_flop = "vce_bwd (recompute+G, dh, dW GEMMs)", ce_bwd_ms, 3 * flop_gemm
-    else:
-        dom_name, dom_ms, dom_flop = "vce_fwd (fused logits GEMM + online LSE)", ce_fwd_ms, flop_gemm
-    achieved = dom_flop / (dom_ms * 1e-3) / 1e12
+    def span(i, j):
+        return float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))
+
+    phase = {
+        "vemb_fwd": span(0, 1),
+        "vce_fwd": span(1, 2),
+        "vce_bwd.transposes": span(3, 4),
+        "vce_bwd.recompute_G": span(4, 5),
+        "vce_bwd.dh": span(5, 6),
+        "vce_bwd.dW": span(6, 7),
+        "vemb_bwd": span(7, 8),
+    }
+    log(f"[bench] {ms_step:.3f} ms/step, phases (ms) {json.dumps(phase)}")
+
+    flop_gemm = 2.0 * T * H * Vr  # algorithmic flops of each of the four CE GEMMs
+    gemms = {
+        "k_gemm_tn<bf16,EPI_FWD> (vce_fwd: logits GEMM + online max/sum-exp)": phase["vce_fwd"],
+        "k_gemm_tn<bf16,EPI_GRAD> (logit recompute + G = scale*(softmax-onehot))":
+            phase["vce_bwd.recompute_G"],
+        "k_gemm_tn<bf16,EPI_STORE> (dh = G W, split-K + fixed-order sum)": phase["vce_bwd.dh"],
+        "k_gemm_tn<bf16,EPI_STORE> (dW = G^T h)": phase["vce_bwd.dW"],
+    }
+    dom = max(gemms, key=gemms.get)
+    dom_ms = gemms[dom]
+    achieved = flop_gemm / (dom_ms * 1e-3) / 1e12
+    traffic = measured_traffic() if ("EPI_GRAD" in dom and a.workload == "c4") else None
     path_frac = 8.0 * T * H * Vr / (ms_step * 1e-3) / PEAK_BF16
     res = {
         "metric": METRIC,
@@ -189,16 +237,29 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": dom_name,
+            "kernel": dom,
             "achieved": achieved,
             "peak": PEAK_BF16 / 1e12,
             "unit": "TFLOP/s",
             "frac": achieved / (PEAK_BF16 / 1e12),
-            "traffic": None,
+            "traffic": traffic,
         },
         "path_mfma_frac": path_frac,
         "phases_ms": phase,
     }
+    if tied:
+        # algorithmic HBM bytes (unique rows read once, outputs written once)
+        uniq = int(np.unique(inp.ids[(inp.ids >= 0) & (inp.ids < Vr)]).shape[0])
+        gather_bytes = uniq * H * 2 + T * H * 2 + 4 * T
+        scatter_bytes = T * H * 4 + 8 * T + 2 * uniq * H * 4
+        res["hbm_rooflines"] = {
+            "vemb_fwd": {"bytes": gather_bytes, "ms": phase["vemb_fwd"],
+                         "GB_s": gather_bytes / (phase["vemb_fwd"] * 1e-3) / 1e9,
+                         "frac": gather_bytes / (phase["vemb_fwd"] * 1e-3) / PEAK_HBM},
+            "vemb_bwd": {"bytes": scatter_bytes, "ms": phase["vemb_bwd"],
+                         "GB_s": scatter_bytes / (phase["vemb_bwd"] * 1e-3) / 1e9,
+                         "frac": scatter_bytes / (phase["vemb_bwd"] * 1e-3) / PEAK_HBM},
+        }
     if a.copy_probe:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -211,9 +272,7 @@ def main():
     torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
         log(f"[bench] CPU baseline: oracle on {a.cpu_tokens} tokens")
-        cb = cpu_baseline(inp, a.cpu_tokens)
-        cb.pop("seconds", None)
-        res["cpu_baseline"] = cb
+        res["cpu_baseline"] = cpu_baseline(inp, a.cpu_tokens)
     print(json.dumps(res), flush=True)
 
 

@@ -134,6 +134,20 @@ vce_status vce_bwd(const void* h, const void* W, const int32_t* targets, const f
                    float* dh, float* dW, int32_t accumulate_dW,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* Same as vce_bwd, for profiling tools: when `events` is not NULL it holds
+ * VCE_BWD_EVENTS hipEvent_t handles (passed as void*) created by the caller;
+ * they are recorded on `stream` at the stage boundaries of the backward:
+ *   events[0] before the first kernel, [1] after the operand transposes,
+ *   [2] after the logit-recompute / G kernel, [3] after dh (including its
+ *   split-K sum), [4] after dW. With events == NULL this is vce_bwd. */
+#define VCE_BWD_EVENTS 5
+vce_status vce_bwd_timed(const void* h, const void* W, const int32_t* targets, const float* lse,
+                         const float* grad_loss, const int32_t* n_valid, vce_reduction red,
+                         int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                         int32_t num_shards, int32_t ignore_index, vce_dtype dt,
+                         float* dh, float* dW, int32_t accumulate_dW,
+                         void* ws, size_t ws_bytes, void* stream, void* const* events);
+
 /* ------------------------------------------------------------------------ *
  * Masked embedding lookup.                                                  *
  *                                                                           *

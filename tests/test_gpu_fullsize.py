@@ -1,0 +1,164 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+bench times. Outputs the oracle cannot afford in full are checked on sampled
+tokens (every quantity of a sampled token is computed one by one from its own
+logit row), plus properties that hold at any size. The sampled-softmax
+workload (c5) is checked in full."""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.ce import MEAN
+from synth import config_inputs
+from tests._cmp import TOL, rel_l2
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def V():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vocab_embedding_softmax_amd as v
+    return v
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _sample_tokens(targets, V_real, k, seed):
+    rng = np.random.default_rng(seed)
+    T = targets.shape[0]
+    pick = set(rng.choice(T, size=k, replace=False).tolist())
+    bad = np.nonzero((targets < 0) | (targets >= V_real))[0]
+    pick.update(bad[:3].tolist())
+    pick.update([0, T - 1])
+    return np.array(sorted(pick))
+
+
+def _check_sampled(g, inp, h64_rows, W64, sample, n_valid_all):
+    """lse, loss and dh rows of the sampled tokens against the oracle."""
+    y = inp.targets[sample]
+    f = oracle.ce_forward(h64_rows, W64, y, inp.V_real, inp.V_pad, inp.num_shards,
+                          inp.ignore_index)
+    scale = 1.0 / max(n_valid_all, 1)
+    dh, _ = oracle.ce_backward(h64_rows, W64, y, f["lse"], inp.V_real, inp.V_pad, scale,
+                               inp.ignore_index)
+    lse_err = np.abs(g["lse"][sample] - f["lse"]).max()
+    assert lse_err <= TOL["bf16"]["lse_abs"], lse_err
+    valid = f["valid"]
+    # per token: the lse bound plus a relative term for the target logit
+    lo = np.abs(g["loss"][sample][valid] - f["loss"][valid])
+    assert (lo <= TOL["bf16"]["lse_abs"] + 1e-3 * np.abs(f["loss"][valid])).all(), lo.max()
+    assert not g["loss"][sample][~valid].any()
+    e = rel_l2(g["dh"][sample], dh)
+    assert e <= TOL["bf16"]["grad"], e
+    assert not g["dh"][sample][~valid].any()
+    return f
+
+
+def _counts(inp):
+    v, ign, bad = oracle.target_status(inp.targets, inp.V_real, inp.ignore_index)
+    return int(v.sum()), int(bad.sum())
+
+
+def test_c3_full_size_sampled_tokens(V):
+    say("case c3 full size")
+    inp = config_inputs("c3")
+    dev = "cuda"
+    h = V.from_bits(inp.h, "bf16", dev)
+    W = V.from_bits(inp.W, "bf16", dev)
+    tg = torch.from_numpy(inp.targets).to(dev)
+    r = V.ce_step(h, W, tg, inp.V_real, inp.num_shards, inp.ignore_index, shard_stats=True)
+    torch.cuda.synchronize()
+    g = dict(lse=r.fwd.lse.cpu().numpy(), loss=r.fwd.loss.cpu().numpy(),
+             dh=r.dh.cpu().numpy())
+    nv, nb = _counts(inp)
+    assert int(r.fwd.n_valid.item()) == nv and int(r.fwd.n_bad.item()) == nb
+    # the per-shard statistics merge to the reported lse
+    ss = r.fwd.shard_stats.cpu().numpy().astype(np.float64)
+    assert np.abs(oracle.merge_shard_stats(ss[0], ss[1]) - g["lse"]).max() < 1e-4
+    # every G row sums to zero, so the dW rows sum to zero
+    dW = r.dW
+    colsum = dW.double().sum(dim=0).abs().max().item()
+    scale = dW.double().abs().sum(dim=0).max().item()
+    assert colsum <= 1e-3 * scale, (colsum, scale)
+    del r, dW
+    torch.cuda.empty_cache()
+    sample = _sample_tokens(inp.targets, inp.V_real, 24, 3)
+    W64 = oracle.decode(inp.W, "bf16")
+    h64 = oracle.decode(inp.h[sample], "bf16")
+    _check_sampled(g, inp, h64, W64, sample, nv)
+
+
+def test_c4_full_size_tied_step(V):
+    say("case c4 full size")
+    inp = config_inputs("c4")
+    dev = "cuda"
+    W = V.from_bits(inp.W, "bf16", dev)
+    ids = torch.from_numpy(inp.ids).to(dev)
+    tg = torch.from_numpy(inp.targets).to(dev)
+    r = V.tied_step(ids, tg, W, inp.V_real, inp.num_shards, inp.ignore_index)
+    torch.cuda.synchronize()
+    # the lookup, bit for bit, and its count of out-of-range IDs
+    hb = r.extra["h"].cpu().view(torch.int16).numpy()
+    ok = (inp.ids >= 0) & (inp.ids < inp.V_real)
+    want = np.zeros_like(hb)
+    want[ok] = inp.W.view(np.int16)[inp.ids[ok]]
+    assert np.array_equal(hb, want)
+    assert int(r.extra["n_bad_id"].item()) == int((~ok).sum())
+    nv, nb = _counts(inp)
+    assert int(r.fwd.n_valid.item()) == nv and int(r.fwd.n_bad.item()) == nb
+    g = dict(lse=r.fwd.lse.cpu().numpy(), loss=r.fwd.loss.cpu().numpy(),
+             dh=r.dh.cpu().numpy())
+    del r
+    torch.cuda.empty_cache()
+    sample = _sample_tokens(inp.targets, inp.V_real, 24, 4)
+    W64 = oracle.decode(inp.W, "bf16")
+    h64 = oracle.gather_direct(inp.ids[sample], W64, inp.V_real)
+    _check_sampled(g, inp, h64, W64, sample, nv)
+
+
+def test_c4_full_size_scatter(V):
+    say("case c4 scatter full size")
+    inp = config_inputs("c4")
+    dev = "cuda"
+    rng = np.random.default_rng(40)
+    dout = rng.standard_normal((inp.T, inp.H)).astype(np.float32)
+    got = V.vemb_bwd(torch.from_numpy(inp.ids).to(dev), torch.from_numpy(dout).to(dev),
+                     inp.V_real, inp.V_pad, inp.num_shards).cpu().numpy()
+    ref, count = oracle.scatter_add(inp.ids, dout, inp.V_real, inp.V_pad)
+    assert rel_l2(got, ref) <= 1e-5   # float32 sums of up to thousands of rows
+    once = count == 1
+    assert np.array_equal(got[once], ref[once].astype(np.float32))
+    assert not got[count == 0].any()
+
+
+def test_c5_full_size_sampled_softmax(V):
+    say("case c5 full size")
+    inp = config_inputs("c5")
+    dev = "cuda"
+    h = V.from_bits(inp.h, "bf16", dev)
+    W = V.from_bits(inp.W, "bf16", dev)
+    r = V.sampled_step(h, W, torch.from_numpy(inp.targets).to(dev),
+                       torch.from_numpy(inp.perm).to(dev), inp.P)
+    torch.cuda.synchronize()
+    ref = oracle.sampled_step(oracle.decode(inp.h, "bf16"), oracle.decode(inp.W, "bf16"),
+                              inp.targets, inp.perm, inp.P, chunk=1024)
+    assert int(r.extra["n_unique"].item()) == ref["n_unique"]
+    assert int(r.extra["n_cand"].item()) == inp.P
+    assert np.array_equal(r.extra["cand"].cpu().numpy()[:inp.P], ref["cand"].astype(np.int32))
+    assert np.array_equal(r.extra["pos"].cpu().numpy(), ref["pos"].astype(np.int32))
+    assert int(r.fwd.n_valid.item()) == ref["n_valid"]
+    dl = abs(float(r.fwd.loss_sum.item()) - ref["loss_sum"]) / abs(ref["loss_sum"])
+    assert dl <= TOL["bf16"]["loss"], dl
+    assert np.abs(r.fwd.lse.cpu().numpy() - ref["lse"]).max() <= TOL["bf16"]["lse_abs"]
+    assert rel_l2(r.dh.cpu().numpy(), ref["dh"]) <= TOL["bf16"]["grad"]
+    assert rel_l2(r.extra["dWc"].cpu().numpy(), ref["dWc"]) <= TOL["bf16"]["grad"]
+    assert rel_l2(r.dW.cpu().numpy(), ref["dW"]) <= TOL["bf16"]["grad"]

@@ -21,6 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvce.so")
 
 VCE_F32, VCE_BF16 = 0, 1
+VCE_BWD_EVENTS = 5
 REDUCE_MEAN, REDUCE_SUM = 0, 1
 
 STATUS = {0: "VCE_OK", 1: "VCE_ERR_NULL", 2: "VCE_ERR_SHAPE", 3: "VCE_ERR_SHARD",
@@ -40,6 +41,8 @@ SIGNATURES = {
     "vce_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32, _I32]),
     "vce_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _I32, _I32, _I32,
                        _P, _P, _I32, _P, _SZ, _P]),
+    "vce_bwd_timed": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _I32, _I32,
+                             _I32, _P, _P, _I32, _P, _SZ, _P, _P]),
     "vemb_fwd": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P, _P, _P]),
     "vemb_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
     "vemb_bwd": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _I64, _I32, _P, _I32, _P, _SZ, _P]),
@@ -57,7 +60,7 @@ class VceError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          f"`python -m vocab_embedding_softmax_amd.build` (hipcc, gfx950)")
+                          f"`python vocab_embedding_softmax_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
@@ -172,8 +175,10 @@ def vce_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.
             ignore_index: int = -100, reduction: int = REDUCE_MEAN, *,
             dh: Optional[torch.Tensor] = None, dW: Optional[torch.Tensor] = None,
             accumulate_dW: bool = False, ws: Optional[torch.Tensor] = None,
-            stream=None) -> BwdOut:
-    """Cross-entropy backward: dh [T,H] and dW [V_pad,H] (float32)."""
+            stream=None, events=None) -> BwdOut:
+    """Cross-entropy backward: dh [T,H] and dW [V_pad,H] (float32). `events`
+    (optional): VCE_BWD_EVENTS torch.cuda.Event objects recorded at the stage
+    boundaries (calls vce_bwd_timed)."""
     T, H = h.shape
     V_pad = W.shape[0]
     dt = _dt(h)
@@ -192,11 +197,19 @@ def vce_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.
     _need(dW, "dW", torch.float32, (V_pad, H))
     need = vce_bwd_workspace_bytes(T, H, V_real, V_pad, num_shards, dt)
     ws = _workspace(need, dev, ws)
-    st = lib.vce_bwd(_ptr(h), _ptr(W), _ptr(targets), _ptr(lse), _ptr(grad_loss), _ptr(n_valid),
-                     reduction, T, H, V_real, V_pad, num_shards, ignore_index, dt, _ptr(dh),
-                     _ptr(dW), 1 if accumulate_dW else 0, _ptr(ws), ws.numel(),
-                     _stream(stream, dev))
-    _check("vce_bwd", st)
+    args = (_ptr(h), _ptr(W), _ptr(targets), _ptr(lse), _ptr(grad_loss), _ptr(n_valid),
+            reduction, T, H, V_real, V_pad, num_shards, ignore_index, dt, _ptr(dh), _ptr(dW),
+            1 if accumulate_dW else 0, _ptr(ws), ws.numel(), _stream(stream, dev))
+    if events is None:
+        _check("vce_bwd", lib.vce_bwd(*args))
+    else:
+        if len(events) != VCE_BWD_EVENTS:
+            raise ValueError(f"events must hold {VCE_BWD_EVENTS} torch.cuda.Event objects")
+        for e in events:
+            if e.cuda_event == 0:   # created lazily by torch: force creation on this device
+                e.record(torch.cuda.current_stream(dev))
+        arr = (ctypes.c_void_p * VCE_BWD_EVENTS)(*[e.cuda_event for e in events])
+        _check("vce_bwd_timed", lib.vce_bwd_timed(*args, arr))
     return BwdOut(dh, dW)
 
 

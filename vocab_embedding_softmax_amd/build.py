@@ -1,6 +1,6 @@
 """Build libvce.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m vocab_embedding_softmax_amd.build        # or build() from Python
+    python vocab_embedding_softmax_amd/build.py        # or __graft_entry__.build()
 
 Objects go to _build/ at the repository root; the library lands next to this
 file so that it travels with the source tree.

@@ -101,6 +101,17 @@ vce_status vce_bwd(const void* h, const void* W, const int32_t* targets, const f
                    int64_t H, int64_t V_real, int64_t V_pad, int32_t num_shards,
                    int32_t ignore_index, vce_dtype dt, float* dh, float* dW,
                    int32_t accumulate_dW, void* ws, size_t ws_bytes, void* stream) {
+  return vce_bwd_timed(h, W, targets, lse, grad_loss, n_valid, red, T, H, V_real, V_pad,
+                       num_shards, ignore_index, dt, dh, dW, accumulate_dW, ws, ws_bytes, stream,
+                       nullptr);
+}
+
+vce_status vce_bwd_timed(const void* h, const void* W, const int32_t* targets, const float* lse,
+                         const float* grad_loss, const int32_t* n_valid, vce_reduction red,
+                         int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t num_shards,
+                         int32_t ignore_index, vce_dtype dt, float* dh, float* dW,
+                         int32_t accumulate_dW, void* ws, size_t ws_bytes, void* stream,
+                         void* const* events) {
   if (!dtype_ok(dt) || (red != VCE_REDUCE_MEAN && red != VCE_REDUCE_SUM)) return VCE_ERR_DTYPE;
   vce_status st = check_table(T, H, V_real, V_pad, num_shards);
   if (st != VCE_OK) return st;
@@ -119,7 +130,7 @@ vce_status vce_bwd(const void* h, const void* W, const int32_t* targets, const f
   const vce::BwdPlan p = vce::plan_bwd(T, H, V_real, V_pad, num_shards, esize_of(dt), ws);
   return hip_status(vce::run_ce_bwd(h, W, targets, lse, grad_loss, n_valid, red, T, H, V_real,
                                     V_pad, num_shards, dt == VCE_BF16, dh, dW, accumulate_dW ? 1 : 0,
-                                    p, static_cast<hipStream_t>(stream)));
+                                    p, static_cast<hipStream_t>(stream), events));
 }
 
 vce_status vemb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, int64_t V_real,

@@ -321,16 +321,22 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
                               const float* lse, const float* grad_loss, const int32_t* n_valid,
                               int32_t reduction, int64_t T, int64_t H, int64_t V_real,
                               int64_t V_pad, int32_t n, float* dh, float* dW, int32_t accumulate,
-                              const BwdPlan& p, hipStream_t s) {
+                              const BwdPlan& p, hipStream_t s, void* const* ev) {
   hipError_t err;
+  auto mark = [&](int i) -> hipError_t {
+    return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
+  };
+  if ((err = mark(0)) != hipSuccess) return err;
   if (T == 0) {
     // no token: dh is empty; dW gets zeros (or is left as it is when accumulating)
     if (!accumulate) {
       const int64_t n4 = V_pad * H / 4;
       hipLaunchKernelGGL(k_zero_f4, dim3(static_cast<uint32_t>(cdiv(n4, 256))), dim3(256), 0, s,
                          reinterpret_cast<float4*>(dW), n4);
-      return hipGetLastError();
+      if ((err = hipGetLastError()) != hipSuccess) return err;
     }
+    for (int i = 1; i < 5; ++i)
+      if ((err = mark(i)) != hipSuccess) return err;
     return hipSuccess;
   }
   // 1. W^T [H][ldV] with rows >= V_real zeroed, h^T [H][ldT] with tokens >= T zeroed
@@ -350,6 +356,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
                        s, static_cast<E*>(p.G), T, p.ldV, V_pad, p.ldV);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  if ((err = mark(1)) != hipSuccess) return err;
   // 2. recompute logits per tile -> G, G^T
   {
     GemmShape g{};
@@ -383,6 +390,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
     e.grad.ldGT = p.ldT;
     if ((err = launch_gemm<E, EPI_GRAD>(g, e, s)) != hipSuccess) return err;
   }
+  if ((err = mark(2)) != hipSuccess) return err;
   // 3. dh = G W  (K = real vocabulary, split into fixed partial planes)
   {
     GemmShape g{};
@@ -416,6 +424,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   }
+  if ((err = mark(3)) != hipSuccess) return err;
   // 4. dW = G^T h  (K = tokens); rows >= V_real are 0 (or untouched when accumulating)
   {
     GemmShape g{};
@@ -442,18 +451,19 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
     e.store.m_zero_from = V_real;
     if ((err = launch_gemm<E, EPI_STORE>(g, e, s)) != hipSuccess) return err;
   }
-  return hipSuccess;
+  return mark(4);
 }
 
 hipError_t run_ce_bwd(const void* h, const void* W, const int32_t* targets, const float* lse,
                       const float* grad_loss, const int32_t* n_valid, int32_t reduction,
                       int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, bool bf16,
-                      float* dh, float* dW, int32_t accumulate, const BwdPlan& p, hipStream_t s) {
+                      float* dh, float* dW, int32_t accumulate, const BwdPlan& p, hipStream_t s,
+                      void* const* events) {
   if (bf16)
     return ce_bwd_impl<uint16_t>(h, W, targets, lse, grad_loss, n_valid, reduction, T, H, V_real,
-                                 V_pad, n, dh, dW, accumulate, p, s);
+                                 V_pad, n, dh, dW, accumulate, p, s, events);
   return ce_bwd_impl<float>(h, W, targets, lse, grad_loss, n_valid, reduction, T, H, V_real, V_pad,
-                            n, dh, dW, accumulate, p, s);
+                            n, dh, dW, accumulate, p, s, events);
 }
 
 }  // namespace vce

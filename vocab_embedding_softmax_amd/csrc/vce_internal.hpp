@@ -84,16 +84,20 @@ struct BwdPlan {
 BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, size_t esize,
                  void* ws);
 
-// Embedding backward plan (sort by ID, then segment sums).
+// Embedding backward plan: a stable sort of the tokens by ID (block-local
+// LDS sorts + per-block counts + scans, no atomics), then segment sums.
 struct EmbBwdPlan {
+  int64_t nblocks;     // token blocks of the local sort
   int64_t nchunks, nslices, scan_blocks;
-  int32_t* counts;   // [V_real] occurrences of each ID
-  int32_t* offs;     // [V_real + 1] exclusive prefix of counts (offs[V_real] = total)
-  int32_t* cursor;   // [V_real] placement cursors
-  int32_t* perm;     // [T] token indices grouped by ID
-  int32_t* sorted;   // [T] token indices sorted by (ID, token)
-  int32_t* scan_tmp; // [scan_blocks + 1]
-  float* partial;    // [nchunks][2][H]
+  int32_t* bcnt;       // [nblocks][V_real] per-block occurrences -> per-block offsets
+  int32_t* counts;     // [V_real] occurrences of each ID
+  int32_t* offs;       // [V_real + 1] exclusive prefix of counts (offs[V_real] = total)
+  uint64_t* lkey;      // [nblocks * block] block-sorted keys (ID << 32 | token)
+  int32_t* lrank;      // [nblocks * block] rank among equal IDs inside the block
+  int32_t* sorted;     // [T] token indices sorted by (ID, token)
+  int32_t* skey;       // [T] the ID of each sorted position
+  int32_t* scan_tmp;   // [scan_blocks + 1]
+  float* partial;      // [nchunks][2][H]
   size_t bytes;
 };
 EmbBwdPlan plan_emb_bwd(int64_t T, int64_t H, int64_t V_real, void* ws);
@@ -118,7 +122,8 @@ hipError_t run_ce_fwd(const void* h, const void* W, const int32_t* targets, int6
 hipError_t run_ce_bwd(const void* h, const void* W, const int32_t* targets, const float* lse,
                       const float* grad_loss, const int32_t* n_valid, int32_t reduction,
                       int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, bool bf16,
-                      float* dh, float* dW, int32_t accumulate, const BwdPlan& p, hipStream_t s);
+                      float* dh, float* dW, int32_t accumulate, const BwdPlan& p, hipStream_t s,
+                      void* const* events);
 
 hipError_t run_emb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, int64_t V_real,
                        int64_t V_pad, int32_t n, size_t esize, void* out, int32_t* n_bad,
