@@ -64,6 +64,7 @@ struct GradArgs {
   int64_t V_real;
   const float* grad_loss;
   const int32_t* n_valid;
+  int64_t v_off;        // vocabulary row of the GEMM's row 0
   int32_t reduction;    // 0 mean over valid tokens, 1 sum
   int32_t vec_store;    // 1 if every tile start is a multiple of 4 columns
   void* G;              // [T][ldG]
@@ -117,6 +118,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses are done
+// (lgkmcnt(0)), outstanding global loads are left in flight. __syncthreads()
+// would also wait for every global load, including the next tile's prefetch.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+  __builtin_amdgcn_s_barrier();
+}
+
 template <typename E>
 __device__ __forceinline__ void mma_chunk(f32x16& acc, const u32x4& a, const u32x4& b);
 
@@ -140,45 +149,90 @@ __device__ __forceinline__ void mma_chunk<float>(f32x16& acc, const u32x4& a, co
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Per-lane byte offsets (relative to the tile's first row and current K) of
-// the chunks this lane brings into LDS for ROWS operand rows of RB-byte K
-// slices. One wave-wide load moves 1 KB = RPI rows: wave w, load q moves tile
-// rows [(q*NW + w)*RPI, +RPI); lane l brings chunk (l % CPR) ^ swz(row) of row
-// l / CPR, landing at LDS row*RB + (l % CPR)*16 (lane-linear).
+// 32-bit LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(p)));
+}
+
+// Global -> LDS copy of one 16-byte chunk per lane, landing at LDS address
+// lds + 16 * lane (global_load_lds_dwordx4). Written as inline assembly on
+// purpose: the compiler cannot tell which LDS bytes such a load writes, so
+// for its own intrinsic it waits for every outstanding load before any later
+// LDS read, which would wait for the next slice's prefetch before computing
+// on the current one. The kernel orders these copies itself (s_waitcnt
+// vmcnt + s_barrier); the compiler only has to keep LDS accesses on their side
+// of the statement, which the memory clobber does. M0 is written here and the
+// compiler keeps nothing in M0 across these kernels' code.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// address = 64-bit scalar base + 32-bit per-lane offset
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+// address = per-lane 64-bit pointer
+__device__ __forceinline__ void dma16(const void* p, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(p), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Global -> LDS staging of ROWS operand rows of RB-byte K slices by NW waves.
+// One wave-wide load moves 1 KB = RPI rows: wave w, load q moves tile rows
+// [(q*NW + w)*RPI, +RPI); lane l brings chunk (l % CPR) ^ swz(row) of row
+// l / CPR, landing at LDS row*RB + (l % CPR)*16 (lane-linear). The chunk a
+// lane brings does not depend on q, so when every row of the tile is valid
+// the lane's global offset is one value plus a uniform stride per load.
 template <int ROWS, int NW, int RB>
 struct RowLoads {
   static constexpr int CPR = RB / 16;     // chunks per row
   static constexpr int RPI = 64 / CPR;    // rows per wave-wide load
   static constexpr int Q = ROWS / (RPI * NW);
   static_assert(ROWS % (RPI * NW) == 0, "load split");
-  uint32_t off[Q];     // byte offset of the chunk in global memory
-  uint32_t kchunk[Q];  // element offset of the chunk inside the K slice
+  static_assert(RB != 128 || NW % 2 == 0, "chunk choice must not depend on q");
+  uint32_t off0;     // this lane's byte offset for load 0 (chunk included)
+  int32_t lrow;      // this lane's tile row for load 0
+  int32_t kch;       // element offset of this lane's chunk inside the K slice
+  int64_t qstride;   // bytes between the rows of load q and load q + 1
+  int64_t rstride;   // bytes between consecutive rows
+  int32_t nrows;     // valid rows of the tile (rows past it read the last valid row)
+  bool all_rows;
 
   template <int EPC>
   __device__ __forceinline__ void init(int64_t row0, int64_t row_end, int64_t ld, int wave,
                                        int lane, int esize) {
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int r = (q * NW + wave) * RPI + lane / CPR;
-      const int lch = (lane % CPR) ^ lds_swz<RB>(r);
-      int64_t gr = row0 + r;
-      if (gr >= row_end) gr = row_end - 1;  // clamp: the result of this row is discarded
-      off[q] = static_cast<uint32_t>(((gr - row0) * ld + lch * EPC) * esize);
-      kchunk[q] = static_cast<uint32_t>(lch * EPC);
-    }
+    lrow = wave * RPI + lane / CPR;
+    const int lch = (lane % CPR) ^ lds_swz<RB>(lrow);
+    kch = lch * EPC;
+    rstride = ld * esize;
+    qstride = static_cast<int64_t>(NW) * RPI * rstride;
+    nrows = static_cast<int32_t>(min(row_end - row0, static_cast<int64_t>(ROWS)));
+    all_rows = nrows == ROWS;
+    off0 = static_cast<uint32_t>(lrow * rstride + kch * esize);
   }
 
-  // stage one K slice: `base` points at (row0, k); `kleft` = K elements left
-  // from k (only consulted for a slice that runs past K)
-  template <int Q0 = 0, int Q1 = Q>
-  __device__ __forceinline__ void issue(char* lds, const char* base, int64_t kleft,
-                                        int wave) const {
+  // stage one K slice: `base` points at (row0, k), `lds` is the stage's LDS
+  // address; `kleft` = K elements left from k. The common case (all rows
+  // valid, a whole slice) addresses from uniform bases; otherwise each lane
+  // clamps its row and takes the zero chunk for chunks past K.
+  __device__ __forceinline__ void issue(uint32_t lds, const char* base, int64_t kleft, bool full,
+                                        int wave, int esize) const {
+    if (full && all_rows) {
 #pragma unroll
-    for (int q = Q0; q < (Q1 < Q ? Q1 : Q); ++q) {
-      const void* p = base + off[q];
-      if (static_cast<int64_t>(kchunk[q]) >= kleft) p = g_zero_chunk;
-      __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(lds + (q * NW + wave) * RPI * RB), 16, 0,
-                                       0);
+      for (int q = 0; q < Q; ++q) dma16(base + q * qstride, off0, lds + (q * NW + wave) * RPI * RB);
+    } else {
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        int r = lrow + q * NW * RPI;
+        if (r >= nrows) r = nrows - 1;  // the result of this row is discarded
+        const void* p = base + r * rstride + kch * esize;
+        if (kch >= kleft) p = g_zero_chunk;
+        dma16(p, lds + (q * NW + wave) * RPI * RB);
+      }
     }
   }
 };
@@ -203,29 +257,34 @@ struct TileGeom {
 };
 
 // Logical tile L -> tile: K split outermost, then groups of group_m tiles
-// along M, each group walking all tiles along N.
+// along M, each group walking all tiles along N. Tile counts fit in 32 bits
+// (checked on the host), so the divisions are 32-bit.
 template <int BM, int BN>
-__device__ __forceinline__ TileGeom decode_tile(const GemmShape& g, int64_t L) {
-  const int64_t tiles_m = static_cast<int64_t>(g.n_seg) * g.tiles_per_seg;
-  const int64_t per_split = tiles_m * g.tiles_n;
+__device__ __forceinline__ TileGeom decode_tile(const GemmShape& g, uint32_t L) {
+  const uint32_t tiles_m = static_cast<uint32_t>(g.n_seg) * static_cast<uint32_t>(g.tiles_per_seg);
+  const uint32_t tiles_n = static_cast<uint32_t>(g.tiles_n);
+  const uint32_t group_m = static_cast<uint32_t>(g.group_m);
+  const uint32_t per_split = tiles_m * tiles_n;
   TileGeom t;
-  t.ks = L / per_split;
-  const int64_t rem = L - t.ks * per_split;
-  const int64_t in_group = static_cast<int64_t>(g.group_m) * g.tiles_n;
-  const int64_t grp = rem / in_group;
-  const int64_t first_m = grp * g.group_m;
-  const int64_t gsz = min(static_cast<int64_t>(g.group_m), tiles_m - first_m);
-  const int64_t r_in = rem - grp * in_group;
-  t.tm = first_m + r_in % gsz;
-  const int64_t tn = r_in / gsz;
-  const int64_t seg = t.tm / g.tiles_per_seg;
-  const int64_t tj = t.tm - seg * g.tiles_per_seg;
-  t.m0 = seg * g.seg_len + tj * BM;
-  t.m_end = min(min(t.m0 + BM, (seg + 1) * g.seg_len), g.m_total);
+  const uint32_t ks = L / per_split;
+  const uint32_t rem = L - ks * per_split;
+  const uint32_t in_group = group_m * tiles_n;
+  const uint32_t grp = rem / in_group;
+  const uint32_t first_m = grp * group_m;
+  const uint32_t gsz = min(group_m, tiles_m - first_m);
+  const uint32_t r_in = rem - grp * in_group;
+  const uint32_t tn = r_in / gsz;
+  const uint32_t tm = first_m + (r_in - tn * gsz);
+  const uint32_t seg = tm / static_cast<uint32_t>(g.tiles_per_seg);
+  const uint32_t tj = tm - seg * static_cast<uint32_t>(g.tiles_per_seg);
+  t.ks = ks;
+  t.tm = tm;
+  t.m0 = static_cast<int64_t>(seg) * g.seg_len + static_cast<int64_t>(tj) * BM;
+  t.m_end = min(min(t.m0 + BM, static_cast<int64_t>(seg + 1) * g.seg_len), g.m_total);
   t.m_load = min(t.m_end, g.m_load_end);
-  t.n0 = tn * BN;
+  t.n0 = static_cast<int64_t>(tn) * BN;
   t.n_end = min(t.n0 + static_cast<int64_t>(BN), g.n_total);
-  t.k_beg = t.ks * g.k_per_split;
+  t.k_beg = static_cast<int64_t>(ks) * g.k_per_split;
   t.k_end = min(t.k_beg + g.k_per_split, g.k_total);
   return t;
 }
@@ -254,7 +313,7 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
   static_assert(NS >= 2, "stages");
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
-  __shared__ float2 red[MODE == EPI_FWD ? WAVES_M * BN : 1];
+  __shared__ float2 red[MODE == EPI_FWD && WAVES_M > 1 ? (WAVES_M - 1) * BN : 1];
 
   using LA = RowLoads<BM, NW, RB>;
   using LB = RowLoads<BN, NW, RB>;
@@ -267,15 +326,15 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
   const int half = lane >> 5, l32 = lane & 31;
 
   // ---- this workgroup's tiles: L = start + wi, start + wi + per_xcd, ... < end
-  const int64_t tiles_m = static_cast<int64_t>(g.n_seg) * g.tiles_per_seg;
-  const int64_t total = tiles_m * g.tiles_n * g.k_splits;
-  const int64_t xcd = blockIdx.x & 7;
-  const int64_t wi = blockIdx.x >> 3;
-  const int64_t per_xcd = gridDim.x >> 3;
-  const int64_t q8 = total >> 3, r8 = total & 7;
-  const int64_t start = xcd * q8 + min(xcd, r8);
-  const int64_t end = start + q8 + (xcd < r8 ? 1 : 0);
-  int64_t L = start + wi;
+  const uint32_t total = static_cast<uint32_t>(g.n_seg) * static_cast<uint32_t>(g.tiles_per_seg) *
+                         static_cast<uint32_t>(g.tiles_n) * static_cast<uint32_t>(g.k_splits);
+  const uint32_t xcd = blockIdx.x & 7;
+  const uint32_t wi = blockIdx.x >> 3;
+  const uint32_t per_xcd = gridDim.x >> 3;
+  const uint32_t q8 = total >> 3, r8 = total & 7;
+  const uint32_t start = xcd * q8 + min(xcd, r8);
+  const uint32_t end = start + q8 + (xcd < r8 ? 1u : 0u);
+  uint32_t L = start + wi;
   if (L >= end) return;
 
   // per-tile load state
@@ -293,13 +352,15 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
     klen = t.k_end - t.k_beg;
     nk = t.active() ? static_cast<int>((klen + BK - 1) / BK) : 0;
   };
+  const uint32_t smem_lds = lds_addr(smem);
   auto issue = [&](int kt) {
-    char* st = smem + (kt % NS) * STAGE;
+    const uint32_t st = smem_lds + (kt % NS) * STAGE;
     const int64_t kleft = klen - static_cast<int64_t>(kt) * BK;
+    const bool full = kleft >= BK;
     const char* a = Ab + static_cast<int64_t>(kt) * BK * ES;
     const char* b = Bb + static_cast<int64_t>(kt) * BK * ES;
-    la.issue(st, a, kleft, wave);
-    lb.issue(st + A_BYTES, b, kleft, wave);
+    la.issue(st, a, kleft, full, wave, ES);
+    lb.issue(st + A_BYTES, b, kleft, full, wave, ES);
   };
   auto prologue = [&]() {
 #pragma unroll
@@ -318,6 +379,29 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
   setup(cur);
   prologue();
 
+  // Per-token epilogue inputs of the current tile. Loaded during its first K
+  // slice, so the explicit vmcnt waits of the K loop cover them and the
+  // epilogue needs no wait of its own (which would also wait for the next
+  // tile's prefetch).
+  int32_t yv[NI];
+  float lv[NI];
+  auto load_epi = [&]() {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int64_t tt = cur.n0 + wn * WN + j * 32 + l32;
+      yv[j] = -1;
+      lv[j] = 0.0f;
+      if constexpr (MODE == EPI_FWD) {
+        if (tt < e.fwd.T) yv[j] = e.fwd.targets[tt];
+      } else if constexpr (MODE == EPI_GRAD) {
+        if (tt < e.grad.T) {
+          yv[j] = e.grad.targets[tt];
+          lv[j] = e.grad.lse[tt];
+        }
+      }
+    }
+  };
+
   f32x16 acc[MI][NI];
   while (true) {
 #pragma unroll
@@ -327,8 +411,9 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // One K slice: wait for it, queue slice kt + NS - 1 (unless past the end),
-    // then run the slice's MFMAs interleaved one-for-one with the next
+    // One K slice: wait for it; read the first sub-step's fragments; queue
+    // slice kt + NS - 1 (unless past the end) while those reads are in
+    // flight; then run the slice's MFMAs interleaved one-for-one with the next
     // sub-step's fragment reads.
     auto kstep = [&](int kt, auto issue_next) {
       constexpr bool ISSUE = decltype(issue_next)::value;
@@ -338,22 +423,24 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
         wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();  // every wave's part of slice kt is in; slice kt-1 is free
       asm volatile("" ::"r"(smem) : "memory");
-      if constexpr (ISSUE) issue(kt + NS - 1);
-      asm volatile("" ::"r"(smem) : "memory");
       const char* st = smem + (kt % NS) * STAGE;
       u32x4 fa[2][MI], fb[2][NI];
+      {
+        const int ch = (half ^ swz) * 16;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+          fa[0][i] = *reinterpret_cast<const u32x4*>(st + rowA + i * 32 * RB + ch);
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          fb[0][j] = *reinterpret_cast<const u32x4*>(st + rowB + j * 32 * RB + ch);
+      }
+      asm volatile("" ::"r"(smem) : "memory");
+      if constexpr (ISSUE) issue(kt + NS - 1);
+      if (kt == 0) load_epi();
+      asm volatile("" ::"r"(smem) : "memory");
 #pragma unroll
       for (int s = 0; s < SS; ++s) {
         const int cb = s & 1;
-        if (s == 0) {
-          const int ch = (half ^ swz) * 16;
-#pragma unroll
-          for (int i = 0; i < MI; ++i)
-            fa[0][i] = *reinterpret_cast<const u32x4*>(st + rowA + i * 32 * RB + ch);
-#pragma unroll
-          for (int j = 0; j < NI; ++j)
-            fb[0][j] = *reinterpret_cast<const u32x4*>(st + rowB + j * 32 * RB + ch);
-        }
         if (s + 1 < SS) {  // next sub-step's fragments, in flight during this one's MFMAs
           const int chn = ((2 * (s + 1) + half) ^ swz) * 16;
 #pragma unroll
@@ -370,7 +457,6 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       }
       constexpr int NF = MI + NI;                              // fragment reads per sub-step
       constexpr int NMF = MI * NI * (sizeof(E) == 2 ? 1 : 4);  // MFMAs per sub-step
-      __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
 #pragma unroll
       for (int s = 0; s + 1 < SS; ++s) {
 #pragma unroll
@@ -387,30 +473,17 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       int kt = 0;
       for (; kt + NS - 1 < nk; ++kt) kstep(kt, std::true_type{});
       for (; kt < nk; ++kt) kstep(kt, std::false_type{});
+    } else {
+      load_epi();
     }
-
-    // Per-token epilogue inputs of the finished tile, fetched before the next
-    // tile's loads are queued (vector loads complete in issue order).
-    int32_t yv[NI];
-    float lv[NI];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int64_t tt = cur.n0 + wn * WN + j * 32 + l32;
-      yv[j] = -1;
-      lv[j] = 0.0f;
-      if constexpr (MODE == EPI_FWD) {
-        if (tt < e.fwd.T) yv[j] = e.fwd.targets[tt];
-      } else if constexpr (MODE == EPI_GRAD) {
-        if (tt < e.grad.T) {
-          yv[j] = e.grad.targets[tt];
-          lv[j] = e.grad.lse[tt];
-        }
-      }
-    }
+    // Every load of this tile has landed (the last K step waited for all of
+    // them); saying so explicitly lets the epilogue use its inputs without a
+    // wait that would also cover the next tile's prefetch.
+    wait_vmcnt<0>();
 
     // every wave is done with the stage buffers: start the next tile's loads
-    __syncthreads();
-    const int64_t Ln = L + per_xcd;
+    lds_barrier();
+    const uint32_t Ln = L + per_xcd;
     const bool has_next = Ln < end;
     const TileGeom t = cur;
     if (has_next) {
@@ -430,15 +503,20 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       const int lim = static_cast<int>(max(min(t.m_load - vbase, static_cast<int64_t>(WM)),
                                            static_cast<int64_t>(0)));
       const bool full = lim == WM;
+      // Element r of block i sits at local row i*32 + 8*(r/4) + r%4 + 4*half;
+      // comparisons move the lane's 4*half to the other side, so each is
+      // against a compile-time constant.
       if (!full) {  // rows past the real vocabulary (or the shard) take no part
+        const int lim_l = lim - 4 * half;
 #pragma unroll
         for (int j = 0; j < NI; ++j)
 #pragma unroll
           for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              if (i * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= lim) acc[i][j][r] = -INFINITY;
+              if (i * 32 + 8 * (r >> 2) + (r & 3) >= lim_l) acc[i][j][r] = -INFINITY;
       }
+      float mj[NI], sj[NI];
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         float m = -INFINITY;
@@ -456,44 +534,61 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
             for (int r = 0; r < 16; ++r) s += fast_exp2(fmaf(acc[i][j][r], kLog2e, -mb));
         }
         s += __shfl_xor(s, 32);
+        mj[j] = m;
+        sj[j] = s;
         const int col = wn * WN + j * 32 + l32;
-        if (half == 0) red[wm * BN + col] = make_float2(m, s);
+        // waves past the first along M hand their pair to the first one
+        if (wm > 0 && half == 0) red[(wm - 1) * BN + col] = make_float2(m, s);
 
         // the owning tile stores the target logit
         const int64_t dy = static_cast<int64_t>(yv[j]) - vbase;
         const bool mine = yv[j] >= 0 && dy >= 0 && dy < lim;
         if (__any(mine)) {
           const int loc = static_cast<int>(mine ? dy : 0);
+          const int loc_l = loc - 4 * half;
           float val = 0.0f;
 #pragma unroll
           for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              val = (i * 32 + 8 * (r >> 2) + 4 * half + (r & 3) == loc) ? acc[i][j][r] : val;
+              val = (i * 32 + 8 * (r >> 2) + (r & 3) == loc_l) ? acc[i][j][r] : val;
           if (mine && ((loc >> 2) & 1) == half) f.zt[t.n0 + col] = val;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      __syncthreads();
-      for (int c = tid; c < BN; c += NT) {
-        const int64_t tt = t.n0 + c;
-        if (tt < f.T) {
-          float2 a = red[c];
+      if constexpr (WAVES_M > 1) lds_barrier();
+      // The first wave along M merges the pairs in wave order and stores them.
+      // red is written again only after the next tile's K loop, whose barriers
+      // every wave passes only after this merge, so no barrier follows.
+      if (wm == 0 && half == 0) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const int col = wn * WN + j * 32 + l32;
+          float m = mj[j], s = sj[j];
 #pragma unroll
           for (int w = 1; w < WAVES_M; ++w) {
-            const float2 b = red[w * BN + c];
-            lse_merge(a.x, a.y, b.x, b.y);
+            const float2 b = red[(w - 1) * BN + col];
+            lse_merge(m, s, b.x, b.y);
           }
-          f.stats[t.tm * f.T + tt] = a;
+          const int64_t tt = t.n0 + col;
+          if (tt < f.T) f.stats[t.tm * f.T + tt] = make_float2(m, s);
         }
       }
-      __syncthreads();  // red is reused by the next tile
     } else if constexpr (MODE == EPI_GRAD) {
       const GradArgs& gr = e.grad;
       const float scale = (gr.reduction == 0)
                               ? gr.grad_loss[0] / static_cast<float>(max(gr.n_valid[0], 1))
                               : gr.grad_loss[0];
-      const int64_t vreal_end = min(t.m_end, gr.V_real);
+      // Element (i, 4q + c) of this lane sits at row vb + i*32 + 8*q + c of
+      // the GEMM (vocabulary row v_off + that of the table). Limits and the
+      // target are taken relative to vb and clamped to [-1, WM], so every
+      // test is a 32-bit compare against a compile-time constant.
+      const int64_t vb = vbase + 4 * half;
+      auto rel = [&](int64_t x) {
+        return static_cast<int>(max(min(x - vb, static_cast<int64_t>(WM)), static_cast<int64_t>(-1)));
+      };
+      const int real_l = rel(min(t.m_end, gr.V_real - gr.v_off));  // rows below are real classes
+      const int end_l = rel(t.m_end);                                 // rows below exist
       E* Gp = static_cast<E*>(gr.G);
       E* GTp = static_cast<E*>(gr.GT);
 #pragma unroll
@@ -502,58 +597,60 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
         const bool tin = tt < gr.T;
         const int64_t y = yv[j];
         const bool valid = tin && y >= 0 && y < gr.V_real;
+        const int y_l = valid ? rel(y - gr.v_off) : -1;
+        const int lim_l = valid ? real_l : -1;
         const float nl = lv[j] * kLog2e;
         const bool t_gt = tt < gr.ldGT;
+        E* grow = Gp + tt * gr.ldG + vb;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int64_t v0 = vbase + i * 32 + 8 * q + 4 * half;
+            const int r0 = i * 32 + 8 * q;
             float gv[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              const int64_t v = v0 + c;
               const float p = fast_exp2(fmaf(acc[i][j][4 * q + c], kLog2e, -nl));
-              const float oh = (v == y) ? 1.0f : 0.0f;
+              const float oh = (r0 + c == y_l) ? 1.0f : 0.0f;
               // select, never multiply, so a non-finite p of a discarded entry cannot leak
-              gv[c] = (valid && v < vreal_end) ? scale * (p - oh) : 0.0f;
+              gv[c] = (r0 + c < lim_l) ? scale * (p - oh) : 0.0f;
             }
             if constexpr (sizeof(E) == 2) {
               uint16_t hb[4];
 #pragma unroll
               for (int c = 0; c < 4; ++c) hb[c] = f32_to_bf16(gv[c]);
               if (tin) {
-                if (gr.vec_store && v0 + 3 < t.m_end) {
+                if (gr.vec_store && r0 + 3 < end_l) {
                   u32x2 pk;
                   pk.x = static_cast<uint32_t>(hb[0]) | (static_cast<uint32_t>(hb[1]) << 16);
                   pk.y = static_cast<uint32_t>(hb[2]) | (static_cast<uint32_t>(hb[3]) << 16);
-                  *reinterpret_cast<u32x2*>(Gp + tt * gr.ldG + v0) = pk;
+                  *reinterpret_cast<u32x2*>(grow + r0) = pk;
                 } else {
 #pragma unroll
                   for (int c = 0; c < 4; ++c)
-                    if (v0 + c < t.m_end) Gp[tt * gr.ldG + v0 + c] = hb[c];
+                    if (r0 + c < end_l) grow[r0 + c] = hb[c];
                 }
               }
               if (t_gt) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                  if (v0 + c < t.m_end) GTp[(v0 + c) * gr.ldGT + tt] = hb[c];
+                  if (r0 + c < end_l) GTp[(vb + r0 + c) * gr.ldGT + tt] = hb[c];
               }
             } else {
               if (tin) {
-                if (gr.vec_store && v0 + 3 < t.m_end) {
+                if (gr.vec_store && r0 + 3 < end_l) {
                   f32x4 pk = {gv[0], gv[1], gv[2], gv[3]};
-                  *reinterpret_cast<f32x4*>(Gp + tt * gr.ldG + v0) = pk;
+                  *reinterpret_cast<f32x4*>(grow + r0) = pk;
                 } else {
 #pragma unroll
                   for (int c = 0; c < 4; ++c)
-                    if (v0 + c < t.m_end) Gp[tt * gr.ldG + v0 + c] = gv[c];
+                    if (r0 + c < end_l) grow[r0 + c] = gv[c];
                 }
               }
               if (t_gt) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                  if (v0 + c < t.m_end) GTp[(v0 + c) * gr.ldGT + tt] = gv[c];
+                  if (r0 + c < end_l) GTp[(vb + r0 + c) * gr.ldGT + tt] = gv[c];
               }
             }
           }
@@ -561,26 +658,34 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
     } else {  // EPI_STORE
       const StoreArgs& st = e.store;
       float* Cp = st.C + t.ks * st.split_stride;
+      // element (i, r) of this lane: row vb + i*32 + 8*(r/4) + r%4
+      const int64_t vb = vbase + 4 * half;
+      auto rel = [&](int64_t x) {
+        return static_cast<int>(max(min(x - vb, static_cast<int64_t>(WM)), static_cast<int64_t>(-1)));
+      };
+      const int end_l = rel(t.m_end);
+      const int zero_l = rel(st.m_zero_from);
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int j = 0; j < NI; ++j) {
+        const int64_t n = t.n0 + wn * WN + j * 32 + l32;
+        if (n >= t.n_end) continue;
+        float* col = Cp + vb * st.ldc + n;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = vbase + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (m >= t.m_end) continue;
-          const bool zero_row = m >= st.m_zero_from;
-          if (zero_row && st.accumulate) continue;
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-          for (int j = 0; j < NI; ++j) {
-            const int64_t n = t.n0 + wn * WN + j * 32 + l32;
-            if (n >= t.n_end) continue;
-            float* dst = Cp + m * st.ldc + n;
+          for (int r = 0; r < 16; ++r) {
+            const int rr = i * 32 + 8 * (r >> 2) + (r & 3);
+            if (rr >= end_l) continue;
+            const bool zero_row = rr >= zero_l;
+            if (zero_row && st.accumulate) continue;
+            float* dst = col + rr * st.ldc;
             const float v = zero_row ? 0.0f : acc[i][j][r];
-            if (st.accumulate)
-              *dst += v;
+            if (st.accumulate)  // the only writer of this element in this launch
+              __hip_atomic_fetch_add(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             else
               *dst = v;
           }
-        }
+      }
     }
 
     if (!has_next) break;
