@@ -153,9 +153,14 @@ def main():
     gl = torch.ones(1, **f32)
     stream = torch.cuda.current_stream(dev)
 
-    # events: 0 start | 1 after lookup | 2 after forward | 3..7 backward stages | 8 after scatter
+    # events: 0 start | 1 after lookup | 2 after forward | backward: start, then per
+    # vocabulary chunk (after G, after dh, after dW) | last: after the scatter
+    n_bwd_ev = V._lib.vce_bwd_event_count(T, H, Vr, Vp, n, dt_code)
+    n_chunks = (n_bwd_ev - 1) // 3
+    n_ev = 3 + n_bwd_ev + 1
+
     def new_events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(9)]
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
 
     def step(ev=None):
         if ev is not None:
@@ -169,11 +174,11 @@ def main():
             ev[2].record(stream)
         V.vce_bwd(h, W, tg, fo.lse, gl, fo.n_valid, Vr, n, inp.ignore_index, V.REDUCE_MEAN,
                   dh=dh, dW=dW, accumulate_dW=False, ws=ws["bwd"],
-                  events=None if ev is None else ev[3:8])
+                  events=None if ev is None else ev[3:3 + n_bwd_ev])
         if tied:
             V.vemb_bwd(ids, dh, Vr, Vp, n, dW=dW, accumulate=True, ws=ws["emb"])
         if ev is not None:
-            ev[8].record(stream)
+            ev[n_ev - 1].record(stream)
 
     log(f"[bench] warmup {a.warmup}")
     for _ in range(a.warmup):
@@ -192,24 +197,29 @@ def main():
     def span(i, j):
         return float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))
 
+    b0 = 3  # first backward event
     phase = {
         "vemb_fwd": span(0, 1),
         "vce_fwd": span(1, 2),
-        "vce_bwd.transposes": span(3, 4),
-        "vce_bwd.recompute_G": span(4, 5),
-        "vce_bwd.dh": span(5, 6),
-        "vce_bwd.dW": span(6, 7),
-        "vemb_bwd": span(7, 8),
+        "vce_bwd.recompute_G": sum(span(b0 + 3 * c, b0 + 3 * c + 1) for c in range(n_chunks)),
+        "vce_bwd.dh": sum(span(b0 + 3 * c + 1, b0 + 3 * c + 2) for c in range(n_chunks)),
+        "vce_bwd.dW": sum(span(b0 + 3 * c + 2, b0 + 3 * c + 3) for c in range(n_chunks)),
+        "vemb_bwd": span(n_ev - 2, n_ev - 1),
     }
     log(f"[bench] {ms_step:.3f} ms/step, phases (ms) {json.dumps(phase)}")
 
-    flop_gemm = 2.0 * T * H * Vr  # algorithmic flops of each of the four CE GEMMs
+    # Algorithmic flops of each of the four CE GEMMs per step: 2*T*H*V_real. The
+    # backward GEMMs run once per vocabulary chunk; their time is summed over the
+    # chunks, so flops / time is also flops per launch / mean launch time.
+    flop_gemm = 2.0 * T * H * Vr
     gemms = {
         "k_gemm_tn<bf16,EPI_FWD> (vce_fwd: logits GEMM + online max/sum-exp)": phase["vce_fwd"],
-        "k_gemm_tn<bf16,EPI_GRAD> (logit recompute + G = scale*(softmax-onehot))":
-            phase["vce_bwd.recompute_G"],
-        "k_gemm_tn<bf16,EPI_STORE> (dh = G W, split-K + fixed-order sum)": phase["vce_bwd.dh"],
-        "k_gemm_tn<bf16,EPI_STORE> (dW = G^T h)": phase["vce_bwd.dW"],
+        f"k_gemm_tn<bf16,EPI_GRAD> (logit recompute + G = scale*(softmax-onehot), "
+        f"{n_chunks} vocabulary chunks)": phase["vce_bwd.recompute_G"],
+        f"k_gemm_tn<bf16,EPI_STORE,KC,KM> (dh += G_chunk W_chunk, {n_chunks} chunks)":
+            phase["vce_bwd.dh"],
+        f"k_gemm_tn<bf16,EPI_STORE,KM,KM> (dW_chunk = G_chunk^T h, {n_chunks} chunks)":
+            phase["vce_bwd.dW"],
     }
     dom = max(gemms, key=gemms.get)
     dom_ms = gemms[dom]

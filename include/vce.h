@@ -121,8 +121,11 @@ vce_status vce_fwd(const void* h, const void* W, const int32_t* targets,
  * accumulate_dW = 0: every row of dW is written (rows >= V_real get 0);     *
  * accumulate_dW = 1: G^T h is added into rows < V_real, rows >= V_real are  *
  * left unchanged. lse must be the forward's output for the same inputs.     *
- * G is staged in the workspace in the input element type (bf16 rounded to  *
- * nearest-even, or float32).                                                *
+ * The vocabulary is processed in chunks (each shard, cut into pieces of at *
+ * most 32768 rows): G of one chunk ([T][chunk], never [T][V]) is staged in  *
+ * the workspace in the input element type (bf16 rounded to nearest-even,    *
+ * or float32), then dh receives G_chunk W_chunk (in chunk order) and the    *
+ * chunk's rows of dW receive G_chunk^T h.                                   *
  * ------------------------------------------------------------------------ */
 size_t vce_bwd_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
                                int32_t num_shards, vce_dtype dt);
@@ -134,19 +137,24 @@ vce_status vce_bwd(const void* h, const void* W, const int32_t* targets, const f
                    float* dh, float* dW, int32_t accumulate_dW,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* Number of events vce_bwd_timed records for these arguments:
+ * 1 + 3 * (number of vocabulary chunks); 0 for invalid arguments. */
+int64_t vce_bwd_event_count(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                            int32_t num_shards, vce_dtype dt);
+
 /* Same as vce_bwd, for profiling tools: when `events` is not NULL it holds
- * VCE_BWD_EVENTS hipEvent_t handles (passed as void*) created by the caller;
- * they are recorded on `stream` at the stage boundaries of the backward:
- *   events[0] before the first kernel, [1] after the operand transposes,
- *   [2] after the logit-recompute / G kernel, [3] after dh (including its
- *   split-K sum), [4] after dW. With events == NULL this is vce_bwd. */
-#define VCE_BWD_EVENTS 5
+ * n_events == vce_bwd_event_count(...) hipEvent_t handles (passed as void*)
+ * created by the caller; they are recorded on `stream`: events[0] before the
+ * first kernel, then for chunk c events[1 + 3c] after its G, [2 + 3c] after
+ * its dh contribution and [3 + 3c] after its dW rows. A different n_events
+ * returns VCE_ERR_SHAPE. With events == NULL this is vce_bwd. */
 vce_status vce_bwd_timed(const void* h, const void* W, const int32_t* targets, const float* lse,
                          const float* grad_loss, const int32_t* n_valid, vce_reduction red,
                          int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
                          int32_t num_shards, int32_t ignore_index, vce_dtype dt,
                          float* dh, float* dW, int32_t accumulate_dW,
-                         void* ws, size_t ws_bytes, void* stream, void* const* events);
+                         void* ws, size_t ws_bytes, void* stream, void* const* events,
+                         int64_t n_events);
 
 /* ------------------------------------------------------------------------ *
  * Masked embedding lookup.                                                  *

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in vce.SIGNATURES, n
@@ -119,6 +119,20 @@ def test_candidates_argument_errors():
 def test_workspace_queries_are_deterministic_and_reject_bad_shapes():
     a = lib.vce_bwd_workspace_bytes(8192, 3072, 201088, 201088, 8, 1)
     b = lib.vce_bwd_workspace_bytes(8192, 3072, 201088, 201088, 8, 1)
-    assert a == b and a > 2 * 8192 * 201088 * 2
+    # one chunk of G (a shard: 25136 columns, padded to 25152) is staged, never [T, V]
+    assert a == b == 8192 * 25152 * 2
+    assert lib.vce_bwd_workspace_bytes(8192, 3072, 201088, 201088, 1, 1) < 8192 * 32768 * 2
     assert lib.vce_fwd_workspace_bytes(8, 64, 100, 101, 2, 1) == 0  # 101 % 2 != 0
     assert lib.vce_bwd_workspace_bytes(8, 64, 100, 128, 4, 3) == 0  # bad dtype
+
+
+def test_bwd_event_count_and_timed_checks():
+    # 8 shards of 25136 rows: one chunk per shard
+    assert lib.vce_bwd_event_count(16384, 3072, 201088, 201088, 8, 1) == 1 + 3 * 8
+    # one shard of 201088 rows: pieces of at most 32768 rows
+    assert lib.vce_bwd_event_count(16384, 3072, 201088, 201088, 1, 1) == 1 + 3 * 7
+    assert lib.vce_bwd_event_count(8, 64, 100, 101, 2, 1) == 0      # 101 % 2 != 0
+    ev = (ctypes.c_void_p * 3)()
+    args = (A, B, C, A, C, A, 0, 4, 64, 1000, 1024, 4, -100, 1, A, B, 0, A, 1 << 40, None)
+    # wrong event count is rejected before any HIP call
+    assert lib.vce_bwd_timed(*args, ev, 3) == SHAPE

@@ -21,7 +21,6 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvce.so")
 
 VCE_F32, VCE_BF16 = 0, 1
-VCE_BWD_EVENTS = 5
 REDUCE_MEAN, REDUCE_SUM = 0, 1
 
 STATUS = {0: "VCE_OK", 1: "VCE_ERR_NULL", 2: "VCE_ERR_SHAPE", 3: "VCE_ERR_SHARD",
@@ -41,8 +40,9 @@ SIGNATURES = {
     "vce_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32, _I32]),
     "vce_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _I32, _I32, _I32,
                        _P, _P, _I32, _P, _SZ, _P]),
+    "vce_bwd_event_count": (_I64, [_I64, _I64, _I64, _I64, _I32, _I32]),
     "vce_bwd_timed": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _I32, _I32,
-                             _I32, _P, _P, _I32, _P, _SZ, _P, _P]),
+                             _I32, _P, _P, _I32, _P, _SZ, _P, _P, _I64]),
     "vemb_fwd": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P, _P, _P]),
     "vemb_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
     "vemb_bwd": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _I64, _I32, _P, _I32, _P, _SZ, _P]),
@@ -126,6 +126,10 @@ def vce_bwd_workspace_bytes(T, H, V_real, V_pad, num_shards, dtype=VCE_BF16) -> 
     return int(lib.vce_bwd_workspace_bytes(T, H, V_real, V_pad, num_shards, dtype))
 
 
+def vce_bwd_event_count(T, H, V_real, V_pad, num_shards, dt) -> int:
+    return int(lib.vce_bwd_event_count(T, H, V_real, V_pad, num_shards, dt))
+
+
 def vemb_bwd_workspace_bytes(T, H, V_real, V_pad) -> int:
     return int(lib.vemb_bwd_workspace_bytes(T, H, V_real, V_pad))
 
@@ -177,8 +181,9 @@ def vce_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.
             accumulate_dW: bool = False, ws: Optional[torch.Tensor] = None,
             stream=None, events=None) -> BwdOut:
     """Cross-entropy backward: dh [T,H] and dW [V_pad,H] (float32). `events`
-    (optional): VCE_BWD_EVENTS torch.cuda.Event objects recorded at the stage
-    boundaries (calls vce_bwd_timed)."""
+    (optional): vce_bwd_event_count(...) torch.cuda.Event objects, recorded
+    before the first kernel and after each vocabulary chunk's G, dh and dW
+    kernels (calls vce_bwd_timed)."""
     T, H = h.shape
     V_pad = W.shape[0]
     dt = _dt(h)
@@ -203,13 +208,14 @@ def vce_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.
     if events is None:
         _check("vce_bwd", lib.vce_bwd(*args))
     else:
-        if len(events) != VCE_BWD_EVENTS:
-            raise ValueError(f"events must hold {VCE_BWD_EVENTS} torch.cuda.Event objects")
+        n_ev = vce_bwd_event_count(T, H, V_real, V_pad, num_shards, dt)
+        if len(events) != n_ev:
+            raise ValueError(f"events must hold {n_ev} torch.cuda.Event objects")
         for e in events:
             if e.cuda_event == 0:   # created lazily by torch: force creation on this device
                 e.record(torch.cuda.current_stream(dev))
-        arr = (ctypes.c_void_p * VCE_BWD_EVENTS)(*[e.cuda_event for e in events])
-        _check("vce_bwd_timed", lib.vce_bwd_timed(*args, arr))
+        arr = (ctypes.c_void_p * n_ev)(*[e.cuda_event for e in events])
+        _check("vce_bwd_timed", lib.vce_bwd_timed(*args, arr, n_ev))
     return BwdOut(dh, dW)
 
 

@@ -1,23 +1,38 @@
 // One MFMA GEMM core for every contraction of the path:
-//     C[m, n] = sum_k A[m, k] * B[n, k]     (both operands K-contiguous)
-// with three epilogues:
+//     C[m, n] = sum_k A(m, k) * B(n, k)
+// Each operand is either K-contiguous (element (p, k) at p*ld + k) or
+// K-major (element (p, k) at k*ld + p). Three epilogues:
 //   EPI_FWD   logits tile -> per-token (max, sum exp) over the tile's real
 //             vocabulary rows + the target logit from the owning tile
-//   EPI_GRAD  logits tile -> G = scale * (softmax - onehot), stored twice
-//             (token-major and vocabulary-major) in the input element type
+//   EPI_GRAD  logits tile -> G = scale * (softmax - onehot), stored
+//             token-major in the input element type
 //   EPI_STORE plain float32 store / accumulate (dh and dW)
 //
 // Workgroup: WAVES_M x WAVES_N waves over a BM x BN tile; each wave owns a
 // (BM/WAVES_M) x (BN/WAVES_N) sub-tile made of 32 x 32 MFMA blocks. K
-// advances in 128-byte slices (64 bf16 or 32 float), staged in LDS by direct
-// global->LDS loads (global_load_lds_dwordx4), two stages deep. Each LDS row
-// holds one 128-byte K slice of one operand row, its eight 16-byte chunks
-// permuted by ((row >> 1) & 7): the 16 lanes that one LDS cycle serves read 16
-// consecutive rows, which then cover all 64 banks exactly once.
+// advances in slices of 128 bytes per operand position (64 bf16 or 32
+// float), staged in LDS by direct global->LDS loads (global_load_lds_dwordx4),
+// NS stages deep; both layouts fill one stage with ROWS * 128 bytes.
 //
-// Operand rows past the valid range are loaded from a clamped (valid) row and
-// their results are discarded by the epilogues; only a K slice that runs past
-// K reads zeros for the missing chunks, so garbage never enters a valid sum.
+// K-contiguous stage: one 128-byte row per position, its eight 16-byte chunks
+// permuted by ((row >> 1) & 7) so that the 16 lanes one LDS cycle serves (16
+// consecutive rows, one chunk) cover all 64 banks. A fragment is one
+// ds_read_b128 per lane.
+//
+// K-major stage: one row per K index holding the tile's positions. bf16
+// fragments come from two ds_read_b64_tr_b16 per lane: within each group of
+// 16 lanes the instruction hands lane i, element e, the element i % 4 of the
+// 8 bytes that lane 4e + i/4 addressed; lane 4e + b of the group addresses
+// row k + e at positions 4b..4b+3, so lane i receives four consecutive K
+// values of position i. The 64-byte blocks of each 256-byte window of a row
+// are permuted by (k & 3), so the four rows one 32-lane pass reads fall on
+// different banks. float fragments are four ds_read_b32; their rows k and
+// k + 4 are separated by permuting 128-byte halves by ((k >> 2) & 1).
+//
+// Operand positions past the valid range read a clamped (valid) position and
+// their results are discarded by the epilogues; K positions past K read zeros
+// in whole 16-byte chunks (a row must therefore be readable up to its valid
+// length rounded up to 16 bytes), so garbage never enters a valid sum.
 //
 // The M side can be cut into equal segments (the vocabulary shards): tiles
 // never cross a segment end, so every tile computes with one shard's rows.
@@ -33,18 +48,18 @@ enum EpiMode { EPI_FWD = 0, EPI_GRAD = 1, EPI_STORE = 2 };
 
 struct GemmShape {
   const void* A;
-  int64_t lda;          // elements between consecutive A rows
+  int64_t lda;          // elements between consecutive rows of A's storage
   const void* B;
   int64_t ldb;
-  int64_t seg_len;      // rows per M segment
+  int64_t seg_len;      // M positions per segment
   int32_t n_seg;        // number of M segments
   int32_t tiles_per_seg;
   int64_t m_total;      // tile ends are clipped to this
-  int64_t m_load_end;   // A rows at or past this are never read
-  int64_t n_total;      // B rows at or past this are never read
+  int64_t m_load_end;   // A positions at or past this are never read
+  int64_t n_total;      // B positions at or past this are never read
   int32_t tiles_n;
   int32_t k_splits;     // split of K into independent partial products
-  int64_t k_total;      // K extent in elements (a multiple of the 16-byte chunk)
+  int64_t k_total;      // K extent; K positions at or past it read as zero
   int64_t k_per_split;  // multiple of the K slice
   int32_t group_m;      // tiles along M visited together by one XCD
 };
@@ -69,8 +84,6 @@ struct GradArgs {
   int32_t vec_store;    // 1 if every tile start is a multiple of 4 columns
   void* G;              // [T][ldG]
   int64_t ldG;
-  void* GT;             // [V rows][ldGT]; columns T..ldGT-1 receive 0
-  int64_t ldGT;
 };
 
 struct StoreArgs {
@@ -87,14 +100,14 @@ struct EpiArgs {
   StoreArgs store;
 };
 
-// 16 zero bytes: the source of the chunks of a K slice that lie past K
+// 16 zero bytes: the source of the chunks that lie past K
 static __device__ __attribute__((aligned(64))) const uint32_t g_zero_chunk[16] = {0};
 
 template <typename E>
 struct Elem;
 template <>
 struct Elem<uint16_t> {  // bf16 bits
-  static constexpr int kSlice = 64;  // elements per 128-byte K slice
+  static constexpr int kSlice = 64;  // K elements per 128-byte slice
   static constexpr int kChunk = 8;   // elements per 16-byte chunk
 };
 template <>
@@ -102,14 +115,6 @@ struct Elem<float> {
   static constexpr int kSlice = 32;
   static constexpr int kChunk = 4;
 };
-
-// Chunk permutation of LDS row `row` for rows of RB bytes (8 or 4 chunks):
-// the 16 lanes of one LDS cycle read 16 consecutive rows at one logical
-// chunk, and the permutation spreads them over all 64 banks.
-template <int RB>
-__device__ __forceinline__ int lds_swz(int row) {
-  return RB == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
-}
 
 // s_waitcnt vmcnt(N) with the other counters left free (gfx9 encoding)
 template <int N>
@@ -137,8 +142,8 @@ __device__ __forceinline__ void mma_chunk<uint16_t>(f32x16& acc, const u32x4& a,
 
 // float32: the lane's 4 floats are 4 K positions; one 32x32x2 MFMA per
 // component (lanes 0-31 give one K position, lanes 32-63 another). A and B
-// use the same assignment, so the four products cover the 8 K values of the
-// two chunks once each.
+// use the same assignment, so the four products cover the 8 K values of a
+// sub-step once each.
 template <>
 __device__ __forceinline__ void mma_chunk<float>(f32x16& acc, const u32x4& a, const u32x4& b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
@@ -148,6 +153,9 @@ __device__ __forceinline__ void mma_chunk<float>(f32x16& acc, const u32x4& a, co
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
 // 32-bit LDS byte address of a pointer into a __shared__ array
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -181,47 +189,56 @@ __device__ __forceinline__ void dma16(const void* p, uint32_t lds) {
 }
 #pragma clang diagnostic pop
 
-// Global -> LDS staging of ROWS operand rows of RB-byte K slices by NW waves.
-// One wave-wide load moves 1 KB = RPI rows: wave w, load q moves tile rows
-// [(q*NW + w)*RPI, +RPI); lane l brings chunk (l % CPR) ^ swz(row) of row
-// l / CPR, landing at LDS row*RB + (l % CPR)*16 (lane-linear). The chunk a
-// lane brings does not depend on q, so when every row of the tile is valid
-// the lane's global offset is one value plus a uniform stride per load.
-template <int ROWS, int NW, int RB>
-struct RowLoads {
+// ---------------------------------------------------------------- stagers
+// A stager brings one operand's K slice of one tile into an LDS stage and
+// reads MFMA fragments out of it. ROWS = positions of the tile (BM or BN),
+// NW = waves of the workgroup. Interface:
+//   init<NB>(p0, p_end, ld, wave, lane, wbase)
+//        tile positions [p0, p_end) are valid; the wave's fragments cover NB
+//        blocks of 32 positions from tile position wbase
+//   issue(lds, base, kleft, wave)   base = element (p0, k); kleft = K left
+//   frag(stage, block, s, lane)     fragment of one block at sub-step s
+//                                   (16 bf16 / 8 float of K)
+//   kReads                          LDS read instructions per fragment
+
+// K-contiguous operand
+template <typename E, int ROWS, int NW>
+struct StageKC {
+  static constexpr int ES = sizeof(E);
+  static constexpr int EPC = Elem<E>::kChunk;
+  static constexpr int BK = Elem<E>::kSlice;
+  static constexpr int RB = 128;          // bytes per LDS row
   static constexpr int CPR = RB / 16;     // chunks per row
   static constexpr int RPI = 64 / CPR;    // rows per wave-wide load
   static constexpr int Q = ROWS / (RPI * NW);
+  static constexpr int kReads = 1;
   static_assert(ROWS % (RPI * NW) == 0, "load split");
-  static_assert(RB != 128 || NW % 2 == 0, "chunk choice must not depend on q");
+  static_assert(NW % 2 == 0, "chunk choice must not depend on the load index");
   uint32_t off0;     // this lane's byte offset for load 0 (chunk included)
   int32_t lrow;      // this lane's tile row for load 0
   int32_t kch;       // element offset of this lane's chunk inside the K slice
-  int64_t qstride;   // bytes between the rows of load q and load q + 1
+  int32_t nrows;     // valid rows of the tile
   int64_t rstride;   // bytes between consecutive rows
-  int32_t nrows;     // valid rows of the tile (rows past it read the last valid row)
-  bool all_rows;
+  uint32_t frag0;    // this lane's LDS row offset for block 0
 
-  template <int EPC>
-  __device__ __forceinline__ void init(int64_t row0, int64_t row_end, int64_t ld, int wave,
-                                       int lane, int esize) {
+  __device__ __forceinline__ static int swz(int row) { return (row >> 1) & 7; }
+
+  template <int NB>
+  __device__ __forceinline__ void init(int64_t p0, int64_t p_end, int64_t ld, int wave, int lane,
+                                       int wbase) {
     lrow = wave * RPI + lane / CPR;
-    const int lch = (lane % CPR) ^ lds_swz<RB>(lrow);
+    const int lch = (lane % CPR) ^ swz(lrow);
     kch = lch * EPC;
-    rstride = ld * esize;
-    qstride = static_cast<int64_t>(NW) * RPI * rstride;
-    nrows = static_cast<int32_t>(min(row_end - row0, static_cast<int64_t>(ROWS)));
-    all_rows = nrows == ROWS;
-    off0 = static_cast<uint32_t>(lrow * rstride + kch * esize);
+    rstride = ld * ES;
+    nrows = static_cast<int32_t>(min(p_end - p0, static_cast<int64_t>(ROWS)));
+    off0 = static_cast<uint32_t>(lrow * rstride + kch * ES);
+    frag0 = static_cast<uint32_t>((wbase + (lane & 31)) * RB);
   }
 
-  // stage one K slice: `base` points at (row0, k), `lds` is the stage's LDS
-  // address; `kleft` = K elements left from k. The common case (all rows
-  // valid, a whole slice) addresses from uniform bases; otherwise each lane
-  // clamps its row and takes the zero chunk for chunks past K.
-  __device__ __forceinline__ void issue(uint32_t lds, const char* base, int64_t kleft, bool full,
-                                        int wave, int esize) const {
-    if (full && all_rows) {
+  __device__ __forceinline__ void issue(uint32_t lds, const char* base, int64_t kleft,
+                                        int wave) const {
+    if (kleft >= BK && nrows == ROWS) {
+      const int64_t qstride = static_cast<int64_t>(NW) * RPI * rstride;
 #pragma unroll
       for (int q = 0; q < Q; ++q) dma16(base + q * qstride, off0, lds + (q * NW + wave) * RPI * RB);
     } else {
@@ -229,13 +246,122 @@ struct RowLoads {
       for (int q = 0; q < Q; ++q) {
         int r = lrow + q * NW * RPI;
         if (r >= nrows) r = nrows - 1;  // the result of this row is discarded
-        const void* p = base + r * rstride + kch * esize;
+        const void* p = base + r * rstride + kch * ES;
         if (kch >= kleft) p = g_zero_chunk;
         dma16(p, lds + (q * NW + wave) * RPI * RB);
       }
     }
   }
+
+  // fragment: row (wbase + block*32 + lane%32), logical chunk 2s + lane/32
+  __device__ __forceinline__ u32x4 frag(const char* st, int block, int s, int lane) const {
+    const int ch = ((2 * s + (lane >> 5)) ^ swz(lane & 31)) * 16;
+    return *reinterpret_cast<const u32x4*>(st + frag0 + block * 32 * RB + ch);
+  }
 };
+
+// K-major operand
+template <typename E, int ROWS, int NW>
+struct StageKM {
+  static constexpr int ES = sizeof(E);
+  static constexpr int EPC = Elem<E>::kChunk;
+  static constexpr int BK = Elem<E>::kSlice;   // K rows per slice
+  static constexpr int RBT = ROWS * ES;        // bytes per K row of the tile
+  static constexpr int RPL = 1024 / RBT;       // K rows per wave-wide load
+  static constexpr int CPR = RBT / 16;         // chunks per K row
+  static constexpr int Q = BK / (RPL * NW);
+  static constexpr int kReads = ES == 2 ? 2 : 4;
+  static_assert(1024 % RBT == 0 && RBT >= 256, "row size");
+  static_assert(BK % (RPL * NW) == 0, "load split");
+  static_assert((RPL * NW) % (ES == 2 ? 4 : 8) == 0, "chunk choice must not depend on q");
+  uint32_t off0;     // this lane's byte offset for load 0 (chunk included)
+  int32_t lk;        // this lane's K row (within the slice) for load 0
+  int32_t lch;       // this lane's logical chunk (of positions) in the row
+  int32_t last_ch;   // last chunk holding a valid position
+  bool all_cols;
+  int64_t rstride;   // bytes between consecutive K rows in global memory
+  uint32_t fb[4];    // this lane's LDS byte offset of each block's fragment (sub-step 0)
+
+  // permutation of the chunks of K row k
+  __device__ __forceinline__ static int swz(int k) {
+    return ES == 2 ? ((k & 3) << 2) : (((k >> 2) & 1) << 3);
+  }
+
+  template <int NB>
+  __device__ __forceinline__ void init(int64_t p0, int64_t p_end, int64_t ld, int wave, int lane,
+                                       int wbase) {
+    static_assert(NB <= 4, "fragment offsets");
+    lk = wave * RPL + lane / CPR;
+    lch = (lane % CPR) ^ swz(lk);
+    rstride = ld * ES;
+    const int64_t npos = min(p_end - p0, static_cast<int64_t>(ROWS));
+    all_cols = npos == ROWS;
+    last_ch = static_cast<int32_t>((npos - 1) / EPC);
+    off0 = static_cast<uint32_t>(lk * rstride + lch * 16);
+    if constexpr (ES == 2) {
+      const int i = lane & 15, g = (lane >> 4) & 1, hk = lane >> 5;
+      const int krow = 8 * hk + (i >> 2);  // row within the sub-step for read 0
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int pos = wbase + b * 32 + 16 * g + 4 * (i & 3);
+        const int ch = (pos / EPC) ^ swz(krow);
+        fb[b] = static_cast<uint32_t>(krow * RBT + ch * 16 + (pos % EPC) * ES);
+      }
+    } else {
+      const int l32 = lane & 31, half = lane >> 5;
+      const int krow = 4 * half;           // row within the sub-step for component 0
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int pos = wbase + b * 32 + l32;
+        const int ch = (pos / EPC) ^ swz(krow);
+        fb[b] = static_cast<uint32_t>(krow * RBT + ch * 16 + (pos % EPC) * ES);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void issue(uint32_t lds, const char* base, int64_t kleft,
+                                        int wave) const {
+    if (kleft >= BK && all_cols) {
+      const int64_t qstride = static_cast<int64_t>(NW) * RPL * rstride;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) dma16(base + q * qstride, off0, lds + (q * NW + wave) * 1024);
+    } else {
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int k = lk + q * NW * RPL;
+        const int c = min(lch, last_ch);  // positions past the valid range: discarded
+        const void* p = base + k * rstride + c * 16;
+        if (k >= kleft) p = g_zero_chunk;
+        dma16(p, lds + (q * NW + wave) * 1024);
+      }
+    }
+  }
+
+  __device__ __forceinline__ u32x4 frag(const char* st, int block, int s, int lane) const {
+    (void)lane;
+    const char* p = st + fb[block];
+    if constexpr (ES == 2) {
+      // read r covers K rows 16s + 8hk + 4r + (0..3); rows 4 apart share the
+      // chunk permutation, so read 1 is read 0 four rows further
+      const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * s * RBT));
+      const s16x4 r1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + (16 * s + 4) * RBT));
+      const u32x2 a = __builtin_bit_cast(u32x2, r0), b = __builtin_bit_cast(u32x2, r1);
+      return u32x4{a.x, a.y, b.x, b.y};
+    } else {
+      // component c: K row 8s + 4*half + c (the permutation depends on half only)
+      u32x4 v;
+      v.x = *(const lds_u32*)(p + (8 * s + 0) * RBT);
+      v.y = *(const lds_u32*)(p + (8 * s + 1) * RBT);
+      v.z = *(const lds_u32*)(p + (8 * s + 2) * RBT);
+      v.w = *(const lds_u32*)(p + (8 * s + 3) * RBT);
+      return v;
+    }
+  }
+};
+
+template <typename E, int ROWS, int NW, bool KMAJ>
+using Stager = typename std::conditional<KMAJ, StageKM<E, ROWS, NW>, StageKC<E, ROWS, NW>>::type;
 
 // Compile-time loop: f(integral_constant<int, I>) for I in [I0, N)
 template <int I0, int N, typename F>
@@ -295,29 +421,28 @@ __device__ __forceinline__ TileGeom decode_tile(const GemmShape& g, uint32_t L) 
 // it together, sharing operand tiles in that XCD's L2. While a tile's
 // epilogue runs, the first K slices of the workgroup's next tile are already
 // on their way into LDS.
-template <typename E, int MODE, int BM, int BN, int WAVES_M, int WAVES_N, int RB, int NS, int OCC>
+template <typename E, int MODE, bool AKM, bool BKM, int BM, int BN, int WAVES_M, int WAVES_N,
+          int NS, int OCC>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N,
                                                       64 * WAVES_M * WAVES_N),
                           amdgpu_waves_per_eu(OCC, OCC)))
 void k_gemm_tn(GemmShape g, EpiArgs e) {
   constexpr int NW = WAVES_M * WAVES_N;
-  constexpr int NT = 64 * NW;
   constexpr int ES = sizeof(E);
-  constexpr int BK = RB / ES;              // K elements per slice
-  constexpr int EPC = Elem<E>::kChunk;
-  constexpr int SS = RB / 32;              // sub-steps per slice (two chunks each)
+  constexpr int BK = Elem<E>::kSlice;      // K elements per slice
+  constexpr int SS = 4;                    // sub-steps per slice
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int MI = WM / 32, NI = WN / 32;
-  constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   constexpr int STAGE = A_BYTES + B_BYTES;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
   static_assert(NS >= 2, "stages");
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
   __shared__ float2 red[MODE == EPI_FWD && WAVES_M > 1 ? (WAVES_M - 1) * BN : 1];
 
-  using LA = RowLoads<BM, NW, RB>;
-  using LB = RowLoads<BN, NW, RB>;
-  constexpr int LOADS = LA::Q + LB::Q;  // VMEM instructions per slice per wave
+  using SA = Stager<E, BM, NW, AKM>;
+  using SB = Stager<E, BN, NW, BKM>;
+  constexpr int LOADS = SA::Q + SB::Q;  // VMEM instructions per slice per wave
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -338,29 +463,33 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
   if (L >= end) return;
 
   // per-tile load state
-  LA la;
-  LB lb;
+  SA sa;
+  SB sb;
   const char* Ab = nullptr;
   const char* Bb = nullptr;
   int64_t klen = 0;
   int nk = 0;
   auto setup = [&](const TileGeom& t) {
-    la.template init<EPC>(t.m0, t.m_load, g.lda, wave, lane, ES);
-    lb.template init<EPC>(t.n0, t.n_end, g.ldb, wave, lane, ES);
-    Ab = static_cast<const char*>(g.A) + (t.m0 * g.lda + t.k_beg) * ES;
-    Bb = static_cast<const char*>(g.B) + (t.n0 * g.ldb + t.k_beg) * ES;
+    sa.template init<MI>(t.m0, t.m_load, g.lda, wave, lane, wm * WM);
+    sb.template init<NI>(t.n0, t.n_end, g.ldb, wave, lane, wn * WN);
+    if constexpr (AKM)
+      Ab = static_cast<const char*>(g.A) + (t.k_beg * g.lda + t.m0) * ES;
+    else
+      Ab = static_cast<const char*>(g.A) + (t.m0 * g.lda + t.k_beg) * ES;
+    if constexpr (BKM)
+      Bb = static_cast<const char*>(g.B) + (t.k_beg * g.ldb + t.n0) * ES;
+    else
+      Bb = static_cast<const char*>(g.B) + (t.n0 * g.ldb + t.k_beg) * ES;
     klen = t.k_end - t.k_beg;
     nk = t.active() ? static_cast<int>((klen + BK - 1) / BK) : 0;
   };
   const uint32_t smem_lds = lds_addr(smem);
   auto issue = [&](int kt) {
     const uint32_t st = smem_lds + (kt % NS) * STAGE;
-    const int64_t kleft = klen - static_cast<int64_t>(kt) * BK;
-    const bool full = kleft >= BK;
-    const char* a = Ab + static_cast<int64_t>(kt) * BK * ES;
-    const char* b = Bb + static_cast<int64_t>(kt) * BK * ES;
-    la.issue(st, a, kleft, full, wave, ES);
-    lb.issue(st + A_BYTES, b, kleft, full, wave, ES);
+    const int64_t kofs = static_cast<int64_t>(kt) * BK;
+    const int64_t kleft = klen - kofs;
+    sa.issue(st, Ab + kofs * (AKM ? g.lda : 1) * ES, kleft, wave);
+    sb.issue(st + A_BYTES, Bb + kofs * (BKM ? g.ldb : 1) * ES, kleft, wave);
   };
   auto prologue = [&]() {
 #pragma unroll
@@ -369,11 +498,12 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
     asm volatile("" ::"r"(smem) : "memory");
   };
 
-
-  // fragment rows of this lane inside a stage; the chunk depends on the sub-step
-  const int rowA = (wm * WM + l32) * RB;
-  const int rowB = A_BYTES + (wn * WN + l32) * RB;
-  const int swz = lds_swz<RB>(l32);
+  // loss scaling of G, read once before any loads are in flight
+  float scale = 0.0f;
+  if constexpr (MODE == EPI_GRAD) {
+    const float gl = e.grad.grad_loss[0];
+    scale = (e.grad.reduction == 0) ? gl / static_cast<float>(max(e.grad.n_valid[0], 1)) : gl;
+  }
 
   TileGeom cur = decode_tile<BM, BN>(g, L);
   setup(cur);
@@ -413,8 +543,8 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
 
     // One K slice: wait for it; read the first sub-step's fragments; queue
     // slice kt + NS - 1 (unless past the end) while those reads are in
-    // flight; then run the slice's MFMAs interleaved one-for-one with the next
-    // sub-step's fragment reads.
+    // flight; then run the slice's MFMAs interleaved with the next sub-step's
+    // fragment reads.
     auto kstep = [&](int kt, auto issue_next) {
       constexpr bool ISSUE = decltype(issue_next)::value;
       if constexpr (ISSUE)
@@ -425,15 +555,10 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       asm volatile("" ::"r"(smem) : "memory");
       const char* st = smem + (kt % NS) * STAGE;
       u32x4 fa[2][MI], fb[2][NI];
-      {
-        const int ch = (half ^ swz) * 16;
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
-          fa[0][i] = *reinterpret_cast<const u32x4*>(st + rowA + i * 32 * RB + ch);
+      for (int i = 0; i < MI; ++i) fa[0][i] = sa.frag(st, i, 0, lane);
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
-          fb[0][j] = *reinterpret_cast<const u32x4*>(st + rowB + j * 32 * RB + ch);
-      }
+      for (int j = 0; j < NI; ++j) fb[0][j] = sb.frag(st + A_BYTES, j, 0, lane);
       asm volatile("" ::"r"(smem) : "memory");
       if constexpr (ISSUE) issue(kt + NS - 1);
       if (kt == 0) load_epi();
@@ -442,29 +567,27 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       for (int s = 0; s < SS; ++s) {
         const int cb = s & 1;
         if (s + 1 < SS) {  // next sub-step's fragments, in flight during this one's MFMAs
-          const int chn = ((2 * (s + 1) + half) ^ swz) * 16;
 #pragma unroll
-          for (int i = 0; i < MI; ++i)
-            fa[cb ^ 1][i] = *reinterpret_cast<const u32x4*>(st + rowA + i * 32 * RB + chn);
+          for (int i = 0; i < MI; ++i) fa[cb ^ 1][i] = sa.frag(st, i, s + 1, lane);
 #pragma unroll
-          for (int j = 0; j < NI; ++j)
-            fb[cb ^ 1][j] = *reinterpret_cast<const u32x4*>(st + rowB + j * 32 * RB + chn);
+          for (int j = 0; j < NI; ++j) fb[cb ^ 1][j] = sb.frag(st + A_BYTES, j, s + 1, lane);
         }
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int j = 0; j < NI; ++j) mma_chunk<E>(acc[i][j], fa[cb][i], fb[cb][j]);
       }
-      constexpr int NF = MI + NI;                              // fragment reads per sub-step
+      // spread each sub-step's LDS reads evenly over its MFMAs
+      constexpr int NF = MI * SA::kReads + NI * SB::kReads;    // LDS reads per sub-step
       constexpr int NMF = MI * NI * (sizeof(E) == 2 ? 1 : 4);  // MFMAs per sub-step
 #pragma unroll
       for (int s = 0; s + 1 < SS; ++s) {
-#pragma unroll
-        for (int k = 0; k < NF; ++k) {
+        static_for<0, NMF>([&](auto kk) {
+          constexpr int k = decltype(kk)::value;
+          constexpr int nd = (NF * (k + 1)) / NMF - (NF * k) / NMF;
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, NMF - NF, 0);
+          if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x100, nd, 0);
+        });
       }
       __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
     };
@@ -576,9 +699,6 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       }
     } else if constexpr (MODE == EPI_GRAD) {
       const GradArgs& gr = e.grad;
-      const float scale = (gr.reduction == 0)
-                              ? gr.grad_loss[0] / static_cast<float>(max(gr.n_valid[0], 1))
-                              : gr.grad_loss[0];
       // Element (i, 4q + c) of this lane sits at row vb + i*32 + 8*q + c of
       // the GEMM (vocabulary row v_off + that of the table). Limits and the
       // target are taken relative to vb and clamped to [-1, WM], so every
@@ -590,7 +710,6 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       const int real_l = rel(min(t.m_end, gr.V_real - gr.v_off));  // rows below are real classes
       const int end_l = rel(t.m_end);                                 // rows below exist
       E* Gp = static_cast<E*>(gr.G);
-      E* GTp = static_cast<E*>(gr.GT);
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         const int64_t tt = t.n0 + wn * WN + j * 32 + l32;
@@ -600,7 +719,6 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
         const int y_l = valid ? rel(y - gr.v_off) : -1;
         const int lim_l = valid ? real_l : -1;
         const float nl = lv[j] * kLog2e;
-        const bool t_gt = tt < gr.ldGT;
         E* grow = Gp + tt * gr.ldG + vb;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -615,42 +733,26 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
               // select, never multiply, so a non-finite p of a discarded entry cannot leak
               gv[c] = (r0 + c < lim_l) ? scale * (p - oh) : 0.0f;
             }
+            if (!tin) continue;
             if constexpr (sizeof(E) == 2) {
-              uint16_t hb[4];
-#pragma unroll
-              for (int c = 0; c < 4; ++c) hb[c] = f32_to_bf16(gv[c]);
-              if (tin) {
-                if (gr.vec_store && r0 + 3 < end_l) {
-                  u32x2 pk;
-                  pk.x = static_cast<uint32_t>(hb[0]) | (static_cast<uint32_t>(hb[1]) << 16);
-                  pk.y = static_cast<uint32_t>(hb[2]) | (static_cast<uint32_t>(hb[3]) << 16);
-                  *reinterpret_cast<u32x2*>(grow + r0) = pk;
-                } else {
-#pragma unroll
-                  for (int c = 0; c < 4; ++c)
-                    if (r0 + c < end_l) grow[r0 + c] = hb[c];
-                }
-              }
-              if (t_gt) {
+              if (gr.vec_store && r0 + 3 < end_l) {
+                u32x2 pk;
+                pk.x = pack_bf16x2(gv[0], gv[1]);
+                pk.y = pack_bf16x2(gv[2], gv[3]);
+                *reinterpret_cast<u32x2*>(grow + r0) = pk;
+              } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                  if (r0 + c < end_l) GTp[(vb + r0 + c) * gr.ldGT + tt] = hb[c];
+                  if (r0 + c < end_l) grow[r0 + c] = f32_to_bf16(gv[c]);
               }
             } else {
-              if (tin) {
-                if (gr.vec_store && r0 + 3 < end_l) {
-                  f32x4 pk = {gv[0], gv[1], gv[2], gv[3]};
-                  *reinterpret_cast<f32x4*>(grow + r0) = pk;
-                } else {
-#pragma unroll
-                  for (int c = 0; c < 4; ++c)
-                    if (r0 + c < end_l) grow[r0 + c] = gv[c];
-                }
-              }
-              if (t_gt) {
+              if (gr.vec_store && r0 + 3 < end_l) {
+                f32x4 pk = {gv[0], gv[1], gv[2], gv[3]};
+                *reinterpret_cast<f32x4*>(grow + r0) = pk;
+              } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                  if (r0 + c < end_l) GTp[(vb + r0 + c) * gr.ldGT + tt] = gv[c];
+                  if (r0 + c < end_l) grow[r0 + c] = gv[c];
               }
             }
           }

@@ -103,7 +103,14 @@ vce_status vce_bwd(const void* h, const void* W, const int32_t* targets, const f
                    int32_t accumulate_dW, void* ws, size_t ws_bytes, void* stream) {
   return vce_bwd_timed(h, W, targets, lse, grad_loss, n_valid, red, T, H, V_real, V_pad,
                        num_shards, ignore_index, dt, dh, dW, accumulate_dW, ws, ws_bytes, stream,
-                       nullptr);
+                       nullptr, 0);
+}
+
+int64_t vce_bwd_event_count(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                            int32_t num_shards, vce_dtype dt) {
+  if (!dtype_ok(dt) || check_table(T, H, V_real, V_pad, num_shards) != VCE_OK) return 0;
+  const vce::BwdPlan p = vce::plan_bwd(T, H, V_real, V_pad, num_shards, esize_of(dt), nullptr);
+  return 1 + 3 * p.n_chunks;
 }
 
 vce_status vce_bwd_timed(const void* h, const void* W, const int32_t* targets, const float* lse,
@@ -111,7 +118,7 @@ vce_status vce_bwd_timed(const void* h, const void* W, const int32_t* targets, c
                          int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t num_shards,
                          int32_t ignore_index, vce_dtype dt, float* dh, float* dW,
                          int32_t accumulate_dW, void* ws, size_t ws_bytes, void* stream,
-                         void* const* events) {
+                         void* const* events, int64_t n_events) {
   if (!dtype_ok(dt) || (red != VCE_REDUCE_MEAN && red != VCE_REDUCE_SUM)) return VCE_ERR_DTYPE;
   vce_status st = check_table(T, H, V_real, V_pad, num_shards);
   if (st != VCE_OK) return st;
@@ -128,6 +135,7 @@ vce_status vce_bwd_timed(const void* h, const void* W, const int32_t* targets, c
   if (T > 0 && (!ws || ws_bytes < probe.bytes)) return VCE_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return VCE_ERR_ALIGN;
   const vce::BwdPlan p = vce::plan_bwd(T, H, V_real, V_pad, num_shards, esize_of(dt), ws);
+  if (events && n_events != 1 + 3 * p.n_chunks) return VCE_ERR_SHAPE;
   return hip_status(vce::run_ce_bwd(h, W, targets, lse, grad_loss, n_valid, red, T, H, V_real,
                                     V_pad, num_shards, dt == VCE_BF16, dh, dW, accumulate_dW ? 1 : 0,
                                     p, static_cast<hipStream_t>(stream), events));

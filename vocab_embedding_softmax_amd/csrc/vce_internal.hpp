@@ -25,13 +25,13 @@ namespace vce {
 constexpr int kTileM = VCE_TILE_M;  // GEMM tile rows (M side)
 constexpr int kTileN = VCE_TILE_N;  // GEMM tile columns (N side)
 constexpr int kOcc = VCE_OCC;       // workgroups resident per CU (waves per SIMD)
-#ifndef VCE_ROW_BYTES
-#define VCE_ROW_BYTES 128
+#ifndef VCE_CHUNK_ROWS
+#define VCE_CHUNK_ROWS 32768
 #endif
 #ifndef VCE_STAGES
 #define VCE_STAGES 2
 #endif
-constexpr int kRowBytes = VCE_ROW_BYTES;  // bytes of one operand row per K slice in LDS
+constexpr int kChunkRows = VCE_CHUNK_ROWS;  // most vocabulary rows of one backward chunk
 constexpr int kStages = VCE_STAGES;       // K slices in flight + the one being consumed
 constexpr int kWavesM = VCE_WAVES_M;  // waves per workgroup along M
 constexpr int kWavesN = VCE_WAVES_N;  // waves per workgroup along N
@@ -68,18 +68,22 @@ struct FwdPlan {
 };
 FwdPlan plan_fwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, void* ws);
 
-// Backward plan: staged G (both layouts), transposed W and h, dh partials.
+// Backward plan: the vocabulary is processed in chunks (a shard, or a piece
+// of one when shards are large); only one chunk's G = [T][chunk] is staged.
 struct BwdPlan {
-  int64_t S, tiles_per_seg, tiles_m, tiles_n, ldV, ldT, Kv;
-  int32_t dh_splits;
-  int64_t dh_k_per_split;
+  int64_t S;                 // rows per shard
+  int64_t pieces;            // chunks per shard
+  int64_t piece_rows;        // rows per chunk (the last chunk of a shard may be shorter)
+  int64_t n_chunks;          // pieces * num_shards
+  int64_t ldC;               // leading dimension of the staged G chunk
   size_t esize;
-  void* G;
-  void* GT;
-  void* WT;
-  void* hT;
-  float* dh_part;
+  void* G;                   // [T][ldC]
   size_t bytes;
+  void chunk(int64_t c, int64_t& c0, int64_t& c1) const {
+    const int64_t k = c / pieces, j = c % pieces;
+    c0 = k * S + j * piece_rows;
+    c1 = (k + 1) * S < c0 + piece_rows ? (k + 1) * S : c0 + piece_rows;
+  }
 };
 BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, size_t esize,
                  void* ws);
@@ -119,6 +123,8 @@ hipError_t run_ce_fwd(const void* h, const void* W, const int32_t* targets, int6
                       float* lse, float* loss, float* loss_sum, int32_t* n_valid, int32_t* n_bad,
                       float* shard_stats, const FwdPlan& p, hipStream_t s);
 
+// events (optional): 1 + 3 * p.n_chunks handles recorded before the first
+// kernel and after each chunk's G, dh contribution and dW rows
 hipError_t run_ce_bwd(const void* h, const void* W, const int32_t* targets, const float* lse,
                       const float* grad_loss, const int32_t* n_valid, int32_t reduction,
                       int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, bool bf16,
