@@ -32,7 +32,7 @@ METRIC = "fused LM-head CE fwd+bwd tokens/s (V=201088,H=3072,bf16); % MFMA peak"
 PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
 CSRC = os.path.join(ROOT, "vocab_embedding_softmax_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_grad_gemm_c4.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ce_gemms_c4.txt")
 
 
 def log(*a):
@@ -63,10 +63,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the gradient GEMM from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, each scaled by the same counter's reading
-    for a copy of known size; None when absent or taken on other kernel sources."""
+def measured_traffic(tag: str):
+    """HBM bytes per launch of one CE GEMM kernel (tag: fwd, grad, dh, dw) from
+    the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, each counter
+    scaled by its own reading for a copy of known size; None when absent or
+    taken on other kernel sources."""
     try:
         vals = {}
         with open(TRAFFIC_FILE) as f:
@@ -80,8 +81,8 @@ def measured_traffic():
         copy_bytes = float(vals["copy_bytes"])
         f_scale = copy_bytes / (float(vals["copy_fetch_kib"]) * 1024.0)
         w_scale = copy_bytes / (float(vals["copy_write_kib"]) * 1024.0)
-        return (float(vals["kernel_fetch_kib"]) * 1024.0 * f_scale +
-                float(vals["kernel_write_kib"]) * 1024.0 * w_scale)
+        return (float(vals[f"{tag}_fetch_kib"]) * 1024.0 * f_scale +
+                float(vals[f"{tag}_write_kib"]) * 1024.0 * w_scale)
     except (OSError, KeyError, ValueError):
         return None
 
@@ -208,23 +209,27 @@ def main():
     }
     log(f"[bench] {ms_step:.3f} ms/step, phases (ms) {json.dumps(phase)}")
 
-    # Algorithmic flops of each of the four CE GEMMs per step: 2*T*H*V_real. The
-    # backward GEMMs run once per vocabulary chunk; their time is summed over the
-    # chunks, so flops / time is also flops per launch / mean launch time.
+    # Each of the four CE GEMMs does 2*T*H*V_real algorithmic flops per step.
+    # The forward is one launch; each backward GEMM is one launch per
+    # vocabulary chunk (2*T*H*(real rows of the chunk) flops), timed on the
+    # stream it runs on; flops per launch / mean launch time equals the step
+    # totals' ratio below.
     flop_gemm = 2.0 * T * H * Vr
     gemms = {
-        "k_gemm_tn<bf16,EPI_FWD> (vce_fwd: logits GEMM + online max/sum-exp)": phase["vce_fwd"],
-        f"k_gemm_tn<bf16,EPI_GRAD> (logit recompute + G = scale*(softmax-onehot), "
-        f"{n_chunks} vocabulary chunks)": phase["vce_bwd.recompute_G"],
-        f"k_gemm_tn<bf16,EPI_STORE,KC,KM> (dh += G_chunk W_chunk, {n_chunks} chunks)":
-            phase["vce_bwd.dh"],
-        f"k_gemm_tn<bf16,EPI_STORE,KM,KM> (dW_chunk = G_chunk^T h, {n_chunks} chunks)":
-            phase["vce_bwd.dW"],
+        "fwd": ("k_gemm_tn<bf16,EPI_FWD> (vce_fwd: logits GEMM + online max/sum-exp, 1 launch)",
+                phase["vce_fwd"], 1),
+        "grad": (f"k_gemm_tn<bf16,EPI_GRAD> (logit recompute + G = scale*(softmax-onehot), "
+                 f"{n_chunks} launches, one per vocabulary chunk)", phase["vce_bwd.recompute_G"],
+                 n_chunks),
+        "dh": (f"k_gemm_tn<bf16,EPI_STORE,KC,KM> (dh += G_chunk W_chunk, {n_chunks} launches)",
+               phase["vce_bwd.dh"], n_chunks),
+        "dw": (f"k_gemm_tn<bf16,EPI_STORE,KM,KM> (dW_chunk = G_chunk^T h, {n_chunks} launches)",
+               phase["vce_bwd.dW"], n_chunks),
     }
-    dom = max(gemms, key=gemms.get)
-    dom_ms = gemms[dom]
+    dom_tag = max(gemms, key=lambda k: gemms[k][1])
+    dom, dom_ms, dom_launches = gemms[dom_tag]
     achieved = flop_gemm / (dom_ms * 1e-3) / 1e12
-    traffic = measured_traffic() if ("EPI_GRAD" in dom and a.workload == "c4") else None
+    traffic = measured_traffic(dom_tag) if a.workload == "c4" else None
     path_frac = 8.0 * T * H * Vr / (ms_step * 1e-3) / PEAK_BF16
     res = {
         "metric": METRIC,
@@ -248,6 +253,7 @@ def main():
         "roofline": {
             "bound": "mfma",
             "kernel": dom,
+            "launches_per_step": dom_launches,
             "achieved": achieved,
             "peak": PEAK_BF16 / 1e12,
             "unit": "TFLOP/s",

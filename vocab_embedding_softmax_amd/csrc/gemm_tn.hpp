@@ -10,14 +10,15 @@
 //
 // Workgroup: WAVES_M x WAVES_N waves over a BM x BN tile; each wave owns a
 // (BM/WAVES_M) x (BN/WAVES_N) sub-tile made of 32 x 32 MFMA blocks. K
-// advances in slices of 128 bytes per operand position (64 bf16 or 32
-// float), staged in LDS by direct global->LDS loads (global_load_lds_dwordx4),
-// NS stages deep; both layouts fill one stage with ROWS * 128 bytes.
+// advances in slices of RB bytes per operand position (RB = 64: 32 bf16 or
+// 16 float), staged in LDS by direct global->LDS loads
+// (global_load_lds_dwordx4), NS stages deep; both layouts fill one stage with
+// ROWS * RB bytes.
 //
-// K-contiguous stage: one 128-byte row per position, its eight 16-byte chunks
-// permuted by ((row >> 1) & 7) so that the 16 lanes one LDS cycle serves (16
-// consecutive rows, one chunk) cover all 64 banks. A fragment is one
-// ds_read_b128 per lane.
+// K-contiguous stage: one RB-byte row per position, its 16-byte chunks
+// permuted by ((row >> 1) & 7) (RB = 128) or ((row >> 2) & 3) (RB = 64) so
+// that the 16 lanes one LDS cycle serves (16 consecutive rows, one chunk)
+// cover all 64 banks. A fragment is one ds_read_b128 per lane.
 //
 // K-major stage: one row per K index holding the tile's positions. bf16
 // fragments come from two ds_read_b64_tr_b16 per lane: within each group of
@@ -196,24 +197,28 @@ __device__ __forceinline__ void dma16(const void* p, uint32_t lds) {
 //   init<NB>(p0, p_end, ld, wave, lane, wbase)
 //        tile positions [p0, p_end) are valid; the wave's fragments cover NB
 //        blocks of 32 positions from tile position wbase
-//   issue(lds, base, kleft, wave)   base = element (p0, k); kleft = K left
+//   fast(kleft)                     all rows valid and a whole slice left
+//   issue_q(q, lds, base, kleft, wave, fast)
+//                                   load q (of Q) of one slice; base =
+//                                   element (p0, k); kleft = K left
+//   issue(lds, base, kleft, wave)   all Q loads of one slice
 //   frag(stage, block, s, lane)     fragment of one block at sub-step s
 //                                   (16 bf16 / 8 float of K)
 //   kReads                          LDS read instructions per fragment
 
-// K-contiguous operand
-template <typename E, int ROWS, int NW>
+// K-contiguous operand; RB = bytes of one position's K slice (128 or 64)
+template <typename E, int ROWS, int NW, int RB>
 struct StageKC {
   static constexpr int ES = sizeof(E);
   static constexpr int EPC = Elem<E>::kChunk;
-  static constexpr int BK = Elem<E>::kSlice;
-  static constexpr int RB = 128;          // bytes per LDS row
+  static constexpr int BK = RB / ES;      // K elements per slice
+  static_assert(RB == 128 || RB == 64, "slice bytes");
   static constexpr int CPR = RB / 16;     // chunks per row
   static constexpr int RPI = 64 / CPR;    // rows per wave-wide load
   static constexpr int Q = ROWS / (RPI * NW);
   static constexpr int kReads = 1;
   static_assert(ROWS % (RPI * NW) == 0, "load split");
-  static_assert(NW % 2 == 0, "chunk choice must not depend on the load index");
+  static_assert(RB == 64 || NW % 2 == 0, "chunk choice must not depend on the load index");
   uint32_t off0;     // this lane's byte offset for load 0 (chunk included)
   int32_t lrow;      // this lane's tile row for load 0
   int32_t kch;       // element offset of this lane's chunk inside the K slice
@@ -221,7 +226,11 @@ struct StageKC {
   int64_t rstride;   // bytes between consecutive rows
   uint32_t frag0;    // this lane's LDS row offset for block 0
 
-  __device__ __forceinline__ static int swz(int row) { return (row >> 1) & 7; }
+  // 16 lanes of one LDS cycle read 16 consecutive rows at one logical chunk;
+  // the permutation spreads them over all 64 banks
+  __device__ __forceinline__ static int swz(int row) {
+    return RB == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+  }
 
   template <int NB>
   __device__ __forceinline__ void init(int64_t p0, int64_t p_end, int64_t ld, int wave, int lane,
@@ -235,48 +244,62 @@ struct StageKC {
     frag0 = static_cast<uint32_t>((wbase + (lane & 31)) * RB);
   }
 
-  __device__ __forceinline__ void issue(uint32_t lds, const char* base, int64_t kleft,
-                                        int wave) const {
-    if (kleft >= BK && nrows == ROWS) {
-      const int64_t qstride = static_cast<int64_t>(NW) * RPI * rstride;
-#pragma unroll
-      for (int q = 0; q < Q; ++q) dma16(base + q * qstride, off0, lds + (q * NW + wave) * RPI * RB);
+  __device__ __forceinline__ bool fast(int64_t kleft) const { return kleft >= BK && nrows == ROWS; }
+
+  __device__ __forceinline__ void issue_q(int q, uint32_t lds, const char* base, int64_t kleft,
+                                          int wave, bool is_fast) const {
+    const uint32_t dst = lds + (q * NW + wave) * RPI * RB;
+    if (is_fast) {
+      dma16(base + q * (static_cast<int64_t>(NW) * RPI * rstride), off0, dst);
     } else {
-#pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        int r = lrow + q * NW * RPI;
-        if (r >= nrows) r = nrows - 1;  // the result of this row is discarded
-        const void* p = base + r * rstride + kch * ES;
-        if (kch >= kleft) p = g_zero_chunk;
-        dma16(p, lds + (q * NW + wave) * RPI * RB);
-      }
+      // recomputed at every use (the empty asm hides that lr is invariant):
+      // kept live across the K loop, these addresses would cost registers
+      int lr = lrow;
+      asm volatile("" : "+v"(lr));
+      int r = lr + q * NW * RPI;
+      if (r >= nrows) r = nrows - 1;  // the result of this row is discarded
+      const void* p = base + static_cast<uint32_t>(r * static_cast<int32_t>(rstride) + kch * ES);
+      if (kch >= kleft) p = g_zero_chunk;
+      dma16(p, dst);
     }
   }
 
+  __device__ __forceinline__ void issue(uint32_t lds, const char* base, int64_t kleft,
+                                        int wave) const {
+    const bool f = fast(kleft);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) issue_q(q, lds, base, kleft, wave, f);
+  }
+
   // fragment: row (wbase + block*32 + lane%32), logical chunk 2s + lane/32
+  // (the rows of a block start at a multiple of 32, so swz depends on lane%32)
   __device__ __forceinline__ u32x4 frag(const char* st, int block, int s, int lane) const {
     const int ch = ((2 * s + (lane >> 5)) ^ swz(lane & 31)) * 16;
     return *reinterpret_cast<const u32x4*>(st + frag0 + block * 32 * RB + ch);
   }
 };
 
-// K-major operand
-template <typename E, int ROWS, int NW>
+// K-major operand; a slice holds RB / sizeof(E) K rows
+template <typename E, int ROWS, int NW, int RB>
 struct StageKM {
   static constexpr int ES = sizeof(E);
   static constexpr int EPC = Elem<E>::kChunk;
-  static constexpr int BK = Elem<E>::kSlice;   // K rows per slice
+  static constexpr int BK = RB / ES;           // K rows per slice
   static constexpr int RBT = ROWS * ES;        // bytes per K row of the tile
   static constexpr int RPL = 1024 / RBT;       // K rows per wave-wide load
   static constexpr int CPR = RBT / 16;         // chunks per K row
   static constexpr int Q = BK / (RPL * NW);
   static constexpr int kReads = ES == 2 ? 2 : 4;
   static_assert(1024 % RBT == 0 && RBT >= 256, "row size");
-  static_assert(BK % (RPL * NW) == 0, "load split");
-  static_assert((RPL * NW) % (ES == 2 ? 4 : 8) == 0, "chunk choice must not depend on q");
+  static_assert(BK % (RPL * NW) == 0 && Q >= 1, "load split");
+  // the chunk permutation repeats every 4 (bf16) / 8 (float) rows: when the
+  // rows of consecutive loads step by a multiple of that, a lane's chunk is
+  // the same for every load
+  static constexpr bool kQIndep = (RPL * NW) % (ES == 2 ? 4 : 8) == 0;
   uint32_t off0;     // this lane's byte offset for load 0 (chunk included)
   int32_t lk;        // this lane's K row (within the slice) for load 0
-  int32_t lch;       // this lane's logical chunk (of positions) in the row
+  int32_t pch;       // this lane's chunk slot in its LDS row
+  int32_t lch;       // the logical chunk (of positions) it brings for load 0
   int32_t last_ch;   // last chunk holding a valid position
   bool all_cols;
   int64_t rstride;   // bytes between consecutive K rows in global memory
@@ -292,7 +315,8 @@ struct StageKM {
                                        int wbase) {
     static_assert(NB <= 4, "fragment offsets");
     lk = wave * RPL + lane / CPR;
-    lch = (lane % CPR) ^ swz(lk);
+    pch = lane % CPR;
+    lch = pch ^ swz(lk);
     rstride = ld * ES;
     const int64_t npos = min(p_end - p0, static_cast<int64_t>(ROWS));
     all_cols = npos == ROWS;
@@ -319,22 +343,32 @@ struct StageKM {
     }
   }
 
+  __device__ __forceinline__ bool fast(int64_t kleft) const {
+    return kQIndep && kleft >= BK && all_cols;
+  }
+
+  __device__ __forceinline__ void issue_q(int q, uint32_t lds, const char* base, int64_t kleft,
+                                          int wave, bool is_fast) const {
+    const uint32_t dst = lds + (q * NW + wave) * 1024;
+    if (is_fast) {
+      dma16(base + q * (static_cast<int64_t>(NW) * RPL * rstride), off0, dst);
+    } else {
+      int l0 = lk;  // recomputed at every use, as in StageKC
+      asm volatile("" : "+v"(l0));
+      const int k = l0 + q * NW * RPL;
+      const int ch = kQIndep ? lch : (pch ^ swz(k));
+      const int c = min(ch, last_ch);  // positions past the valid range: discarded
+      const void* p = base + static_cast<uint32_t>(k * static_cast<int32_t>(rstride) + c * 16);
+      if (k >= kleft) p = g_zero_chunk;
+      dma16(p, dst);
+    }
+  }
+
   __device__ __forceinline__ void issue(uint32_t lds, const char* base, int64_t kleft,
                                         int wave) const {
-    if (kleft >= BK && all_cols) {
-      const int64_t qstride = static_cast<int64_t>(NW) * RPL * rstride;
+    const bool f = fast(kleft);
 #pragma unroll
-      for (int q = 0; q < Q; ++q) dma16(base + q * qstride, off0, lds + (q * NW + wave) * 1024);
-    } else {
-#pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        const int k = lk + q * NW * RPL;
-        const int c = min(lch, last_ch);  // positions past the valid range: discarded
-        const void* p = base + k * rstride + c * 16;
-        if (k >= kleft) p = g_zero_chunk;
-        dma16(p, lds + (q * NW + wave) * 1024);
-      }
-    }
+    for (int q = 0; q < Q; ++q) issue_q(q, lds, base, kleft, wave, f);
   }
 
   __device__ __forceinline__ u32x4 frag(const char* st, int block, int s, int lane) const {
@@ -360,8 +394,9 @@ struct StageKM {
   }
 };
 
-template <typename E, int ROWS, int NW, bool KMAJ>
-using Stager = typename std::conditional<KMAJ, StageKM<E, ROWS, NW>, StageKC<E, ROWS, NW>>::type;
+template <typename E, int ROWS, int NW, int RB, bool KMAJ>
+using Stager =
+    typename std::conditional<KMAJ, StageKM<E, ROWS, NW, RB>, StageKC<E, ROWS, NW, RB>>::type;
 
 // Compile-time loop: f(integral_constant<int, I>) for I in [I0, N)
 template <int I0, int N, typename F>
@@ -422,28 +457,34 @@ __device__ __forceinline__ TileGeom decode_tile(const GemmShape& g, uint32_t L) 
 // epilogue runs, the first K slices of the workgroup's next tile are already
 // on their way into LDS.
 template <typename E, int MODE, bool AKM, bool BKM, int BM, int BN, int WAVES_M, int WAVES_N,
-          int NS, int OCC>
+          int RB, int NS, int OCC>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N,
                                                       64 * WAVES_M * WAVES_N),
                           amdgpu_waves_per_eu(OCC, OCC)))
 void k_gemm_tn(GemmShape g, EpiArgs e) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int ES = sizeof(E);
-  constexpr int BK = Elem<E>::kSlice;      // K elements per slice
-  constexpr int SS = 4;                    // sub-steps per slice
+  constexpr int BK = RB / ES;              // K elements per slice
+  constexpr int SS = RB / 32;              // sub-steps per slice (16 bf16 / 8 float of K each)
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int MI = WM / 32, NI = WN / 32;
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
   constexpr int STAGE = A_BYTES + B_BYTES;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
-  static_assert(NS >= 2, "stages");
+  static_assert(NS >= 2 && SS >= 2 && SS % 2 == 0, "stages");
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
   __shared__ float2 red[MODE == EPI_FWD && WAVES_M > 1 ? (WAVES_M - 1) * BN : 1];
 
-  using SA = Stager<E, BM, NW, AKM>;
-  using SB = Stager<E, BN, NW, BKM>;
+  using SA = Stager<E, BM, NW, RB, AKM>;
+  using SB = Stager<E, BN, NW, RB, BKM>;
   constexpr int LOADS = SA::Q + SB::Q;  // VMEM instructions per slice per wave
-
+  if constexpr (MI * NI * 16 > 128) {
+    // Accumulators above half the register file: naming an accumulation
+    // register keeps the compiler from assuming the kernel uses none, so it
+    // selects the MFMA forms that accumulate in AGPRs instead of copying
+    // between the two register files.
+    asm volatile("" ::: "a0");
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
@@ -483,6 +524,7 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
     klen = t.k_end - t.k_beg;
     nk = t.active() ? static_cast<int>((klen + BK - 1) / BK) : 0;
   };
+
   const uint32_t smem_lds = lds_addr(smem);
   auto issue = [&](int kt) {
     const uint32_t st = smem_lds + (kt % NS) * STAGE;
@@ -532,7 +574,28 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
     }
   };
 
+  // Fragment reads of one sub-step and the MFMAs of one sub-step.
+  auto read_frags = [&](const char* st, int sub, u32x4 (&fa)[MI], u32x4 (&fb)[NI]) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) fa[i] = sa.frag(st, i, sub, lane);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) fb[j] = sb.frag(st + A_BYTES, j, sub, lane);
+  };
+  constexpr int NF = MI * SA::kReads + NI * SB::kReads;    // LDS reads per sub-step
+  constexpr int NMF = MI * NI * (sizeof(E) == 2 ? 1 : 4);  // MFMAs per sub-step
+  // scheduling hint: the next sub-step's NF reads spread evenly over this
+  // sub-step's NMF MFMAs
+  auto interleave = [&]() {
+    static_for<0, NMF>([&](auto kk) {
+      constexpr int k = decltype(kk)::value;
+      constexpr int nd = (NF * (k + 1)) / NMF - (NF * k) / NMF;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x100, nd, 0);
+    });
+  };
+
   f32x16 acc[MI][NI];
+  u32x4 fa[2][MI], fb[2][NI];
   while (true) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -540,62 +603,111 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       for (int j = 0; j < NI; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    auto mfmas = [&](const u32x4 (&a)[MI], const u32x4 (&b)[NI]) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) mma_chunk<E>(acc[i][j], a[i], b[j]);
+    };
 
-    // One K slice: wait for it; read the first sub-step's fragments; queue
-    // slice kt + NS - 1 (unless past the end) while those reads are in
-    // flight; then run the slice's MFMAs interleaved with the next sub-step's
-    // fragment reads.
-    auto kstep = [&](int kt, auto issue_next) {
+    // Software pipeline over K slices. The prologue has queued slices
+    // 0 .. NS-2. Slice kt+1's barrier sits before slice kt's last sub-step,
+    // whose fragments are already in registers: its MFMAs cover the barrier
+    // and the reads of slice kt+1's first fragments. Right after that barrier
+    // every wave is done reading slice kt, so slice kt+NS is queued into its
+    // stage; NS-1 slices are then in flight while one is consumed.
+    //   WAIT_ALL: wait for every load (near the end, fewer slices are younger)
+    //   ISSUE:    queue slice kt + NS
+    //   LAST:     the tile's last slice (no barrier, nothing more to read)
+    auto kstep = [&](int kt, auto wait_all, auto issue_next, auto last) {
+      constexpr bool WAIT_ALL = decltype(wait_all)::value;
       constexpr bool ISSUE = decltype(issue_next)::value;
-      if constexpr (ISSUE)
-        wait_vmcnt<(NS - 2) * LOADS>();
-      else
-        wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();  // every wave's part of slice kt is in; slice kt-1 is free
-      asm volatile("" ::"r"(smem) : "memory");
+      constexpr bool LAST = decltype(last)::value;
       const char* st = smem + (kt % NS) * STAGE;
-      u32x4 fa[2][MI], fb[2][NI];
 #pragma unroll
-      for (int i = 0; i < MI; ++i) fa[0][i] = sa.frag(st, i, 0, lane);
-#pragma unroll
-      for (int j = 0; j < NI; ++j) fb[0][j] = sb.frag(st + A_BYTES, j, 0, lane);
-      asm volatile("" ::"r"(smem) : "memory");
-      if constexpr (ISSUE) issue(kt + NS - 1);
-      if (kt == 0) load_epi();
-      asm volatile("" ::"r"(smem) : "memory");
-#pragma unroll
-      for (int s = 0; s < SS; ++s) {
-        const int cb = s & 1;
-        if (s + 1 < SS) {  // next sub-step's fragments, in flight during this one's MFMAs
-#pragma unroll
-          for (int i = 0; i < MI; ++i) fa[cb ^ 1][i] = sa.frag(st, i, s + 1, lane);
-#pragma unroll
-          for (int j = 0; j < NI; ++j) fb[cb ^ 1][j] = sb.frag(st + A_BYTES, j, s + 1, lane);
+      for (int sub = 0; sub + 1 < SS; ++sub) {
+        read_frags(st, sub + 1, fa[(sub + 1) & 1], fb[(sub + 1) & 1]);
+        mfmas(fa[sub & 1], fb[sub & 1]);
+        interleave();
+      }
+      constexpr int LB = (SS - 1) & 1;
+      if constexpr (!LAST) {
+        // this wave's reads of slice kt are complete, its part of slice kt+1 is in
+        __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+        if constexpr (WAIT_ALL)
+          wait_vmcnt<0>();
+        else
+          wait_vmcnt<(NS - 2) * LOADS>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::"r"(smem) : "memory");
+        // The last sub-step's MFMAs, each followed by one load of slice kt+NS
+        // and, in turn, the next slice's first fragment reads.
+        const char* stn = smem + ((kt + 1) % NS) * STAGE;
+        const char *pa = nullptr, *pb = nullptr;
+        uint32_t stl = 0;
+        int64_t kleft = 0;
+        bool fast_a = true, fast_b = true;
+        if constexpr (ISSUE) {
+          const int kn = kt + NS;
+          const int64_t kofs = static_cast<int64_t>(kn) * BK;
+          stl = smem_lds + (kn % NS) * STAGE;
+          kleft = klen - kofs;
+          pa = Ab + kofs * (AKM ? g.lda : 1) * ES;
+          pb = Bb + kofs * (BKM ? g.ldb : 1) * ES;
+          fast_a = sa.fast(kleft);
+          fast_b = sb.fast(kleft);
         }
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NI; ++j) mma_chunk<E>(acc[i][j], fa[cb][i], fb[cb][j]);
-      }
-      // spread each sub-step's LDS reads evenly over its MFMAs
-      constexpr int NF = MI * SA::kReads + NI * SB::kReads;    // LDS reads per sub-step
-      constexpr int NMF = MI * NI * (sizeof(E) == 2 ? 1 : 4);  // MFMAs per sub-step
-#pragma unroll
-      for (int s = 0; s + 1 < SS; ++s) {
-        static_for<0, NMF>([&](auto kk) {
+        constexpr int NT = MI * NI;
+        static_for<0, (NT > LOADS ? NT : LOADS)>([&](auto kk) {
           constexpr int k = decltype(kk)::value;
-          constexpr int nd = (NF * (k + 1)) / NMF - (NF * k) / NMF;
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x100, nd, 0);
+          if constexpr (ISSUE && k < LOADS) {
+            if constexpr (k < SA::Q)
+              sa.issue_q(k, stl, pa, kleft, wave, fast_a);
+            else
+              sb.issue_q(k - SA::Q, stl + A_BYTES, pb, kleft, wave, fast_b);
+          }
+          if constexpr (k < NT) mma_chunk<E>(acc[k / NI][k % NI], fa[LB][k / NI], fb[LB][k % NI]);
+          if constexpr (k < MI)
+            fa[0][k] = sa.frag(stn, k, 0, lane);
+          else if constexpr (k < MI + NI)
+            fb[0][k - MI] = sb.frag(stn + A_BYTES, k - MI, 0, lane);
         });
+        if constexpr (NT < MI + NI) {
+#pragma unroll
+          for (int k = NT; k < MI + NI; ++k) {
+            if (k < MI)
+              fa[0][k] = sa.frag(stn, k, 0, lane);
+            else
+              fb[0][k - MI] = sb.frag(stn + A_BYTES, k - MI, 0, lane);
+          }
+        }
+      } else {
+        mfmas(fa[LB], fb[LB]);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
     };
 
     if (nk > 0) {
+      // slice 0 in; queue slice NS-1; first fragments
+      if (nk >= NS - 1)
+        wait_vmcnt<(NS - 2) * LOADS>();
+      else
+        wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::"r"(smem) : "memory");
+      if (NS - 1 < nk) issue(NS - 1);
+      load_epi();
+      asm volatile("" ::"r"(smem) : "memory");
+      read_frags(smem, 0, fa[0], fb[0]);
       int kt = 0;
-      for (; kt + NS - 1 < nk; ++kt) kstep(kt, std::true_type{});
-      for (; kt < nk; ++kt) kstep(kt, std::false_type{});
+      for (; kt + NS < nk; ++kt)
+        kstep(kt, std::false_type{}, std::true_type{}, std::false_type{});
+      if (kt + NS == nk && kt + 1 < nk) {
+        kstep(kt, std::false_type{}, std::false_type{}, std::false_type{});
+        ++kt;
+      }
+      for (; kt + 1 < nk; ++kt)
+        kstep(kt, std::true_type{}, std::false_type{}, std::false_type{});
+      kstep(kt, std::true_type{}, std::false_type{}, std::true_type{});
     } else {
       load_epi();
     }

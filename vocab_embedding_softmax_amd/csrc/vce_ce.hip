@@ -219,7 +219,7 @@ static hipError_t launch_gemm(const GemmShape& g, const EpiArgs& e, hipStream_t 
   if (tiles >= (int64_t{1} << 31)) return hipErrorInvalidValue;
   const int64_t blocks = persistent_blocks(tiles);
   hipLaunchKernelGGL(
-      (k_gemm_tn<E, MODE, AKM, BKM, kTileM, kTileN, kWavesM, kWavesN, kStages, kOcc>),
+      (k_gemm_tn<E, MODE, AKM, BKM, kTileM, kTileN, kWavesM, kWavesN, kRowBytes, kStages, kOcc>),
       dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWavesM * kWavesN), 0, s, g, e);
   return hipGetLastError();
 }

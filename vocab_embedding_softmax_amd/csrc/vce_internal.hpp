@@ -31,8 +31,12 @@ constexpr int kOcc = VCE_OCC;       // workgroups resident per CU (waves per SIM
 #ifndef VCE_STAGES
 #define VCE_STAGES 2
 #endif
+#ifndef VCE_ROW_BYTES
+#define VCE_ROW_BYTES 128
+#endif
 constexpr int kChunkRows = VCE_CHUNK_ROWS;  // most vocabulary rows of one backward chunk
 constexpr int kStages = VCE_STAGES;       // K slices in flight + the one being consumed
+constexpr int kRowBytes = VCE_ROW_BYTES;  // bytes of one operand position per K slice
 constexpr int kWavesM = VCE_WAVES_M;  // waves per workgroup along M
 constexpr int kWavesN = VCE_WAVES_N;  // waves per workgroup along N
 constexpr int kPadK = 64;     // staged operands are padded to this many K elements
