@@ -243,6 +243,43 @@ def test_scatter_add_heavy_repeats(V):
     assert np.array_equal(got.view(np.uint32), got_b.view(np.uint32))
 
 
+@pytest.mark.parametrize("T,H,Vr,label", [
+    (20000, 64, 3000, "T above the one-workgroup sort"),
+    (4000, 72, (1 << 20) + 5, "packed (ID, token) key wider than 32 bits"),
+    (16384, 40, 262143, "largest ID range of the one-workgroup sort at T = 16384"),
+    (1, 8, 10, "one token"),
+    (777, 8, 5, "five IDs, long runs over many chunks"),
+])
+def test_scatter_add_sort_paths(V, T, H, Vr, label):
+    """Both ways the library sorts tokens by ID (one workgroup, or block-local
+    sorts + scans) against the oracle, with repeats that cross chunk ends."""
+    say(f"case scatter sort path T={T} H={H} V={Vr}: {label}")
+    dev = "cuda"
+    rng = np.random.default_rng(T + H)
+    ids = rng.integers(0, Vr, T)
+    rep = rng.random(T) < 0.5
+    ids[rep] = rng.integers(0, min(Vr, 4), rep.sum())        # heavy repeats of a few IDs
+    ids[rng.random(T) < 0.03] = -1                            # out of range
+    if T > 2:
+        ids[-1] = Vr - 1                                      # the largest ID
+    ids = ids.astype(np.int32)
+    dout = rng.standard_normal((T, H)).astype(np.float32)
+    ref, count = oracle.scatter_add(ids, dout, Vr, Vr)
+    got = V.vemb_bwd(torch.from_numpy(ids).to(dev), torch.from_numpy(dout).to(dev), Vr, Vr,
+                     1).cpu().numpy()
+    assert rel_l2(got, ref) <= 1e-6
+    assert not got[count == 0].any()
+    once = count == 1
+    assert np.array_equal(got[once], ref[once].astype(np.float32))
+    base = rng.standard_normal((Vr, H)).astype(np.float32)
+    dW = torch.from_numpy(base).to(dev)
+    V.vemb_bwd(torch.from_numpy(ids).to(dev), torch.from_numpy(dout).to(dev), Vr, Vr, 1,
+               dW=dW, accumulate=True)
+    got2 = dW.cpu().numpy()
+    assert np.array_equal(got2[count == 0], base[count == 0])
+    assert rel_l2(got2 - base, ref) <= 1e-5
+
+
 # ------------------------------------------------------------------ tied step
 
 def test_tied_step_small(V):

@@ -8,12 +8,17 @@
 // rows are copied (selected), so they are bit-exact with the table.
 //
 // Backward (same page, ¶2): repeated IDs add into their one owned row.
-// Deterministic, one writer per row, no atomics:
-//   per block of 1024 tokens, an LDS sort by (ID, token) with per-block ID
-//   counts -> per-ID offsets over the blocks -> exclusive scan over IDs ->
-//   stable placement of every token -> segment sums in fixed-size chunks of
-//   the sorted list (balanced even under Zipf skew) -> a fix-up that adds the
-//   partial sums of groups that span chunks in a fixed order.
+// Deterministic, one writer per row, no atomics on the table:
+//   1. the valid tokens are sorted by (ID, token): up to 16384 tokens whose
+//      packed (ID, token) key fits 32 bits are radix-sorted in the LDS of one
+//      workgroup (one launch); larger inputs use block-local LDS sorts, per-
+//      block ID counts and scans;
+//   2. the sorted list is cut into chunks of kSegC positions; each chunk sums
+//      the dout rows of its runs (tokens of one ID) in sorted order and writes
+//      the sum of every run that lies wholly inside it into its row of dW;
+//      a run cut by a chunk end leaves a partial sum instead;
+//   3. the chunk where such an ID's run ends adds the ID's partial sums in
+//      chunk order and writes the row.
 #include "vce_device.hpp"
 #include "vce_internal.hpp"
 
@@ -22,9 +27,12 @@ namespace vce {
 constexpr int kScanThreads = 256;
 constexpr int kScanPerThread = 16;
 constexpr int kScanBlock = kScanThreads * kScanPerThread;  // 4096 values per block
-constexpr int kSegChunk = 16;                              // sorted positions per chunk
-constexpr int kSegBatch = 16;                              // rows loaded together
+constexpr int kSegC = 16;                                  // sorted positions per chunk
+constexpr int kSegBatch = 16;                              // dout rows in flight per lane
 constexpr int kSegCols = 256;                              // dW columns per wave (64 lanes x 4)
+constexpr int kPlanThreads = 1024;                         // the one-workgroup sort
+constexpr int kPlanMaxT = 16384;                           // tokens it holds in LDS
+constexpr int kPlanDigit = 6;                              // ID bits per radix pass
 constexpr int kSortBlock = 1024;                           // tokens per local sort
 constexpr int kSortThreads = 512;
 
@@ -32,23 +40,43 @@ constexpr int kSortThreads = 512;
 
 int64_t scan_blocks(int64_t n) { return cdiv(n < 1 ? 1 : n, kScanBlock); }
 
+static int32_t bit_width(int64_t x) {
+  int32_t b = 0;
+  while (x > 0) {
+    ++b;
+    x >>= 1;
+  }
+  return b;
+}
+
 EmbBwdPlan plan_emb_bwd(int64_t T, int64_t H, int64_t V_real, void* ws) {
   EmbBwdPlan p{};
   const int64_t Tp = T < 1 ? 1 : T;
+  p.tbits = bit_width(Tp - 1);
+  p.vbits = bit_width(V_real);
+  // IDs < V_real < 2^vbits never have all ID bits set, which the sort
+  // reserves for tokens without a valid ID
+  p.one_wg = Tp <= kPlanMaxT && p.tbits + p.vbits <= 32;
   p.nblocks = cdiv(Tp, kSortBlock);
-  p.nchunks = cdiv(Tp, kSegChunk);
+  p.nchunks = cdiv(Tp, kSegC);
   p.nslices = cdiv(H, kSegCols);
   p.scan_blocks = scan_blocks(V_real);
   Carve c(ws);
-  p.bcnt = c.take<int32_t>(static_cast<size_t>(p.nblocks * V_real));
-  p.counts = c.take<int32_t>(static_cast<size_t>(V_real));
-  p.offs = c.take<int32_t>(static_cast<size_t>(V_real + 1));
-  p.lkey = c.take<uint64_t>(static_cast<size_t>(p.nblocks * kSortBlock));
-  p.lrank = c.take<int32_t>(static_cast<size_t>(p.nblocks * kSortBlock));
+  if (!p.one_wg) {
+    p.bcnt = c.take<int32_t>(static_cast<size_t>(p.nblocks * V_real));
+    p.counts = c.take<int32_t>(static_cast<size_t>(V_real));
+    p.offs = c.take<int32_t>(static_cast<size_t>(V_real + 1));
+    p.lkey = c.take<uint64_t>(static_cast<size_t>(p.nblocks * kSortBlock));
+    p.lrank = c.take<int32_t>(static_cast<size_t>(p.nblocks * kSortBlock));
+    p.scan_tmp = c.take<int32_t>(static_cast<size_t>(p.scan_blocks + 1));
+  } else {
+    p.n_sorted = c.take<int32_t>(1);
+  }
   p.sorted = c.take<int32_t>(static_cast<size_t>(Tp));
   p.skey = c.take<int32_t>(static_cast<size_t>(Tp));
-  p.scan_tmp = c.take<int32_t>(static_cast<size_t>(p.scan_blocks + 1));
+  p.chunk_start = c.take<int32_t>(static_cast<size_t>(p.nchunks));
   p.partial = c.take<float>(static_cast<size_t>(p.nchunks * 2 * H));
+  if (p.offs) p.n_sorted = p.offs + V_real;
   p.bytes = c.used;
   return p;
 }
@@ -69,40 +97,65 @@ CandPlan plan_cand(int64_t T, int64_t V, void* ws) {
 
 // ------------------------------------------------------------------ lookup
 
-// One wave per output row, in 16-byte pieces: every load of the row is in
-// flight before the first store. row_bytes is a multiple of 16.
+// kRowsPerWave output rows per wave, in 16-byte pieces: every load of the
+// wave's rows is in flight before the first store. row_bytes is a multiple
+// of 16. Workgroup 0 also counts the IDs outside [0, V_real) over all tokens
+// and writes the count (a plain store: no counter to clear beforehand).
+constexpr int kRowsPerWave = 1;
 __global__ __launch_bounds__(256) void k_vemb_fwd(const int32_t* __restrict__ ids,
                                                   const char* __restrict__ W, int64_t T,
                                                   int64_t row_bytes, int64_t V_real, int64_t S,
                                                   char* __restrict__ out, int32_t* n_bad) {
-  constexpr int U = 8;  // pieces per lane held at once
+  constexpr int U = 8;  // pieces per lane and row held at once
+  constexpr int RW = kRowsPerWave;
   const int lane = threadIdx.x & 63;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const int64_t id = ids[t];
+  if (blockIdx.x == 0 && n_bad) {
+    __shared__ int32_t cnt[4];
+    int32_t bad = 0;
+    for (int64_t t = threadIdx.x; t < T; t += 256) {
+      const int64_t id = ids[t];
+      bad += (id < 0 || id >= V_real) ? 1 : 0;
+    }
+    for (int o = 32; o > 0; o >>= 1) bad += __shfl_xor(bad, o);
+    if (lane == 0) cnt[threadIdx.x >> 6] = bad;
+    __syncthreads();
+    if (threadIdx.x == 0) *n_bad = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+  }
+  const int64_t t0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * RW;
+  if (t0 >= T) return;
   const int64_t nvec = row_bytes >> 4;
-  u32x4* dst = reinterpret_cast<u32x4*>(out + t * row_bytes);
-  // owner test, then the local index within the owner's slice
-  const bool owned = (id >= 0) && (id < V_real);
-  if (!owned && lane == 0 && n_bad) atomicAdd(n_bad, 1);
-  const u32x4* src = nullptr;
-  if (owned) {
-    const int64_t k = id / S;
-    const int64_t local = id - k * S;
-    src = reinterpret_cast<const u32x4*>(W + (k * S + local) * row_bytes);
+  const u32x4* src[RW];
+  u32x4* dst[RW];
+  bool owned[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int64_t t = min(t0 + r, T - 1);
+    const int64_t id = ids[t];
+    // owner test, then the local index within the owner's slice
+    owned[r] = (t0 + r < T) && (id >= 0) && (id < V_real);
+    const int64_t k = owned[r] ? id / S : 0;
+    const int64_t local = owned[r] ? id - k * S : 0;
+    src[r] = reinterpret_cast<const u32x4*>(W + (k * S + local) * row_bytes);
+    dst[r] = reinterpret_cast<u32x4*>(out + t * row_bytes);
   }
   for (int64_t c0 = 0; c0 < nvec; c0 += 64 * U) {
-    u32x4 v[U];
+    u32x4 v[RW][U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = c0 + lane + 64 * u;
-      v[u] = (owned && c < nvec) ? src[c] : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int r = 0; r < RW; ++r)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = c0 + lane + 64 * u;
-      if (c < nvec) __builtin_nontemporal_store(v[u], dst + c);
-    }
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + lane + 64 * u;
+        v[r][u] = (owned[r] && c < nvec) ? src[r][c] : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + lane + 64 * u;
+        if (t0 + r < T && c < nvec) {
+          __builtin_nontemporal_store(v[r][u], dst[r] + c);
+        }
+      }
   }
 }
 
@@ -334,122 +387,309 @@ __device__ __forceinline__ f32x4 load_row4<uint16_t>(const uint16_t* row, int64_
   return r;
 }
 
-// One wave per (chunk of kSegChunk sorted positions, 256-column slice).
-// Runs of one ID that lie wholly in the chunk are added into dW here; runs
-// that continue into a neighbouring chunk leave a partial sum: slot 0 for
-// the run that began in an earlier chunk, slot 1 for the run that begins
-// here and continues. Rows are summed in sorted (= increasing token) order.
+// ---------------------------------------------------------- one-workgroup sort
+
+// Bits [0, 64) of a wave-wide mask: lanes whose value v equals this lane's
+// (kPlanDigit-bit digits compared bit by bit through ballots).
+__device__ __forceinline__ uint64_t match_digit(uint32_t d) {
+  uint64_t eq = ~0ull;
+#pragma unroll
+  for (int b = 0; b < kPlanDigit; ++b) {
+    // x: all ones where this lane's bit b is set; lanes that agree with it
+    // on bit b are the set bits of ~(ballot ^ x)
+    const uint32_t x32 = 0u - ((d >> b) & 1u);
+    const uint64_t x = (static_cast<uint64_t>(x32) << 32) | x32;
+    const uint64_t m = __ballot(x32 != 0u);
+    eq &= ~(m ^ x);
+  }
+  return eq;
+}
+
+// Sorts the tokens of one call by (ID, token) in the LDS of one workgroup.
+// Token t with a valid ID gets the key (ID << tbits) | t; the others get
+// all bits set and sort last. A least-significant-digit radix sort over the
+// ID bits keeps equal IDs in token order. Each pass: every wave ranks its
+// contiguous span of positions, 64 at a time, among equal digits (ballot
+// match + a per-wave running count per digit); one block-wide scan over
+// (digit, wave) counts gives every key its place.
+// Writes sorted tokens and IDs for the n valid tokens, n, and for every
+// chunk of kSegC sorted positions the first position of the ID found at the
+// chunk's first position.
+__global__ __launch_bounds__(kPlanThreads) void k_emb_plan(
+    const int32_t* __restrict__ ids, int64_t T, int64_t V_real, int32_t tbits, int32_t vbits,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ skey, int32_t* __restrict__ n_sorted,
+    int32_t* __restrict__ chunk_start) {
+  constexpr int NW = kPlanThreads / 64;
+  constexpr int ND = 1 << kPlanDigit;
+  constexpr int MAXR = kPlanMaxT / kPlanThreads;  // rounds of 64 positions per wave
+  static_assert(NW * ND == kPlanThreads, "one thread per (wave, digit) count");
+  __shared__ uint32_t kb[2][kPlanMaxT];
+  __shared__ uint32_t wrun[NW][ND];
+  __shared__ uint32_t wtot[NW];
+  __shared__ int32_t s_n;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int R = static_cast<int>((T + kPlanThreads - 1) / kPlanThreads);  // 1..MAXR
+  const int span = R * 64;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  if (tid == 0) s_n = 0;
+  __syncthreads();
+
+  // all loads of the IDs in flight at once (clamped indices, results selected)
+  int nv = 0;
+  int32_t idv[MAXR];
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r) {
+    const int p = w * span + r * 64 + lane;
+    idv[r] = ids[min(p, static_cast<int>(T) - 1)];
+  }
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r) {
+    const int p = w * span + r * 64 + lane;
+    const int64_t id = idv[r];
+    uint32_t key = ~0u;
+    if (r < R && p < T && id >= 0 && id < V_real) {
+      key = (static_cast<uint32_t>(id) << tbits) | static_cast<uint32_t>(p);
+      ++nv;
+    }
+    if (r < R) kb[0][p] = key;
+  }
+  for (int o = 32; o > 0; o >>= 1) nv += __shfl_xor(nv, o);
+  if (lane == 0) atomicAdd(&s_n, nv);
+
+  int src = 0;
+  const int npass = (vbits + kPlanDigit - 1) / kPlanDigit;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int shift = tbits + kPlanDigit * pass;
+    wrun[w][lane] = 0u;  // this wave's counters; only this wave touches them until the barrier
+    uint32_t keys[MAXR];
+    uint32_t rank[MAXR];
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+      if (r < R) {
+        const uint32_t key = kb[src][w * span + r * 64 + lane];
+        const uint32_t d = (key >> shift) & (ND - 1);
+        const uint64_t eq = match_digit(d);
+        const uint32_t below = static_cast<uint32_t>(__popcll(eq & lt));
+        const uint32_t prev = wrun[w][d];
+        if (below == 0) wrun[w][d] = prev + static_cast<uint32_t>(__popcll(eq));
+        keys[r] = key;
+        rank[r] = prev + below;
+      }
+    }
+    __syncthreads();
+    // exclusive scan of the counts in (digit, wave) order: thread i holds
+    // digit i / NW, wave i % NW
+    const int di = tid / NW, wi = tid % NW;
+    const uint32_t v = wrun[wi][di];
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wtot[w] = x;
+    __syncthreads();
+    uint32_t base = 0;
+    for (int k = 0; k < w; ++k) base += wtot[k];
+    wrun[wi][di] = base + x - v;  // every thread has read its count above
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+      if (r < R) {
+        const uint32_t d = (keys[r] >> shift) & (ND - 1);
+        kb[src ^ 1][wrun[w][d] + rank[r]] = keys[r];
+      }
+    }
+    __syncthreads();
+    src ^= 1;
+  }
+
+  const int n = s_n;
+  const uint32_t tmask = (tbits >= 32) ? ~0u : ((1u << tbits) - 1u);
+  for (int p = tid; p < n; p += kPlanThreads) {
+    const uint32_t key = kb[src][p];
+    sorted[p] = static_cast<int32_t>(key & tmask);
+    skey[p] = static_cast<int32_t>(key >> tbits);
+  }
+  if (tid == 0) *n_sorted = n;
+
+  // for every chunk: the first sorted position of the ID found at the
+  // chunk's first position (binary search; the keys are ascending)
+  const int nch = (n + kSegC - 1) / kSegC;
+  for (int ch = tid; ch < nch; ch += kPlanThreads) {
+    const int q0 = ch * kSegC;
+    const uint32_t first = (kb[src][q0] >> tbits) << tbits;  // smallest key of that ID
+    int lo = 0, hi = q0;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (kb[src][mid] < first) lo = mid + 1; else hi = mid;
+    }
+    chunk_start[ch] = lo;
+  }
+}
+
+// General sort: the first sorted position of the ID at every chunk's start.
+__global__ __launch_bounds__(256) void k_chunk_starts(const int32_t* __restrict__ skey,
+                                                      const int32_t* __restrict__ offs,
+                                                      const int32_t* __restrict__ n_sorted,
+                                                      int64_t nchunks,
+                                                      int32_t* __restrict__ chunk_start) {
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t n = *n_sorted;
+  if (c >= nchunks || c * kSegC >= n) return;
+  chunk_start[c] = offs[skey[c * kSegC]];
+}
+
+// ------------------------------------------------------------------ segment sums
+
+// One wave per (chunk of kSegC sorted positions, 256-column slice of dW).
+// The chunk's runs (positions with one ID) are summed in sorted (= token)
+// order. A run that lies wholly in the chunk is added into (or stored to)
+// its row of dW. A run cut by a chunk end is stored as a partial sum: slot 0
+// for the run that continues from the previous chunk, slot 1 for the run
+// that starts here and continues into the next one. Run boundaries depend
+// on the sorted IDs only, so every branch is uniform across the wave; the
+// dout rows of a batch and the dW rows its closed runs update are all in
+// flight before the first add.
 template <typename D>
-__global__ __launch_bounds__(256) void k_segsum(const int32_t* __restrict__ skey,
-                                                const int32_t* __restrict__ sorted,
-                                                const int32_t* __restrict__ offs,
-                                                const int32_t* __restrict__ counts,
-                                                const D* __restrict__ dout, int64_t T, int64_t H,
-                                                int64_t V_real, int64_t nslices,
-                                                float* __restrict__ dW, int32_t accumulate,
-                                                float* __restrict__ partial) {
+__global__ __launch_bounds__(256) void k_seg_chunks(const int32_t* __restrict__ skey,
+                                                    const int32_t* __restrict__ sorted,
+                                                    const int32_t* __restrict__ n_sorted,
+                                                    const D* __restrict__ dout, int64_t H,
+                                                    int64_t nslices, float* __restrict__ dW,
+                                                    int32_t accumulate,
+                                                    float* __restrict__ partial) {
   const int lane = threadIdx.x & 63;
   const int64_t slice = static_cast<int64_t>(blockIdx.y) * 4 + (threadIdx.x >> 6);
   const int64_t c = blockIdx.x;
-  const int64_t N = offs[V_real];
-  const int64_t p0 = c * kSegChunk;
+  const int64_t N = *n_sorted;
+  const int64_t p0 = c * kSegC;
   if (slice >= nslices || p0 >= N) return;
-  const int64_t p1 = min(p0 + kSegChunk, N);
+  const int64_t p1 = min(p0 + kSegC, N);
   const int64_t col = slice * kSegCols + lane * 4;
   const bool active = col < H;
+  const int32_t v_first = skey[p0];
+  const bool cont_before = p0 > 0 && skey[p0 - 1] == v_first;
+  const int32_t v_after = p1 < N ? skey[p1] : -1;
+  bool first_run = true;  // the run being summed is the chunk's first
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  int32_t next_key = skey[p0];
+  const int64_t colc = active ? col : H - 4;  // a readable column; its results are dropped
   for (int64_t b0 = p0; b0 < p1; b0 += kSegBatch) {
-    int32_t key[kSegBatch + 1];
-    f32x4 row[kSegBatch];
+    // every index is clamped into the chunk so that all loads of a batch are
+    // issued back to back; entries past the chunk are masked afterwards
+    // (loaded into vector registers: as scalars, the 33 values and 16 row
+    // addresses exhaust the scalar registers and the loads serialise)
+    int32_t key[kSegBatch + 1], tok[kSegBatch];
 #pragma unroll
-    for (int i = 0; i < kSegBatch; ++i) {
-      const int64_t p = b0 + i;
-      int32_t tk = 0;
-      if (p < p1) tk = sorted[p];
-      key[i] = (i == 0) ? next_key : ((p < p1) ? skey[p] : -1);
-      if (p < p1 && active)
-        row[i] = load_row4<D>(dout + static_cast<int64_t>(tk) * H, col);
-      else
-        row[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    {
-      const int64_t p = b0 + kSegBatch;
-      key[kSegBatch] = (p < p1) ? skey[p] : -1;
-      next_key = key[kSegBatch];
+    for (int i = 0; i <= kSegBatch; ++i) {
+      int32_t p = static_cast<int32_t>(min(b0 + i, p1 - 1));
+      asm volatile("v_mov_b32 %0, %0" : "+v"(p));
+      key[i] = skey[p];
+      if (i < kSegBatch) tok[i] = sorted[p];
     }
 #pragma unroll
+    for (int i = 0; i <= kSegBatch; ++i)
+      if (b0 + i >= p1) key[i] = v_after;
+    f32x4 row[kSegBatch], cur[kSegBatch];
+#pragma unroll
     for (int i = 0; i < kSegBatch; ++i) {
-      const int64_t p = b0 + i;
-      if (p >= p1) break;
-      acc += row[i];
-      if (p + 1 == p1 || key[i + 1] != key[i]) {  // last position of a run
-        const int64_t v = key[i];
-        const int64_t a = offs[v];
-        const int64_t e = a + counts[v];
-        if (active) {
-          if (a >= p0 && e <= p1) {
-            f32x4* dst = reinterpret_cast<f32x4*>(dW + v * H + col);
-            if (accumulate) {
-              f32x4 cur = *dst;
-              cur += acc;
-              *dst = cur;
-            } else {
-              *dst = acc;
-            }
-          } else {
-            const int slot = (a < p0) ? 0 : 1;
-            *reinterpret_cast<f32x4*>(partial + (c * 2 + slot) * H + col) = acc;
-          }
+      row[i] = load_row4<D>(dout + static_cast<int64_t>(tok[i]) * H, colc);
+      cur[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < kSegBatch; ++i)
+      if (b0 + i >= p1 || !active) row[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // dW rows of runs that close in this batch and lie wholly in the chunk
+    if (accumulate) {
+      bool fr = first_run;
+#pragma unroll
+      for (int i = 0; i < kSegBatch; ++i) {
+        const int64_t p = b0 + i;
+        if (p < p1 && key[i + 1] != key[i]) {
+          const bool closed = !(fr && cont_before) && !(p + 1 == p1 && v_after == key[i]);
+          if (closed && active)
+            cur[i] = *reinterpret_cast<const f32x4*>(dW + static_cast<int64_t>(key[i]) * H + col);
+          fr = false;
         }
+      }
+    }
+    // sums first (every load of the batch is waited for once), stores after:
+    // on this GPU stores count in the same counter as loads, so a store
+    // between two uses would make the second wait for the store as well
+    int dest[kSegBatch];  // 0 none, 1 the ID's row of dW, 2 partial slot 0, 3 slot 1
+#pragma unroll
+    for (int i = 0; i < kSegBatch; ++i) {
+      const int64_t p = b0 + i;
+      dest[i] = 0;
+      if (p < p1) acc += row[i];
+      if (p < p1 && (p + 1 == p1 || key[i + 1] != key[i])) {  // last position of a run here
+        const bool from_before = first_run && cont_before;
+        const bool into_next = p + 1 == p1 && v_after == key[i];
+        dest[i] = (!from_before && !into_next) ? 1 : (from_before ? 2 : 3);
+        row[i] = (dest[i] == 1 && accumulate) ? cur[i] + acc : acc;
         acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        first_run = false;
+      }
+    }
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < kSegBatch; ++i) {
+        if (dest[i] == 1)
+          *reinterpret_cast<f32x4*>(dW + static_cast<int64_t>(key[i]) * H + col) = row[i];
+        else if (dest[i] > 1)
+          *reinterpret_cast<f32x4*>(partial + (c * 2 + (dest[i] - 2)) * H + col) = row[i];
       }
     }
   }
 }
 
-// A group that begins in chunk c and continues past it: slot 1 of c plus
-// slot 0 of every following chunk it covers, added in a fixed pattern
-// (eight interleaved partial sums, then combined in a fixed tree).
-__global__ __launch_bounds__(256) void k_segfix(const int32_t* __restrict__ skey,
-                                                const int32_t* __restrict__ offs,
-                                                const int32_t* __restrict__ counts, int64_t H,
-                                                int64_t V_real, int64_t nslices,
-                                                float* __restrict__ dW, int32_t accumulate,
-                                                const float* __restrict__ partial) {
-  const int lane = threadIdx.x & 63;
-  const int64_t slice = static_cast<int64_t>(blockIdx.y) * 4 + (threadIdx.x >> 6);
+// One workgroup per (chunk, 256-column slice): if the chunk's first run
+// continues from the previous chunk and ends in this one, the workgroup
+// closes that ID: slot 1 of the chunk where the ID's run starts, then slot 0
+// of every later chunk up to this one. Wave w sums every kFixWaves-th of
+// those slots in chunk order, with kSegBatch loads in flight; the wave sums
+// are added in wave order.
+constexpr int kFixWaves = 4;
+__global__ __launch_bounds__(64 * kFixWaves) void k_seg_fix(const int32_t* __restrict__ skey,
+                                                            const int32_t* __restrict__ n_sorted,
+                                                            const int32_t* __restrict__ chunk_start,
+                                                            int64_t H, float* __restrict__ dW,
+                                                            int32_t accumulate,
+                                                            const float* __restrict__ partial) {
+  __shared__ f32x4 red[kFixWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t c = blockIdx.x;
-  const int64_t N = offs[V_real];
-  const int64_t p0 = c * kSegChunk;
-  if (slice >= nslices || p0 >= N) return;
-  const int64_t p1 = min(p0 + kSegChunk, N);
-  const int64_t v = skey[p1 - 1];
-  const int64_t a = offs[v];
-  const int64_t e = a + counts[v];
-  if (!(a >= p0 && e > p1)) return;
-  const int64_t col = slice * kSegCols + lane * 4;
-  if (col >= H) return;
-  const int64_t last = (e - 1) / kSegChunk;
-  f32x4 part[8];
+  const int64_t N = *n_sorted;
+  const int64_t p0 = c * kSegC;
+  if (c == 0 || p0 >= N) return;
+  const int32_t v = skey[p0];
+  if (skey[p0 - 1] != v) return;  // the first run starts here
+  const int64_t p1 = min(p0 + kSegC, N);
+  if (p1 < N && skey[p1 - 1] == v && skey[p1] == v) return;  // ... and goes on past this chunk
+  const int64_t col = static_cast<int64_t>(blockIdx.y) * kSegCols + lane * 4;
+  const int64_t colc = col < H ? col : H - 4;
+  const int64_t ca = chunk_start[c] / kSegC;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int STEP = kFixWaves * kSegBatch;
+  for (int64_t c0 = ca + 1 + w; c0 <= c; c0 += STEP) {
+    f32x4 part[kSegBatch];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) part[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t cc = c + 1; cc <= last; cc += 8) {
+    for (int u = 0; u < kSegBatch; ++u) {
+      const int64_t cc = min(c0 + static_cast<int64_t>(u) * kFixWaves, c);
+      part[u] = *reinterpret_cast<const f32x4*>(partial + (cc * 2 + 0) * H + colc);
+    }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (cc + u <= last)
-        part[u] += *reinterpret_cast<const f32x4*>(partial + ((cc + u) * 2 + 0) * H + col);
+    for (int u = 0; u < kSegBatch; ++u)
+      if (c0 + static_cast<int64_t>(u) * kFixWaves <= c) acc += part[u];
   }
-  f32x4 acc = *reinterpret_cast<const f32x4*>(partial + (c * 2 + 1) * H + col);
-  acc += ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
-  f32x4* dst = reinterpret_cast<f32x4*>(dW + v * H + col);
-  if (accumulate) {
-    f32x4 cur = *dst;
-    cur += acc;
-    *dst = cur;
-  } else {
-    *dst = acc;
-  }
+  red[w][lane] = acc;
+  __syncthreads();
+  if (w != 0 || col >= H) return;
+  f32x4 tot = *reinterpret_cast<const f32x4*>(partial + (ca * 2 + 1) * H + col);
+#pragma unroll
+  for (int k = 0; k < kFixWaves; ++k) tot += red[k][lane];
+  f32x4* dst = reinterpret_cast<f32x4*>(dW + static_cast<int64_t>(v) * H + col);
+  *dst = accumulate ? *dst + tot : tot;
 }
 
 // ------------------------------------------------------------------ candidates
@@ -515,15 +755,16 @@ __global__ void k_cand_counts(const int32_t* __restrict__ uidx, int64_t V, int64
 hipError_t run_emb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, int64_t V_real,
                        int64_t V_pad, int32_t n, size_t esize, void* out, int32_t* n_bad,
                        hipStream_t s) {
-  hipError_t err;
-  if (n_bad) {
+  if (T == 0) {
+    if (!n_bad) return hipSuccess;
     hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(64), 0, s, n_bad);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    return hipGetLastError();
   }
-  if (T == 0) return hipSuccess;
   const int64_t S = V_pad / n;
-  hipLaunchKernelGGL(k_vemb_fwd, dim3(static_cast<uint32_t>(cdiv(T, 4))), dim3(256), 0, s, ids,
-                     static_cast<const char*>(W), T, H * static_cast<int64_t>(esize), V_real, S,
+  const int64_t row_bytes = H * static_cast<int64_t>(esize);
+  const int64_t blocks = cdiv(T, 4 * kRowsPerWave);
+  hipLaunchKernelGGL(k_vemb_fwd, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, ids,
+                     static_cast<const char*>(W), T, row_bytes, V_real, S,
                      static_cast<char*>(out), n_bad);
   return hipGetLastError();
 }
@@ -540,39 +781,49 @@ hipError_t run_emb_bwd(const int32_t* ids, const void* dout, bool dout_bf16, int
   }
   if (T == 0) return hipSuccess;
   // 1. stable sort of the tokens by ID
-  const int64_t ncnt = p.nblocks * V_real;
-  if (ncnt % 4 == 0) {
-    hipLaunchKernelGGL(k_fill_i32x4, dim3(static_cast<uint32_t>(cdiv(ncnt / 4, 256))), dim3(256),
-                       0, s, reinterpret_cast<int4*>(p.bcnt), ncnt / 4);
+  if (p.one_wg) {
+    hipLaunchKernelGGL(k_emb_plan, dim3(1), dim3(kPlanThreads), 0, s, ids, T, V_real, p.tbits,
+                       p.vbits, p.sorted, p.skey, p.n_sorted, p.chunk_start);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
   } else {
-    hipLaunchKernelGGL(k_fill_i32, dim3(static_cast<uint32_t>(cdiv(ncnt, kScanThreads))),
-                       dim3(kScanThreads), 0, s, p.bcnt, ncnt, 0);
+    const int64_t ncnt = p.nblocks * V_real;
+    if (ncnt % 4 == 0) {
+      hipLaunchKernelGGL(k_fill_i32x4, dim3(static_cast<uint32_t>(cdiv(ncnt / 4, 256))),
+                         dim3(256), 0, s, reinterpret_cast<int4*>(p.bcnt), ncnt / 4);
+    } else {
+      hipLaunchKernelGGL(k_fill_i32, dim3(static_cast<uint32_t>(cdiv(ncnt, kScanThreads))),
+                         dim3(kScanThreads), 0, s, p.bcnt, ncnt, 0);
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_block_sort, dim3(static_cast<uint32_t>(p.nblocks)), dim3(kSortThreads), 0,
+                       s, ids, T, V_real, p.lkey, p.lrank, p.bcnt);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_col_scan, dim3(static_cast<uint32_t>(cdiv(V_real, 256))), dim3(256), 0, s,
+                       p.bcnt, p.nblocks, V_real, p.counts);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = run_scan(p.counts, V_real, p.offs, nullptr, p.scan_tmp, s)) != hipSuccess)
+      return err;
+    const int64_t nkeys = p.nblocks * kSortBlock;
+    hipLaunchKernelGGL(k_place_sorted, dim3(static_cast<uint32_t>(cdiv(nkeys, 256))), dim3(256), 0,
+                       s, p.lkey, p.lrank, p.bcnt, p.offs, nkeys, V_real, p.sorted, p.skey);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_chunk_starts, dim3(static_cast<uint32_t>(cdiv(p.nchunks, 256))),
+                       dim3(256), 0, s, p.skey, p.offs, p.n_sorted, p.nchunks, p.chunk_start);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(k_block_sort, dim3(static_cast<uint32_t>(p.nblocks)), dim3(kSortThreads), 0, s,
-                     ids, T, V_real, p.lkey, p.lrank, p.bcnt);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(k_col_scan, dim3(static_cast<uint32_t>(cdiv(V_real, 256))), dim3(256), 0, s,
-                     p.bcnt, p.nblocks, V_real, p.counts);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if ((err = run_scan(p.counts, V_real, p.offs, nullptr, p.scan_tmp, s)) != hipSuccess) return err;
-  const int64_t nkeys = p.nblocks * kSortBlock;
-  hipLaunchKernelGGL(k_place_sorted, dim3(static_cast<uint32_t>(cdiv(nkeys, 256))), dim3(256), 0, s,
-                     p.lkey, p.lrank, p.bcnt, p.offs, nkeys, V_real, p.sorted, p.skey);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  // 2. segment sums in fixed-size chunks of the sorted list, then the fix-up
+  // 2. chunk sums, then the IDs that cross chunk ends
   const dim3 grid(static_cast<uint32_t>(p.nchunks), static_cast<uint32_t>(cdiv(p.nslices, 4)));
   if (dout_bf16)
-    hipLaunchKernelGGL(k_segsum<uint16_t>, grid, dim3(256), 0, s, p.skey, p.sorted, p.offs, p.counts,
-                       static_cast<const uint16_t*>(dout), T, H, V_real, p.nslices, dW,
-                       accumulate, p.partial);
-  else
-    hipLaunchKernelGGL(k_segsum<float>, grid, dim3(256), 0, s, p.skey, p.sorted, p.offs, p.counts,
-                       static_cast<const float*>(dout), T, H, V_real, p.nslices, dW, accumulate,
+    hipLaunchKernelGGL(k_seg_chunks<uint16_t>, grid, dim3(256), 0, s, p.skey, p.sorted, p.n_sorted,
+                       static_cast<const uint16_t*>(dout), H, p.nslices, dW, accumulate,
                        p.partial);
+  else
+    hipLaunchKernelGGL(k_seg_chunks<float>, grid, dim3(256), 0, s, p.skey, p.sorted, p.n_sorted,
+                       static_cast<const float*>(dout), H, p.nslices, dW, accumulate, p.partial);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(k_segfix, grid, dim3(256), 0, s, p.skey, p.offs, p.counts, H, V_real,
-                     p.nslices, dW, accumulate, p.partial);
+  const dim3 fgrid(static_cast<uint32_t>(p.nchunks), static_cast<uint32_t>(p.nslices));
+  hipLaunchKernelGGL(k_seg_fix, fgrid, dim3(64 * kFixWaves), 0, s, p.skey, p.n_sorted,
+                     p.chunk_start, H, dW, accumulate, p.partial);
   return hipGetLastError();
 }
 

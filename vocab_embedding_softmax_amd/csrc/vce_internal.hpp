@@ -92,20 +92,29 @@ struct BwdPlan {
 BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, size_t esize,
                  void* ws);
 
-// Embedding backward plan: a stable sort of the tokens by ID (block-local
-// LDS sorts + per-block counts + scans, no atomics), then segment sums.
+// Embedding backward plan: a stable sort of the tokens by ID, then segment
+// sums over fixed-size chunks of the sorted list and a fix-up for the IDs
+// whose tokens span several chunks. Two ways to sort:
+//   one-workgroup: up to 16384 tokens whose (ID, token) pairs pack into 32
+//     bits are radix-sorted in one workgroup's LDS (one launch);
+//   general: block-local LDS sorts + per-block counts + scans (any size).
 struct EmbBwdPlan {
-  int64_t nblocks;     // token blocks of the local sort
+  bool one_wg;         // the one-workgroup sort applies
+  int32_t tbits;       // bits of a token index in a packed key (one-workgroup sort)
+  int32_t vbits;       // bits of an ID (one-workgroup sort)
+  int64_t nblocks;     // token blocks of the local sort (general)
   int64_t nchunks, nslices, scan_blocks;
-  int32_t* bcnt;       // [nblocks][V_real] per-block occurrences -> per-block offsets
-  int32_t* counts;     // [V_real] occurrences of each ID
-  int32_t* offs;       // [V_real + 1] exclusive prefix of counts (offs[V_real] = total)
-  uint64_t* lkey;      // [nblocks * block] block-sorted keys (ID << 32 | token)
-  int32_t* lrank;      // [nblocks * block] rank among equal IDs inside the block
+  int32_t* bcnt;       // [nblocks][V_real] per-block occurrences -> per-block offsets (general)
+  int32_t* counts;     // [V_real] occurrences of each ID (general)
+  int32_t* offs;       // [V_real + 1] exclusive prefix of counts, offs[V_real] = total (general)
+  uint64_t* lkey;      // [nblocks * block] block-sorted keys (ID << 32 | token) (general)
+  int32_t* lrank;      // [nblocks * block] rank among equal IDs inside the block (general)
+  int32_t* scan_tmp;   // [scan_blocks + 1] (general)
   int32_t* sorted;     // [T] token indices sorted by (ID, token)
   int32_t* skey;       // [T] the ID of each sorted position
-  int32_t* scan_tmp;   // [scan_blocks + 1]
-  float* partial;      // [nchunks][2][H]
+  int32_t* n_sorted;   // [1] number of valid tokens (one-workgroup sort; general: offs + V_real)
+  int32_t* chunk_start;// [nchunks] first sorted position of the ID at each chunk's first position
+  float* partial;      // [nchunks][2][H] partial sums of IDs that cross chunk ends
   size_t bytes;
 };
 EmbBwdPlan plan_emb_bwd(int64_t T, int64_t H, int64_t V_real, void* ws);
