@@ -457,7 +457,7 @@ __device__ __forceinline__ TileGeom decode_tile(const GemmShape& g, uint32_t L) 
 // epilogue runs, the first K slices of the workgroup's next tile are already
 // on their way into LDS.
 template <typename E, int MODE, bool AKM, bool BKM, int BM, int BN, int WAVES_M, int WAVES_N,
-          int RB, int NS, int OCC>
+          int RB, int NS, int OCC, bool SPREAD>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N,
                                                       64 * WAVES_M * WAVES_N),
                           amdgpu_waves_per_eu(OCC, OCC)))
@@ -472,6 +472,7 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
   constexpr int STAGE = A_BYTES + B_BYTES;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
   static_assert(NS >= 2 && SS >= 2 && SS % 2 == 0, "stages");
+  static_assert(!SPREAD || NS >= 3, "spread issue needs a free stage ahead");
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
   __shared__ float2 red[MODE == EPI_FWD && WAVES_M > 1 ? (WAVES_M - 1) * BN : 1];
 
@@ -624,11 +625,45 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       constexpr bool ISSUE = decltype(issue_next)::value;
       constexpr bool LAST = decltype(last)::value;
       const char* st = smem + (kt % NS) * STAGE;
+      if constexpr (SPREAD && ISSUE) {
+        // slice kt+NS-1 goes into the stage slice kt-1 used (free since the
+        // previous barrier); its loads are spread over the MFMAs of the
+        // sub-steps before this slice's barrier
+        const int kn = kt + NS - 1;
+        const int64_t kofs = static_cast<int64_t>(kn) * BK;
+        const uint32_t stl = smem_lds + (kn % NS) * STAGE;
+        const int64_t kleft = klen - kofs;
+        const char* pa = Ab + kofs * (AKM ? g.lda : 1) * ES;
+        const char* pb = Bb + kofs * (BKM ? g.ldb : 1) * ES;
+        const bool fast_a = sa.fast(kleft), fast_b = sb.fast(kleft);
+        constexpr int NT = MI * NI;
+        constexpr int SLOTS = (SS - 1) * NT;  // MFMAs before the barrier
+        static_for<0, SS - 1>([&](auto ss) {
+          constexpr int sub = decltype(ss)::value;
+          read_frags(st, sub + 1, fa[(sub + 1) & 1], fb[(sub + 1) & 1]);
+          static_for<0, NT>([&](auto kk) {
+            constexpr int k = decltype(kk)::value;
+            constexpr int slot = sub * NT + k;
+            // loads l with l * SLOTS / LOADS == slot go right before this MFMA
+            static_for<0, LOADS>([&](auto ll) {
+              constexpr int l = decltype(ll)::value;
+              if constexpr ((l * SLOTS) / LOADS == slot) {
+                if constexpr (l < SA::Q)
+                  sa.issue_q(l, stl, pa, kleft, wave, fast_a);
+                else
+                  sb.issue_q(l - SA::Q, stl + A_BYTES, pb, kleft, wave, fast_b);
+              }
+            });
+            mma_chunk<E>(acc[k / NI][k % NI], fa[sub & 1][k / NI], fb[sub & 1][k % NI]);
+          });
+        });
+      } else {
 #pragma unroll
-      for (int sub = 0; sub + 1 < SS; ++sub) {
-        read_frags(st, sub + 1, fa[(sub + 1) & 1], fb[(sub + 1) & 1]);
-        mfmas(fa[sub & 1], fb[sub & 1]);
-        interleave();
+        for (int sub = 0; sub + 1 < SS; ++sub) {
+          read_frags(st, sub + 1, fa[(sub + 1) & 1], fb[(sub + 1) & 1]);
+          mfmas(fa[sub & 1], fb[sub & 1]);
+          interleave();
+        }
       }
       constexpr int LB = (SS - 1) & 1;
       if constexpr (!LAST) {
@@ -647,7 +682,7 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
         uint32_t stl = 0;
         int64_t kleft = 0;
         bool fast_a = true, fast_b = true;
-        if constexpr (ISSUE) {
+        if constexpr (ISSUE && !SPREAD) {
           const int kn = kt + NS;
           const int64_t kofs = static_cast<int64_t>(kn) * BK;
           stl = smem_lds + (kn % NS) * STAGE;
@@ -660,7 +695,7 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
         constexpr int NT = MI * NI;
         static_for<0, (NT > LOADS ? NT : LOADS)>([&](auto kk) {
           constexpr int k = decltype(kk)::value;
-          if constexpr (ISSUE && k < LOADS) {
+          if constexpr (ISSUE && !SPREAD && k < LOADS) {
             if constexpr (k < SA::Q)
               sa.issue_q(k, stl, pa, kleft, wave, fast_a);
             else
@@ -694,19 +729,28 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
         wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::"r"(smem) : "memory");
-      if (NS - 1 < nk) issue(NS - 1);
+      if (!SPREAD && NS - 1 < nk) issue(NS - 1);
       load_epi();
       asm volatile("" ::"r"(smem) : "memory");
       read_frags(smem, 0, fa[0], fb[0]);
       int kt = 0;
-      for (; kt + NS < nk; ++kt)
-        kstep(kt, std::false_type{}, std::true_type{}, std::false_type{});
-      if (kt + NS == nk && kt + 1 < nk) {
-        kstep(kt, std::false_type{}, std::false_type{}, std::false_type{});
-        ++kt;
+      if constexpr (SPREAD) {
+        // kstep(kt) queues slice kt+NS-1; at its barrier the slices after
+        // kt+1 that are in flight are kt+2 .. kt+NS-1
+        for (; kt + NS - 1 < nk; ++kt)
+          kstep(kt, std::false_type{}, std::true_type{}, std::false_type{});
+        for (; kt + 1 < nk; ++kt)
+          kstep(kt, std::true_type{}, std::false_type{}, std::false_type{});
+      } else {
+        for (; kt + NS < nk; ++kt)
+          kstep(kt, std::false_type{}, std::true_type{}, std::false_type{});
+        if (kt + NS == nk && kt + 1 < nk) {
+          kstep(kt, std::false_type{}, std::false_type{}, std::false_type{});
+          ++kt;
+        }
+        for (; kt + 1 < nk; ++kt)
+          kstep(kt, std::true_type{}, std::false_type{}, std::false_type{});
       }
-      for (; kt + 1 < nk; ++kt)
-        kstep(kt, std::true_type{}, std::false_type{}, std::false_type{});
       kstep(kt, std::true_type{}, std::false_type{}, std::true_type{});
     } else {
       load_epi();

@@ -212,15 +212,32 @@ static int64_t persistent_blocks(int64_t tiles) {
   return min(grid, round_up(tiles, 8));
 }
 
+// K staging of each GEMM: bytes per operand position per K slice, LDS
+// stages, and whether a slice's loads are spread over the MFMAs of the slice
+// two before its use (needs three or more stages) or issued together right
+// after the barrier that frees their stage.
+struct Staging {
+  int rb, ns;
+  bool spread;
+};
+template <int MODE, bool AKM, bool BKM>
+constexpr Staging staging() {
+  if constexpr (MODE == EPI_FWD) return {VCE_FWD_RB, VCE_FWD_NS, VCE_FWD_SPREAD != 0};
+  else if constexpr (MODE == EPI_GRAD) return {VCE_GRAD_RB, VCE_GRAD_NS, VCE_GRAD_SPREAD != 0};
+  else if constexpr (!AKM) return {VCE_DH_RB, VCE_DH_NS, VCE_DH_SPREAD != 0};
+  else return {VCE_DW_RB, VCE_DW_NS, VCE_DW_SPREAD != 0};
+}
+
 template <typename E, int MODE, bool AKM = false, bool BKM = false>
 static hipError_t launch_gemm(const GemmShape& g, const EpiArgs& e, hipStream_t s) {
   const int64_t tiles = static_cast<int64_t>(g.n_seg) * g.tiles_per_seg * g.tiles_n * g.k_splits;
   if (tiles <= 0) return hipSuccess;
   if (tiles >= (int64_t{1} << 31)) return hipErrorInvalidValue;
   const int64_t blocks = persistent_blocks(tiles);
-  hipLaunchKernelGGL(
-      (k_gemm_tn<E, MODE, AKM, BKM, kTileM, kTileN, kWavesM, kWavesN, kRowBytes, kStages, kOcc>),
-      dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWavesM * kWavesN), 0, s, g, e);
+  constexpr Staging st = staging<MODE, AKM, BKM>();
+  hipLaunchKernelGGL((k_gemm_tn<E, MODE, AKM, BKM, kTileM, kTileN, kWavesM, kWavesN, st.rb, st.ns,
+                                kOcc, st.spread>),
+                     dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWavesM * kWavesN), 0, s, g, e);
   return hipGetLastError();
 }
 

@@ -28,15 +28,47 @@ constexpr int kOcc = VCE_OCC;       // workgroups resident per CU (waves per SIM
 #ifndef VCE_CHUNK_ROWS
 #define VCE_CHUNK_ROWS 32768
 #endif
-#ifndef VCE_STAGES
-#define VCE_STAGES 2
+// K staging per GEMM (bytes per position per K slice, LDS stages, spread
+// issue of a slice's loads). Measured on the tied-step shapes: the forward
+// and G GEMMs run fastest with two 128-byte stages, dh and dW with four
+// 64-byte stages (dh with its loads spread over the slice before).
+#ifndef VCE_FWD_RB
+#define VCE_FWD_RB 128
 #endif
-#ifndef VCE_ROW_BYTES
-#define VCE_ROW_BYTES 128
+#ifndef VCE_FWD_NS
+#define VCE_FWD_NS 2
+#endif
+#ifndef VCE_FWD_SPREAD
+#define VCE_FWD_SPREAD 0
+#endif
+#ifndef VCE_GRAD_RB
+#define VCE_GRAD_RB 128
+#endif
+#ifndef VCE_GRAD_NS
+#define VCE_GRAD_NS 2
+#endif
+#ifndef VCE_GRAD_SPREAD
+#define VCE_GRAD_SPREAD 0
+#endif
+#ifndef VCE_DH_RB
+#define VCE_DH_RB 64
+#endif
+#ifndef VCE_DH_NS
+#define VCE_DH_NS 4
+#endif
+#ifndef VCE_DH_SPREAD
+#define VCE_DH_SPREAD 1
+#endif
+#ifndef VCE_DW_RB
+#define VCE_DW_RB 64
+#endif
+#ifndef VCE_DW_NS
+#define VCE_DW_NS 4
+#endif
+#ifndef VCE_DW_SPREAD
+#define VCE_DW_SPREAD 0
 #endif
 constexpr int kChunkRows = VCE_CHUNK_ROWS;  // most vocabulary rows of one backward chunk
-constexpr int kStages = VCE_STAGES;       // K slices in flight + the one being consumed
-constexpr int kRowBytes = VCE_ROW_BYTES;  // bytes of one operand position per K slice
 constexpr int kWavesM = VCE_WAVES_M;  // waves per workgroup along M
 constexpr int kWavesN = VCE_WAVES_N;  // waves per workgroup along N
 constexpr int kPadK = 64;     // staged operands are padded to this many K elements
