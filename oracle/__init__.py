@@ -26,4 +26,5 @@ from .ce import (  # noqa: F401
     ce_forward, ce_backward, grad_scale, cross_entropy,
 )
 from .sampled import candidates, sampled_step  # noqa: F401
+from .argmax import shard_argmax, merge_shard_argmax, greedy_argmax  # noqa: F401
 from .tied import tied_step  # noqa: F401

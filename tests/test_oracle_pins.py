@@ -434,3 +434,99 @@ def test_sampled_full_candidate_set_equals_full_ce():
     assert np.allclose(s["loss"], f["loss"], rtol=1e-13, atol=1e-15)
     assert np.allclose(s["dh"], f["dh"], rtol=1e-12, atol=1e-15)
     assert np.allclose(s["dW"], f["dW"], rtol=1e-12, atol=1e-15)
+
+
+# ------------------------------------------------------------------ greedy argmax
+
+def _bruteforce_argmax(h, W, V_real):
+    """Pure-Python: exact logits by math.fsum, first index holding the maximum."""
+    out = []
+    for row in h:
+        best_v, best_i = None, None
+        for v in range(V_real):
+            z = math.fsum(a * b for a, b in zip(row, W[v]))
+            if best_v is None or z > best_v:
+                best_v, best_i = z, v
+        out.append((best_i, best_v))
+    return out
+
+
+@pytest.mark.parametrize("V_real,V_pad,n", [(1, 2, 2), (3, 4, 4), (7, 8, 2), (9, 12, 3),
+                                             (16, 16, 1), (13, 16, 8)])
+def test_argmax_bruteforce_tiny(V_real, V_pad, n):
+    rng = np.random.default_rng(V_real * 31 + V_pad)
+    T, H = 9, 4
+    h = rng.standard_normal((T, H))
+    W = rng.standard_normal((V_pad, H))
+    W[V_real:] = np.nan                     # padded rows must never be read
+    r = oracle.greedy_argmax(h, W, V_real, V_pad, n)
+    ref = _bruteforce_argmax(h.tolist(), W.tolist(), V_real)
+    assert r["index"].tolist() == [i for i, _ in ref]
+    assert np.allclose(r["value"], [v for _, v in ref], rtol=1e-14, atol=1e-14)
+
+
+def test_argmax_padded_rows_never_chosen():
+    rng = np.random.default_rng(8)
+    T, H, V_real, V_pad = 5, 6, 10, 16
+    h = np.abs(rng.standard_normal((T, H)))
+    W = rng.standard_normal((V_pad, H))
+    for pad in (1e30, np.inf, np.nan):
+        W[V_real:] = pad
+        for n in (1, 2, 4, 8):
+            r = oracle.greedy_argmax(h, W, V_real, V_pad, n)
+            assert (r["index"] < V_real).all() and (r["index"] >= 0).all()
+    # the last shard of n = 8 (rows 14, 15) owns no real row
+    r = oracle.greedy_argmax(h, W, V_real, V_pad, 8)
+    assert (r["shard_index"][5:] == -1).all() and np.isneginf(r["shard_value"][5:]).all()
+
+
+def test_argmax_ties_take_lowest_index():
+    # rows 2, 5, 9 and 13 are copies of one row that beats every other row;
+    # with 4 shards of 4 rows the copies sit in shards 0, 1, 2 and 3
+    rng = np.random.default_rng(9)
+    T, H, V = 4, 3, 16
+    h = np.abs(rng.standard_normal((T, H))) + 0.1
+    W = -np.abs(rng.standard_normal((V, H)))
+    top = np.array([3.0, 2.0, 1.0])
+    for v in (13, 9, 5, 2):
+        W[v] = top
+    for n in (1, 2, 4, 8, 16):
+        r = oracle.greedy_argmax(h, W, V, V, n)
+        assert (r["index"] == 2).all()
+    # without row 2 the lowest copy left is row 5 (shard 1 of 4)
+    W[2] = -top
+    r = oracle.greedy_argmax(h, W, V, V, 4)
+    assert (r["index"] == 5).all()
+    assert (r["shard_index"][1:, 0] == [5, 9, 13]).all()
+
+
+def test_argmax_one_hot_hidden_rows():
+    # h_t = e_j makes z[t, v] = W[v, j]: the argmax is the row holding the
+    # largest entry of column j
+    V_real, V_pad, H = 37, 40, 5
+    W = np.tile(np.arange(V_pad, dtype=np.float64)[:, None] * 0.0, (1, H))
+    winners = [3, 36, 17, 0, 22]
+    for j, v in enumerate(winners):
+        W[:, j] = -1.0
+        W[v, j] = 2.0 + j
+    W[V_real:] = 100.0                       # padding: larger, but not classes
+    h = np.eye(H)
+    for n in (1, 2, 4, 5, 8):
+        r = oracle.greedy_argmax(h, W, V_real, V_pad, n)
+        assert r["index"].tolist() == winners
+        assert r["value"].tolist() == [2.0 + j for j in range(H)]
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8])
+def test_argmax_sharded_equals_unsharded(n):
+    inp = config_inputs("c1")
+    h = oracle.decode(inp.h, inp.dtype)
+    W = oracle.decode(inp.W, inp.dtype)
+    z = h @ W[:inp.V_real].T
+    r = oracle.greedy_argmax(h, W, inp.V_real, inp.V_pad, n)
+    # the global maximum of the merged reports equals the unsharded maximum,
+    # and the chosen index holds it
+    assert np.array_equal(r["value"], z.max(axis=1))
+    assert np.array_equal(z[np.arange(z.shape[0]), r["index"]], r["value"])
+    one = oracle.greedy_argmax(h, W, inp.V_real, inp.V_pad, 1)
+    assert np.array_equal(r["index"], one["index"])
