@@ -295,6 +295,26 @@ def main():
                          "GB_s": scatter_bytes / (ms_s * 1e-3) / 1e9,
                          "frac": scatter_bytes / (ms_s * 1e-3) / PEAK_HBM},
         }
+    # Greedy argmax over the same table and hidden rows (the decoding twin of
+    # the forward: same logits GEMM, (max, lowest index) epilogue), timed on
+    # its own after the step: flops per call = 2*T*H*V_real.
+    ws_arg = torch.empty(V.vce_argmax_workspace_bytes(T, H, Vr, Vp, n, dt_code),
+                         dtype=torch.uint8, device=dev)
+    out_arg = V.vce_argmax(h, W, Vr, n, ws=ws_arg)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record(stream)
+    for _ in range(reps):
+        V.vce_argmax(h, W, Vr, n, out=out_arg, ws=ws_arg)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_arg = e0.elapsed_time(e1) / reps
+    res["argmax"] = {"kernel": "k_gemm_tn<bf16,EPI_ARGMAX> + k_argmax_merge (vce_argmax)",
+                     "ms": ms_arg, "tokens_s": T / (ms_arg * 1e-3),
+                     "achieved_TFLOP_s": flop_gemm / (ms_arg * 1e-3) / 1e12,
+                     "frac": flop_gemm / (ms_arg * 1e-3) / PEAK_BF16}
+    log(f"[bench] argmax {ms_arg:.3f} ms/call")
     if a.copy_probe:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -303,7 +323,7 @@ def main():
         torch.cuda.synchronize()
         res["copy_probe_bytes"] = src.numel() * 4
         del src, dst
-    del ws, dh, dW, W, h
+    del ws, dh, dW, W, h, ws_arg, out_arg
     torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
         log(f"[bench] CPU baseline: oracle on {a.cpu_tokens} tokens")

@@ -157,6 +157,36 @@ vce_status vce_bwd_timed(const void* h, const void* W, const int32_t* targets, c
                          int64_t n_events);
 
 /* ------------------------------------------------------------------------ *
+ * Greedy argmax over the sharded LM head (greedy decoding).                 *
+ *                                                                           *
+ * [TP] "LM Head (ColumnParallelLinear)": every rank computes the logits of  *
+ * its own vocabulary shard, and an on-device sampler finds the global       *
+ * argmax across the shards without gathering the [T, V] logits. Here every  *
+ * vocabulary tile reduces its logits tile to (largest logit, lowest row     *
+ * holding it) over its real rows; the tiles of a shard merge into the       *
+ * shard's report, and the shard reports into the global result, always by   *
+ * larger value, then lower index (so ties go to the lowest vocabulary       *
+ * index, as for an unsharded argmax that returns the first maximum).        *
+ * Padded rows are never read and never chosen ([VS] paragraph 4).           *
+ *                                                                           *
+ * In:  h [T,H] dt, W [V_pad,H] dt.                                          *
+ * Out: index [T] int32   argmax over v < V_real of z[t,v] = h[t,:].W[v,:];  *
+ *      value [T] float   that logit (float32 accumulation);                 *
+ *      shard_value, shard_index: optional (NULL = not written) [num_shards] *
+ *                        [T] float / int32, each shard's report (-inf and   *
+ *                        -1 for a shard that owns no real row).             *
+ * ws: device workspace of at least vce_argmax_workspace_bytes(...) bytes.   *
+ * Errors as for vce_fwd.                                                    *
+ * ------------------------------------------------------------------------ */
+size_t vce_argmax_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                                  int32_t num_shards, vce_dtype dt);
+
+vce_status vce_argmax(const void* h, const void* W, int64_t T, int64_t H, int64_t V_real,
+                      int64_t V_pad, int32_t num_shards, vce_dtype dt, int32_t* index,
+                      float* value, float* shard_value, int32_t* shard_index,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Masked embedding lookup.                                                  *
  *                                                                           *
  * [VS] paragraph 1: a shard tests whether an ID is in its row range, turns  *

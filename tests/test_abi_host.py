@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in vce.SIGNATURES, n
@@ -102,6 +102,24 @@ def test_emb_argument_errors():
     assert lib.vemb_bwd(A, B, 0, 4, 64, 1000, 1024, 4, C, 1, A, need - 1, None) == WORKSPACE
     assert lib.vemb_bwd(A, B, 0, 4, 64, 1000, 1024, 4, NUL, 1, A, need, None) == NULL
     assert lib.vemb_bwd(A, B, 0, 4, 64, 1001, 1000, 4, C, 1, A, need, None) == SHAPE
+
+
+def test_argmax_argument_errors():
+    need = lib.vce_argmax_workspace_bytes(4, 64, 1000, 1024, 4, 1)
+    assert need > 0
+    args = lambda T=4, H=64, Vr=1000, Vp=1024, n=4, dt=1, h=A, W=B, idx=C, val=A, ws=A, \
+        wsb=need: lib.vce_argmax(h, W, T, H, Vr, Vp, n, dt, idx, val, NUL, NUL, ws, wsb, None)
+    assert args(n=3) == SHARD
+    assert args(dt=7) == DTYPE
+    assert args(Vr=1025) == SHAPE
+    assert args(h=NUL) == NULL
+    assert args(idx=NUL) == NULL
+    assert args(H=12) == ALIGN
+    assert args(W=MIS) == ALIGN
+    assert args(wsb=need - 1) == WORKSPACE
+    assert args(ws=NUL) == WORKSPACE
+    assert args(T=0, h=NUL, W=NUL, idx=NUL, val=NUL, ws=NUL, wsb=0) == OK  # nothing to do
+    assert lib.vce_argmax_workspace_bytes(8, 64, 100, 101, 2, 1) == 0     # 101 % 2 != 0
 
 
 def test_candidates_argument_errors():

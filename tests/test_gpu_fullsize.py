@@ -162,3 +162,32 @@ def test_c5_full_size_sampled_softmax(V):
     assert rel_l2(r.dh.cpu().numpy(), ref["dh"]) <= TOL["bf16"]["grad"]
     assert rel_l2(r.extra["dWc"].cpu().numpy(), ref["dWc"]) <= TOL["bf16"]["grad"]
     assert rel_l2(r.dW.cpu().numpy(), ref["dW"]) <= TOL["bf16"]["grad"]
+
+
+def test_c3_full_size_argmax_sampled_tokens(V):
+    """Greedy argmax at the large-vocabulary shape (T=8192, H=3072, V=201088,
+    8 shards), in the launch configuration the bench times; sampled tokens
+    against the oracle, every token against properties of the merge."""
+    from tests.test_gpu_argmax import check_argmax
+    say("case c3 full-size argmax")
+    inp = config_inputs("c3")
+    dev = "cuda"
+    h = V.from_bits(inp.h, inp.dtype, dev)
+    W = V.from_bits(inp.W, inp.dtype, dev)
+    r = V.vce_argmax(h, W, inp.V_real, inp.num_shards, shard_reports=True)
+    torch.cuda.synchronize()
+    idx = r.index.cpu().numpy().astype(np.int64)
+    val = r.value.cpu().numpy().astype(np.float64)
+    sv = r.shard_value.cpu().numpy()
+    si = r.shard_index.cpu().numpy()
+    S = inp.V_pad // inp.num_shards
+    # every token: the global result is the best shard report, and each shard
+    # report lies inside its shard
+    assert np.array_equal(r.value.cpu().numpy(), sv.max(axis=0))
+    for k in range(inp.num_shards):
+        assert ((si[k] >= k * S) & (si[k] < (k + 1) * S)).all()
+    sample = _sample_tokens(inp.targets, inp.V_real, 40, 17)
+    h64 = oracle.decode(inp.h[sample], inp.dtype)
+    W64 = oracle.decode(inp.W, inp.dtype)
+    nclear = check_argmax(idx[sample], val[sample], h64, W64, inp.V_real, "c3 sampled")
+    say(f"c3 argmax: {nclear} of {len(sample)} sampled tokens without a near tie")

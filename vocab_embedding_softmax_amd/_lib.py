@@ -46,6 +46,9 @@ SIGNATURES = {
     "vemb_fwd": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P, _P, _P]),
     "vemb_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
     "vemb_bwd": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _I64, _I32, _P, _I32, _P, _SZ, _P]),
+    "vce_argmax_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32, _I32]),
+    "vce_argmax": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _SZ,
+                          _P]),
     "vss_candidates_workspace_bytes": (_SZ, [_I64, _I64]),
     "vss_candidates": (_I32, [_P, _I64, _I64, _I32, _P, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _P]),
 }
@@ -128,6 +131,10 @@ def vce_bwd_workspace_bytes(T, H, V_real, V_pad, num_shards, dtype=VCE_BF16) -> 
 
 def vce_bwd_event_count(T, H, V_real, V_pad, num_shards, dt) -> int:
     return int(lib.vce_bwd_event_count(T, H, V_real, V_pad, num_shards, dt))
+
+
+def vce_argmax_workspace_bytes(T, H, V_real, V_pad, num_shards, dtype=VCE_BF16) -> int:
+    return int(lib.vce_argmax_workspace_bytes(T, H, V_real, V_pad, num_shards, dtype))
 
 
 def vemb_bwd_workspace_bytes(T, H, V_real, V_pad) -> int:
@@ -217,6 +224,35 @@ def vce_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.
         arr = (ctypes.c_void_p * n_ev)(*[e.cuda_event for e in events])
         _check("vce_bwd_timed", lib.vce_bwd_timed(*args, arr, n_ev))
     return BwdOut(dh, dW)
+
+
+ArgOut = namedtuple("ArgOut", "index value shard_value shard_index")
+
+
+def vce_argmax(h: torch.Tensor, W: torch.Tensor, V_real: int, num_shards: int, *,
+               shard_reports: bool = False, out: Optional[ArgOut] = None,
+               ws: Optional[torch.Tensor] = None, stream=None) -> ArgOut:
+    """Greedy argmax over the real rows: index [T] int32, value [T] float32, and
+    (shard_reports=True) each shard's (value, index) [num_shards, T]."""
+    T, H = h.shape
+    V_pad = W.shape[0]
+    dt = _dt(h)
+    _need(h, "h")
+    _need(W, "W", h.dtype, (V_pad, H))
+    dev = h.device
+    if out is None:
+        f = dict(dtype=torch.float32, device=dev)
+        i = dict(dtype=torch.int32, device=dev)
+        out = ArgOut(torch.empty(T, **i), torch.empty(T, **f),
+                     torch.empty(num_shards, T, **f) if shard_reports else None,
+                     torch.empty(num_shards, T, **i) if shard_reports else None)
+    need = vce_argmax_workspace_bytes(T, H, V_real, V_pad, num_shards, dt)
+    ws = _workspace(need, dev, ws)
+    st = lib.vce_argmax(_ptr(h), _ptr(W), T, H, V_real, V_pad, num_shards, dt, _ptr(out.index),
+                        _ptr(out.value), _ptr(out.shard_value), _ptr(out.shard_index), _ptr(ws),
+                        ws.numel(), _stream(stream, dev))
+    _check("vce_argmax", st)
+    return out
 
 
 def vemb_fwd(ids: torch.Tensor, W: torch.Tensor, V_real: int, num_shards: int, *,

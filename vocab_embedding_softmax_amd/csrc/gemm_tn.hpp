@@ -7,6 +7,8 @@
 //   EPI_GRAD  logits tile -> G = scale * (softmax - onehot), stored
 //             token-major in the input element type
 //   EPI_STORE plain float32 store / accumulate (dh and dW)
+//   EPI_ARGMAX logits tile -> per-token (largest logit, lowest row index
+//             holding it) over the tile's real vocabulary rows
 //
 // Workgroup: WAVES_M x WAVES_N waves over a BM x BN tile; each wave owns a
 // (BM/WAVES_M) x (BN/WAVES_N) sub-tile made of 32 x 32 MFMA blocks. K
@@ -45,7 +47,7 @@
 
 namespace vce {
 
-enum EpiMode { EPI_FWD = 0, EPI_GRAD = 1, EPI_STORE = 2 };
+enum EpiMode { EPI_FWD = 0, EPI_GRAD = 1, EPI_STORE = 2, EPI_ARGMAX = 3 };
 
 struct GemmShape {
   const void* A;
@@ -95,10 +97,17 @@ struct StoreArgs {
   int64_t m_zero_from;  // rows at or past this receive 0 (or are left alone when accumulating)
 };
 
+struct ArgArgs {
+  int64_t T;
+  float* val;           // [tiles_m][T]: largest logit of the tile's real rows (-inf if none)
+  int32_t* idx;         // [tiles_m][T]: its vocabulary row, the lowest on ties (-1 if none)
+};
+
 struct EpiArgs {
   FwdArgs fwd;
   GradArgs grad;
   StoreArgs store;
+  ArgArgs arg;
 };
 
 // 16 zero bytes: the source of the chunks that lie past K
@@ -474,7 +483,7 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
   static_assert(NS >= 2 && SS >= 2 && SS % 2 == 0, "stages");
   static_assert(!SPREAD || NS >= 3, "spread issue needs a free stage ahead");
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
-  __shared__ float2 red[MODE == EPI_FWD && WAVES_M > 1 ? (WAVES_M - 1) * BN : 1];
+  __shared__ float2 red[(MODE == EPI_FWD || MODE == EPI_ARGMAX) && WAVES_M > 1 ? (WAVES_M - 1) * BN : 1];
 
   using SA = Stager<E, BM, NW, RB, AKM>;
   using SB = Stager<E, BN, NW, RB, BKM>;
@@ -851,6 +860,65 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
           }
           const int64_t tt = t.n0 + col;
           if (tt < f.T) f.stats[t.tm * f.T + tt] = make_float2(m, s);
+        }
+      }
+    } else if constexpr (MODE == EPI_ARGMAX) {
+      const ArgArgs& a = e.arg;
+      // real rows of this wave's sub-tile: local rows [0, lim)  (m_load_end = V_real)
+      const int lim = static_cast<int>(max(min(t.m_load - vbase, static_cast<int64_t>(WM)),
+                                           static_cast<int64_t>(0)));
+      const int lim_l = lim - 4 * half;
+      float bvj[NI];
+      int bij[NI];
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        // this lane's rows in increasing order; strict > keeps the lowest row on ties
+        float bv = -INFINITY;
+        int bi = -1;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rl = i * 32 + 8 * (r >> 2) + (r & 3);  // row - 4*half
+            const float v = acc[i][j][r];
+            if (rl < lim_l && v > bv) {
+              bv = v;
+              bi = rl + 4 * half;
+            }
+          }
+        const float ov = __shfl_xor(bv, 32);
+        const int oi = __shfl_xor(bi, 32);
+        if (ov > bv || (ov == bv && oi >= 0 && (bi < 0 || oi < bi))) {
+          bv = ov;
+          bi = oi;
+        }
+        bvj[j] = bv;
+        bij[j] = bi < 0 ? -1 : wm * WM + bi;  // row within the tile
+        const int col = wn * WN + j * 32 + l32;
+        if (wm > 0 && half == 0) red[(wm - 1) * BN + col] = make_float2(bv, __int_as_float(bij[j]));
+      }
+      if constexpr (WAVES_M > 1) lds_barrier();
+      // the first wave along M merges in wave order (rows increase with the wave)
+      if (wm == 0 && half == 0) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          const int col = wn * WN + j * 32 + l32;
+          float bv = bvj[j];
+          int bi = bij[j];
+#pragma unroll
+          for (int w = 1; w < WAVES_M; ++w) {
+            const float2 o = red[(w - 1) * BN + col];
+            const int oi = __float_as_int(o.y);
+            if (o.x > bv || (o.x == bv && oi >= 0 && (bi < 0 || oi < bi))) {
+              bv = o.x;
+              bi = oi;
+            }
+          }
+          const int64_t tt = t.n0 + col;
+          if (tt < a.T) {
+            a.val[t.tm * a.T + tt] = bv;
+            a.idx[t.tm * a.T + tt] = bi < 0 ? -1 : static_cast<int32_t>(t.m0 + bi);
+          }
         }
       }
     } else if constexpr (MODE == EPI_GRAD) {

@@ -61,6 +61,12 @@ size_t vce_bwd_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_p
   return vce::plan_bwd(T, H, V_real, V_pad, num_shards, esize_of(dt), nullptr).bytes;
 }
 
+size_t vce_argmax_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                                  int32_t num_shards, vce_dtype dt) {
+  if (check_table(T, H, V_real, V_pad, num_shards) != VCE_OK || !dtype_ok(dt)) return 0;
+  return vce::plan_argmax(T, H, V_real, V_pad, num_shards, nullptr).bytes;
+}
+
 size_t vemb_bwd_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_pad) {
   if (check_table(T, H, V_real, V_pad, 1) != VCE_OK) return 0;
   return vce::plan_emb_bwd(T, H, V_real, nullptr).bytes;
@@ -139,6 +145,28 @@ vce_status vce_bwd_timed(const void* h, const void* W, const int32_t* targets, c
   return hip_status(vce::run_ce_bwd(h, W, targets, lse, grad_loss, n_valid, red, T, H, V_real,
                                     V_pad, num_shards, dt == VCE_BF16, dh, dW, accumulate_dW ? 1 : 0,
                                     p, static_cast<hipStream_t>(stream), events));
+}
+
+vce_status vce_argmax(const void* h, const void* W, int64_t T, int64_t H, int64_t V_real,
+                      int64_t V_pad, int32_t num_shards, vce_dtype dt, int32_t* index,
+                      float* value, float* shard_value, int32_t* shard_index, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dt)) return VCE_ERR_DTYPE;
+  vce_status st = check_table(T, H, V_real, V_pad, num_shards);
+  if (st != VCE_OK) return st;
+  if (T > 0 && (!h || !W || !index || !value)) return VCE_ERR_NULL;
+  if (H % 8 != 0) return VCE_ERR_ALIGN;
+  if (T > 0 && (!aligned16(h) || !aligned16(W) || !aligned4(index) || !aligned4(value) ||
+                (shard_value && !aligned4(shard_value)) ||
+                (shard_index && !aligned4(shard_index))))
+    return VCE_ERR_ALIGN;
+  const vce::ArgPlan probe = vce::plan_argmax(T, H, V_real, V_pad, num_shards, nullptr);
+  if (T > 0 && (!ws || ws_bytes < probe.bytes)) return VCE_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return VCE_ERR_ALIGN;
+  const vce::ArgPlan p = vce::plan_argmax(T, H, V_real, V_pad, num_shards, ws);
+  return hip_status(vce::run_argmax(h, W, T, H, V_real, V_pad, num_shards, dt == VCE_BF16, index,
+                                    value, shard_value, shard_index, p,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 vce_status vemb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, int64_t V_real,

@@ -44,6 +44,21 @@ FwdPlan plan_fwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
   return p;
 }
 
+ArgPlan plan_argmax(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, void* ws) {
+  (void)H;
+  (void)V_real;
+  ArgPlan p{};
+  p.S = V_pad / n;
+  p.tiles_per_seg = tiles_per_shard(p.S);
+  p.tiles_m = p.tiles_per_seg * n;
+  p.tiles_n = cdiv(T, kTileN);
+  Carve c(ws);
+  p.val = c.take<float>(static_cast<size_t>(p.tiles_m * T));
+  p.idx = c.take<int32_t>(static_cast<size_t>(p.tiles_m * T));
+  p.bytes = c.used;
+  return p;
+}
+
 BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, size_t esize,
                  void* ws) {
   (void)H;
@@ -177,6 +192,58 @@ __global__ __launch_bounds__(256) void k_ce_finalize(const float* __restrict__ p
   }
 }
 
+// (v, i) beats (bv, bi): a larger value, or an equal value at a lower index
+// (-1 marks "no row"). A total order, so any merge order gives one result.
+__device__ __forceinline__ void argmax_merge(float& bv, int32_t& bi, float v, int32_t i) {
+  if (v > bv || (v == bv && i >= 0 && (bi < 0 || i < bi))) {
+    bv = v;
+    bi = i;
+  }
+}
+
+// Per token: the tile reports of each shard merged into the shard's report
+// (what one rank would hold), then the shard reports into the global argmax.
+// 32 tokens per workgroup, 8 lane groups over every 8th tile of a shard.
+__global__ __launch_bounds__(256) void k_argmax_merge(
+    const float* __restrict__ val, const int32_t* __restrict__ idx, int64_t T, int32_t n_seg,
+    int64_t tiles_per_seg, int32_t* __restrict__ index, float* __restrict__ value,
+    float* __restrict__ shard_value, int32_t* __restrict__ shard_index) {
+  constexpr int NSUB = 256 / kMergeTok;
+  __shared__ float rv[NSUB][kMergeTok];
+  __shared__ int32_t ri[NSUB][kMergeTok];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tok = lane & (kMergeTok - 1);
+  const int sub = wave * 2 + (lane >> 5);
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kMergeTok + tok;
+  const bool tin = t < T;
+  float gv = -INFINITY;
+  int32_t gi = -1;
+  for (int32_t k = 0; k < n_seg; ++k) {
+    float bv = -INFINITY;
+    int32_t bi = -1;
+    if (tin) {
+      const int64_t base = static_cast<int64_t>(k) * tiles_per_seg * T + t;
+      for (int64_t j = sub; j < tiles_per_seg; j += NSUB)
+        argmax_merge(bv, bi, val[base + j * T], idx[base + j * T]);
+    }
+    rv[sub][tok] = bv;
+    ri[sub][tok] = bi;
+    __syncthreads();
+    if (sub == 0 && tin) {
+#pragma unroll
+      for (int w = 1; w < NSUB; ++w) argmax_merge(bv, bi, rv[w][tok], ri[w][tok]);
+      if (shard_value) shard_value[static_cast<int64_t>(k) * T + t] = bv;
+      if (shard_index) shard_index[static_cast<int64_t>(k) * T + t] = bi;
+      argmax_merge(gv, gi, bv, bi);
+    }
+    __syncthreads();
+  }
+  if (sub == 0 && tin) {
+    index[t] = gi;
+    value[t] = gv;
+  }
+}
+
 __global__ void k_fill_scalars(float* f0, int32_t* i0, int32_t* i1) {
   if (threadIdx.x == 0) {
     if (f0) *f0 = 0.0f;
@@ -222,7 +289,8 @@ struct Staging {
 };
 template <int MODE, bool AKM, bool BKM>
 constexpr Staging staging() {
-  if constexpr (MODE == EPI_FWD) return {VCE_FWD_RB, VCE_FWD_NS, VCE_FWD_SPREAD != 0};
+  if constexpr (MODE == EPI_FWD || MODE == EPI_ARGMAX)
+    return {VCE_FWD_RB, VCE_FWD_NS, VCE_FWD_SPREAD != 0};
   else if constexpr (MODE == EPI_GRAD) return {VCE_GRAD_RB, VCE_GRAD_NS, VCE_GRAD_SPREAD != 0};
   else if constexpr (!AKM) return {VCE_DH_RB, VCE_DH_NS, VCE_DH_SPREAD != 0};
   else return {VCE_DW_RB, VCE_DW_NS, VCE_DW_SPREAD != 0};
@@ -281,6 +349,40 @@ hipError_t run_ce_fwd(const void* h, const void* W, const int32_t* targets, int6
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(k_ce_finalize, dim3(1), dim3(256), 0, s, p.part_loss, p.part_nv, p.part_nb,
                      p.merge_blocks, loss_sum, n_valid, n_bad);
+  return hipGetLastError();
+}
+
+hipError_t run_argmax(const void* h, const void* W, int64_t T, int64_t H, int64_t V_real,
+                      int64_t V_pad, int32_t n, bool bf16, int32_t* index, float* value,
+                      float* shard_value, int32_t* shard_index, const ArgPlan& p,
+                      hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  GemmShape g{};
+  g.A = W;
+  g.lda = H;
+  g.B = h;
+  g.ldb = H;
+  g.seg_len = p.S;
+  g.n_seg = n;
+  g.tiles_per_seg = static_cast<int32_t>(p.tiles_per_seg);
+  g.m_total = V_pad;
+  g.m_load_end = V_real;
+  g.n_total = T;
+  g.tiles_n = static_cast<int32_t>(p.tiles_n);
+  g.k_splits = 1;
+  g.k_total = H;
+  g.k_per_split = round_up(H, kPadK);
+  g.group_m = 8;
+  EpiArgs e{};
+  e.arg.T = T;
+  e.arg.val = p.val;
+  e.arg.idx = p.idx;
+  hipError_t err =
+      bf16 ? launch_gemm<uint16_t, EPI_ARGMAX>(g, e, s) : launch_gemm<float, EPI_ARGMAX>(g, e, s);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_argmax_merge, dim3(static_cast<uint32_t>(cdiv(T, kMergeTok))), dim3(256), 0,
+                     s, p.val, p.idx, T, n, p.tiles_per_seg, index, value, shard_value,
+                     shard_index);
   return hipGetLastError();
 }
 

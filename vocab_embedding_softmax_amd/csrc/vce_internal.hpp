@@ -104,6 +104,16 @@ struct FwdPlan {
 };
 FwdPlan plan_fwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, void* ws);
 
+// Greedy argmax plan: per-tile reports (largest logit, its row) of every
+// vocabulary tile of every shard, [tiles_m][T] each.
+struct ArgPlan {
+  int64_t S, tiles_per_seg, tiles_m, tiles_n;
+  float* val;
+  int32_t* idx;
+  size_t bytes;
+};
+ArgPlan plan_argmax(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, void* ws);
+
 // Backward plan: the vocabulary is processed in chunks (a shard, or a piece
 // of one when shards are large); only one chunk's G = [T][chunk] is staged.
 struct BwdPlan {
@@ -175,6 +185,10 @@ hipError_t run_ce_bwd(const void* h, const void* W, const int32_t* targets, cons
                       int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, bool bf16,
                       float* dh, float* dW, int32_t accumulate, const BwdPlan& p, hipStream_t s,
                       void* const* events);
+
+hipError_t run_argmax(const void* h, const void* W, int64_t T, int64_t H, int64_t V_real,
+                      int64_t V_pad, int32_t n, bool bf16, int32_t* index, float* value,
+                      float* shard_value, int32_t* shard_index, const ArgPlan& p, hipStream_t s);
 
 hipError_t run_emb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, int64_t V_real,
                        int64_t V_pad, int32_t n, size_t esize, void* out, int32_t* n_bad,
