@@ -121,11 +121,13 @@ vce_status vce_fwd(const void* h, const void* W, const int32_t* targets,
  * accumulate_dW = 0: every row of dW is written (rows >= V_real get 0);     *
  * accumulate_dW = 1: G^T h is added into rows < V_real, rows >= V_real are  *
  * left unchanged. lse must be the forward's output for the same inputs.     *
- * The vocabulary is processed in chunks (each shard, cut into pieces of at *
- * most 32768 rows): G of one chunk ([T][chunk], never [T][V]) is staged in  *
- * the workspace in the input element type (bf16 rounded to nearest-even,    *
- * or float32), then dh receives G_chunk W_chunk (in chunk order) and the    *
- * chunk's rows of dW receive G_chunk^T h.                                   *
+ * The vocabulary is processed in chunks: at least two once V_pad spans two *
+ * 256-row tiles, each at most 131072 rows; equal groups of whole shards     *
+ * when shards fit, else every shard cut into tile-aligned pieces. G of one  *
+ * chunk ([T][chunk], never [T][V]) is staged in the workspace in the input  *
+ * element type (bf16 rounded to nearest-even, or float32), then dh receives *
+ * G_chunk W_chunk (in chunk order) and the chunk's rows of dW receive       *
+ * G_chunk^T h.                                                              *
  * ------------------------------------------------------------------------ */
 size_t vce_bwd_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
                                int32_t num_shards, vce_dtype dt);

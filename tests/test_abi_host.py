@@ -137,18 +137,25 @@ def test_candidates_argument_errors():
 def test_workspace_queries_are_deterministic_and_reject_bad_shapes():
     a = lib.vce_bwd_workspace_bytes(8192, 3072, 201088, 201088, 8, 1)
     b = lib.vce_bwd_workspace_bytes(8192, 3072, 201088, 201088, 8, 1)
-    # one chunk of G (a shard: 25136 columns, padded to 25152) is staged, never [T, V]
-    assert a == b == 8192 * 25152 * 2
-    assert lib.vce_bwd_workspace_bytes(8192, 3072, 201088, 201088, 1, 1) < 8192 * 32768 * 2
+    # one chunk of G (four shards: 100544 columns) is staged, never [T, V]
+    assert a == b == 8192 * 100544 * 2
+    # one shard of 201088 rows: two tile-aligned pieces of 100608 rows
+    assert lib.vce_bwd_workspace_bytes(8192, 3072, 201088, 201088, 1, 1) == 8192 * 100608 * 2
+    # a table of two tiles or more is never staged whole
+    for T, H, Vr, Vp, n in ((64, 64, 1000, 1024, 4), (2048, 1024, 50000, 50016, 8),
+                            (300, 72, 1001, 1002, 1)):
+        assert lib.vce_bwd_workspace_bytes(T, H, Vr, Vp, n, 1) < T * Vp * 2
     assert lib.vce_fwd_workspace_bytes(8, 64, 100, 101, 2, 1) == 0  # 101 % 2 != 0
     assert lib.vce_bwd_workspace_bytes(8, 64, 100, 128, 4, 3) == 0  # bad dtype
 
 
 def test_bwd_event_count_and_timed_checks():
-    # 8 shards of 25136 rows: one chunk per shard
-    assert lib.vce_bwd_event_count(16384, 3072, 201088, 201088, 8, 1) == 1 + 3 * 8
-    # one shard of 201088 rows: pieces of at most 32768 rows
-    assert lib.vce_bwd_event_count(16384, 3072, 201088, 201088, 1, 1) == 1 + 3 * 7
+    # 8 shards of 25136 rows: two chunks of four shards
+    assert lib.vce_bwd_event_count(16384, 3072, 201088, 201088, 8, 1) == 1 + 3 * 2
+    # one shard of 201088 rows: two pieces
+    assert lib.vce_bwd_event_count(16384, 3072, 201088, 201088, 1, 1) == 1 + 3 * 2
+    # a table narrower than two tiles: one chunk
+    assert lib.vce_bwd_event_count(8, 64, 300, 300, 3, 1) == 1 + 3 * 1
     assert lib.vce_bwd_event_count(8, 64, 100, 101, 2, 1) == 0      # 101 % 2 != 0
     ev = (ctypes.c_void_p * 3)()
     args = (A, B, C, A, C, A, 0, 4, 64, 1000, 1024, 4, -100, 1, A, B, 0, A, 1 << 40, None)

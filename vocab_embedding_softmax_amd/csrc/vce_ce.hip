@@ -65,11 +65,27 @@ BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
   (void)V_real;
   BwdPlan p{};
   p.S = V_pad / n;
-  // chunks of at most about kChunkRows rows, tile-aligned inside the shard
-  p.piece_rows = min(p.S, round_up(cdiv(p.S, cdiv(p.S, kChunkRows)), kTileM));
-  p.pieces = cdiv(p.S, p.piece_rows);
-  p.n_chunks = p.pieces * n;
-  p.ldC = round_up(p.piece_rows, kPadK);
+  p.n = n;
+  // At least two chunks once the table spans two tiles (G is never staged for
+  // the whole vocabulary), more when a chunk would pass kChunkRows rows.
+  // Whole shards are grouped into equal chunks when they fit; otherwise
+  // every shard is cut into tile-aligned pieces.
+  const int64_t want = V_pad >= 2 * kTileM ? max(int64_t{2}, cdiv(V_pad, kChunkRows)) : 1;
+  if (want <= n) {
+    p.group = cdiv(n, want);
+    p.n_chunks = cdiv(n, p.group);
+    p.pieces = 1;
+    p.piece_rows = p.S;
+    p.chunk_rows = p.group * p.S;
+  } else {
+    p.group = 0;
+    const int64_t per = cdiv(want, n);
+    p.piece_rows = min(p.S, round_up(cdiv(p.S, per), kTileM));
+    p.pieces = cdiv(p.S, p.piece_rows);
+    p.n_chunks = p.pieces * n;
+    p.chunk_rows = p.piece_rows;
+  }
+  p.ldC = round_up(p.chunk_rows, kPadK);
   p.esize = esize;
   Carve c(ws);
   p.G = c.take<char>(static_cast<size_t>(T * p.ldC) * esize);

@@ -26,7 +26,7 @@ constexpr int kTileM = VCE_TILE_M;  // GEMM tile rows (M side)
 constexpr int kTileN = VCE_TILE_N;  // GEMM tile columns (N side)
 constexpr int kOcc = VCE_OCC;       // workgroups resident per CU (waves per SIMD)
 #ifndef VCE_CHUNK_ROWS
-#define VCE_CHUNK_ROWS 32768
+#define VCE_CHUNK_ROWS 131072
 #endif
 // K staging per GEMM (bytes per position per K slice, LDS stages, spread
 // issue of a slice's loads). Measured on the tied-step shapes: the forward
@@ -114,18 +114,27 @@ struct ArgPlan {
 };
 ArgPlan plan_argmax(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, void* ws);
 
-// Backward plan: the vocabulary is processed in chunks (a shard, or a piece
-// of one when shards are large); only one chunk's G = [T][chunk] is staged.
+// Backward plan: the vocabulary is processed in chunks; only one chunk's
+// G = [T][chunk] is staged. A chunk is a group of whole shards, or a piece of
+// one shard when shards are larger than a chunk may be.
 struct BwdPlan {
   int64_t S;                 // rows per shard
-  int64_t pieces;            // chunks per shard
-  int64_t piece_rows;        // rows per chunk (the last chunk of a shard may be shorter)
-  int64_t n_chunks;          // pieces * num_shards
+  int64_t n;                 // shards
+  int64_t group;             // shards per chunk (0: chunks are pieces of a shard)
+  int64_t pieces;            // chunks per shard (pieces)
+  int64_t piece_rows;        // rows per piece (the last piece of a shard may be shorter)
+  int64_t chunk_rows;        // most rows of a chunk
+  int64_t n_chunks;
   int64_t ldC;               // leading dimension of the staged G chunk
   size_t esize;
   void* G;                   // [T][ldC]
   size_t bytes;
   void chunk(int64_t c, int64_t& c0, int64_t& c1) const {
+    if (group > 0) {
+      c0 = c * group * S;
+      c1 = (c + 1) * group < n ? (c + 1) * group * S : n * S;
+      return;
+    }
     const int64_t k = c / pieces, j = c % pieces;
     c0 = k * S + j * piece_rows;
     c1 = (k + 1) * S < c0 + piece_rows ? (k + 1) * S : c0 + piece_rows;
