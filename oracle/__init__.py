@@ -28,3 +28,4 @@ from .ce import (  # noqa: F401
 from .sampled import candidates, sampled_step  # noqa: F401
 from .argmax import shard_argmax, merge_shard_argmax, greedy_argmax  # noqa: F401
 from .tied import tied_step  # noqa: F401
+from .oth import OT_H_WEIGHT, ot_h_step  # noqa: F401

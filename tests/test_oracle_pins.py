@@ -530,3 +530,42 @@ def test_argmax_sharded_equals_unsharded(n):
     assert np.array_equal(z[np.arange(z.shape[0]), r["index"]], r["value"])
     one = oracle.greedy_argmax(h, W, inp.V_real, inp.V_pad, 1)
     assert np.array_equal(r["index"], one["index"])
+
+
+# ------------------------------------------------------------------ OT-H step
+
+def test_ot_h_step_finite_difference():
+    """Central differences of the OT-H loss in every entry of W and W2 equal
+    the step's dW and dW2; the first head's loss plus 0.1 times the second's."""
+    rng = np.random.default_rng(14)
+    T, H, V_real, V_pad, n = 6, 3, 6, 8, 2
+    W = rng.standard_normal((V_pad, H))
+    W2 = rng.standard_normal((V_pad, H))
+    tokens = np.array([2, 2, 7, 5, 1, 3, 0, 4])   # a repeat, a padded ID
+    ids = tokens[:T].copy()
+    ids[4] = -3                                    # an out-of-range ID
+    y1 = tokens[1:T + 1].copy()
+    y1[2] = -100                                   # ignored in the first head only
+    y2 = tokens[2:T + 1].copy()
+    y2[0] = 7                                      # a padded class: a bad target
+    r = oracle.ot_h_step(ids, y1, y2, W, W2, V_real, V_pad, n)
+
+    def loss_of(Wx, W2x):
+        hx = oracle.gather_direct(ids, Wx, V_real)
+        return (_loss_mean(hx, Wx, y1, V_real, V_pad, n) +
+                0.1 * _loss_mean(hx[:T - 1], W2x, y2, V_real, V_pad, n))
+
+    assert abs(loss_of(W, W2) - r["loss"]) < 1e-12
+    eps = 1e-6
+    for v in range(V_pad):
+        for j in range(H):
+            for which, G in ((0, r["dW"]), (1, r["dW2"])):
+                P = [W.copy(), W2.copy()]
+                M = [W.copy(), W2.copy()]
+                P[which][v, j] += eps
+                M[which][v, j] -= eps
+                num = (loss_of(*P) - loss_of(*M)) / (2 * eps)
+                assert abs(num - G[v, j]) < 1e-8, (which, v, j, num, G[v, j])
+    # the second head never sees the last row, and its padded rows stay zero
+    assert not r["dW2"][V_real:].any()
+    assert r["f2"]["n_bad"] == 1
