@@ -315,6 +315,34 @@ def main():
                      "achieved_TFLOP_s": flop_gemm / (ms_arg * 1e-3) / 1e12,
                      "frac": flop_gemm / (ms_arg * 1e-3) / PEAK_BF16}
     log(f"[bench] argmax {ms_arg:.3f} ms/call")
+    if tied:
+        # OT-H step: the tied step plus a second, untied head two tokens ahead
+        # at weight 0.1 (its own table of the same shape, drawn on the device:
+        # only its timing is used here); flops = 8*H*V_real*(T + T - 1).
+        g = torch.Generator(device=dev)
+        g.manual_seed(7)
+        W2 = (torch.randn(Vp, H, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+        tg2 = tg[1:].contiguous()
+        ws2 = V.Workspaces(dev, fwd=V.vce_fwd_workspace_bytes(T - 1, H, Vr, Vp, n, dt_code),
+                           bwd=V.vce_bwd_workspace_bytes(T - 1, H, Vr, Vp, n, dt_code))
+        dW2 = torch.empty(Vp, H, **f32)
+
+        def oth():
+            V.ot_h_step(ids, tg, tg2, W, W2, Vr, n, inp.ignore_index, ws=ws, ws2=ws2, h=h,
+                        dh=dh, dW=dW, dW2=dW2)
+
+        oth()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            oth()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_oth = e0.elapsed_time(e1) / reps
+        res["ot_h_step"] = {"ms": ms_oth, "tokens_s": T / (ms_oth * 1e-3),
+                            "mfma_frac": 8.0 * H * Vr * (2 * T - 1) / (ms_oth * 1e-3) / PEAK_BF16}
+        log(f"[bench] OT-H step {ms_oth:.3f} ms")
+        del W2, ws2, dW2
     if a.copy_probe:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

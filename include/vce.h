@@ -62,6 +62,9 @@ typedef enum { VCE_F32 = 0, VCE_BF16 = 1 } vce_dtype;
 
 typedef enum { VCE_REDUCE_MEAN = 0, VCE_REDUCE_SUM = 1 } vce_reduction;
 
+/* Flags of vce_bwd's `accumulate` argument. */
+enum { VCE_ACC_DW = 1, VCE_ACC_DH = 2 };
+
 /* Version of this interface (changes when a signature changes). */
 int32_t vce_abi_version(void);
 
@@ -113,14 +116,17 @@ vce_status vce_fwd(const void* h, const void* W, const int32_t* targets,
  * tile by tile (never stored whole) to form                                 *
  *   G[t,v] = scale * (exp(z[t,v] - lse[t]) - [v == y_t])                    *
  * for valid targets and real rows, else exactly 0, and then                 *
- *   dh = G W        (overwritten, [T,H] float32)                            *
+ *   dh = G W        ([T,H] float32; see accumulate)                         *
  *   dW = G^T h      (rows < V_real; [V_pad,H] float32)                      *
  * scale = grad_loss[0] / max(n_valid[0], 1) for VCE_REDUCE_MEAN ([SP]       *
  * paragraph 3: one average over the valid tokens) or grad_loss[0] for       *
  * VCE_REDUCE_SUM; both scalars are read on the device (no host sync).       *
- * accumulate_dW = 0: every row of dW is written (rows >= V_real get 0);     *
- * accumulate_dW = 1: G^T h is added into rows < V_real, rows >= V_real are  *
- * left unchanged. lse must be the forward's output for the same inputs.     *
+ * accumulate: a set of VCE_ACC_* flags. Without VCE_ACC_DW every row of   *
+ * dW is written (rows >= V_real get 0); with it G^T h is added into rows   *
+ * < V_real and rows >= V_real are left unchanged. Without VCE_ACC_DH dh is *
+ * overwritten; with it G W is added into dh (a second head's gradient on   *
+ * the same hidden rows, [SS] Setup, OT-H). Other bits: VCE_ERR_DTYPE.      *
+ * lse must be the forward's output for the same inputs.                    *
  * The vocabulary is processed in chunks: at least two once V_pad spans two *
  * 256-row tiles, each at most 131072 rows; equal groups of whole shards     *
  * when shards fit, else every shard cut into tile-aligned pieces. G of one  *
@@ -136,7 +142,7 @@ vce_status vce_bwd(const void* h, const void* W, const int32_t* targets, const f
                    const float* grad_loss, const int32_t* n_valid, vce_reduction red,
                    int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
                    int32_t num_shards, int32_t ignore_index, vce_dtype dt,
-                   float* dh, float* dW, int32_t accumulate_dW,
+                   float* dh, float* dW, int32_t accumulate,
                    void* ws, size_t ws_bytes, void* stream);
 
 /* Number of events vce_bwd_timed records for these arguments:
@@ -154,7 +160,7 @@ vce_status vce_bwd_timed(const void* h, const void* W, const int32_t* targets, c
                          const float* grad_loss, const int32_t* n_valid, vce_reduction red,
                          int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
                          int32_t num_shards, int32_t ignore_index, vce_dtype dt,
-                         float* dh, float* dW, int32_t accumulate_dW,
+                         float* dh, float* dW, int32_t accumulate,
                          void* ws, size_t ws_bytes, void* stream, void* const* events,
                          int64_t n_events);
 

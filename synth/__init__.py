@@ -14,6 +14,7 @@ from .gen import (  # noqa: F401
     CEInputs,
     make_ce_inputs,
     make_tied_inputs,
+    make_oth_inputs,
     make_sampled_inputs,
 )
 from .configs import CONFIGS, config_inputs  # noqa: F401

@@ -245,6 +245,19 @@ def make_tied_inputs(T: int, H: int, V_real: int, V_pad: int, num_shards: int,
                     targets=tgt.astype(np.int32), ids=ids.astype(np.int32), name=name)
 
 
+def make_oth_inputs(T: int, H: int, V_real: int, V_pad: int, num_shards: int,
+                    dtype: str = "bf16", seed: int = 0, **kw):
+    """The tied-step inputs (make_tied_inputs, same arguments and draws) plus,
+    for the second head of the OT-H step, its table W2 (same distribution and
+    geometry, its own stream) and its targets: the tokens two positions ahead
+    of rows 0..T-2, i.e. targets[1:] of the tied step.
+    Returns (CEInputs, W2, targets2)."""
+    inp = make_tied_inputs(T, H, V_real, V_pad, num_shards, dtype, seed, **kw)
+    rs = _streams(seed)
+    W2 = _table(rs[_S_SPARE], V_real, V_pad, H, kw.get("w_std", 0.02), dtype, kw.get("pad_fill"))
+    return inp, W2, inp.targets[1:].copy()
+
+
 def make_sampled_inputs(T: int, H: int, V: int, P: int, dtype: str = "bf16",
                         seed: int = 0, *, zipf_s: float = 1.1, ignore_frac: float = 0.0,
                         ignore_index: int = -100, w_std: float = 0.02,

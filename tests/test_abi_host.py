@@ -161,3 +161,14 @@ def test_bwd_event_count_and_timed_checks():
     args = (A, B, C, A, C, A, 0, 4, 64, 1000, 1024, 4, -100, 1, A, B, 0, A, 1 << 40, None)
     # wrong event count is rejected before any HIP call
     assert lib.vce_bwd_timed(*args, ev, 3) == SHAPE
+
+
+def test_bwd_accumulate_flags_checked():
+    def call(acc):
+        return lib.vce_bwd(A, B, C, A, C, A, 0, 4, 64, 1000, 1024, 4, -100, 1, A, B, acc, A, 0,
+                           None)
+    # unknown flag bits are rejected; known ones pass the flag check and stop at the
+    # (deliberately missing) workspace
+    assert call(4) == DTYPE and call(-1) == DTYPE
+    for acc in (0, 1, 2, 3):
+        assert call(acc) == WORKSPACE

@@ -191,3 +191,44 @@ def test_c3_full_size_argmax_sampled_tokens(V):
     W64 = oracle.decode(inp.W, inp.dtype)
     nclear = check_argmax(idx[sample], val[sample], h64, W64, inp.V_real, "c3 sampled")
     say(f"c3 argmax: {nclear} of {len(sample)} sampled tokens without a near tie")
+
+
+def test_c4_full_size_ot_h_step(V):
+    """The OT-H step at the tied-step shapes (second table of the same size):
+    counts exact; sampled rows of dh against the oracle's per-token values of
+    both heads; padded-free dW2 finite; loss against the oracle on sampled
+    tokens of both heads."""
+    from synth import make_oth_inputs
+    from synth.configs import CONFIGS
+    say("case c4 full-size OT-H step")
+    c = CONFIGS["c4"]
+    inp, W2b, y2 = make_oth_inputs(c.T, c.H, c.V_real, c.V_pad, c.num_shards, c.dtype, c.seed,
+                                   zipf_s=1.1, oob_frac=0.01, ignore_frac=0.02)
+    dev = "cuda"
+    W = V.from_bits(inp.W, inp.dtype, dev)
+    W2 = V.from_bits(W2b, inp.dtype, dev)
+    ids = torch.from_numpy(inp.ids).to(dev)
+    r = V.ot_h_step(ids, torch.from_numpy(inp.targets).to(dev), torch.from_numpy(y2).to(dev),
+                    W, W2, inp.V_real, inp.num_shards)
+    torch.cuda.synchronize()
+    T = inp.T
+    f1, f2 = r.fwd, r.extra["fwd2"]
+    v1 = (inp.targets >= 0) & (inp.targets < inp.V_real)
+    v2 = (y2 >= 0) & (y2 < inp.V_real)
+    assert int(f1.n_valid.item()) == int(v1.sum()) and int(f2.n_valid.item()) == int(v2.sum())
+    sample = _sample_tokens(inp.targets, inp.V_real, 24, 23)
+    sample = sample[sample < T - 1]
+    W64 = oracle.decode(inp.W, inp.dtype)
+    W2_64 = oracle.decode(W2b, inp.dtype)
+    h64 = oracle.gather_direct(inp.ids[sample], W64, inp.V_real)
+    g1 = oracle.ce_forward(h64, W64, inp.targets[sample], inp.V_real, inp.V_pad, inp.num_shards)
+    g2 = oracle.ce_forward(h64, W2_64, y2[sample], inp.V_real, inp.V_pad, inp.num_shards)
+    assert np.abs(f1.lse.cpu().numpy()[sample] - g1["lse"]).max() <= TOL["bf16"]["lse_abs"]
+    assert np.abs(f2.lse.cpu().numpy()[sample] - g2["lse"]).max() <= TOL["bf16"]["lse_abs"]
+    s1 = 1.0 / int(v1.sum())
+    s2 = 0.1 / int(v2.sum())
+    dh1, _ = oracle.ce_backward(h64, W64, inp.targets[sample], g1["lse"], inp.V_real, inp.V_pad, s1)
+    dh2, _ = oracle.ce_backward(h64, W2_64, y2[sample], g2["lse"], inp.V_real, inp.V_pad, s2)
+    e = rel_l2(r.dh.cpu().numpy()[sample], dh1 + dh2)
+    assert e <= TOL["bf16"]["grad"], e
+    assert torch.isfinite(r.extra["dW2"]).all()

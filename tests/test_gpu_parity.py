@@ -304,6 +304,48 @@ def test_tied_step_small(V):
     check_ce(g, ref, "bf16", inp.V_real)
 
 
+@pytest.mark.parametrize("dt,T,H,Vr,Vp,n", [("f32", 64, 64, 1000, 1024, 4),
+                                              ("bf16", 1024, 256, 8000, 8192, 8)])
+def test_ot_h_step(V, dt, T, H, Vr, Vp, n):
+    """Tied step plus the untied second head (two tokens ahead, weight 0.1):
+    both losses, the summed dh, dW (head 1 + scatter of the summed dh) and dW2."""
+    from synth import make_oth_inputs
+    say(f"case OT-H step {dt} T={T} H={H} V={Vr}/{Vp} n={n}")
+    inp, W2b, y2 = make_oth_inputs(T, H, Vr, Vp, n, dt, seed=T + 7)
+    dev = "cuda"
+    W = V.from_bits(inp.W, dt, dev)
+    W2 = V.from_bits(W2b, dt, dev)
+    r = V.ot_h_step(torch.from_numpy(inp.ids).to(dev), torch.from_numpy(inp.targets).to(dev),
+                    torch.from_numpy(y2).to(dev), W, W2, Vr, n)
+    torch.cuda.synchronize()
+    ref = oracle.ot_h_step(inp.ids, inp.targets, y2, oracle.decode(inp.W, dt),
+                           oracle.decode(W2b, dt), Vr, Vp, n)
+    tol = TOL[dt]
+    f1, f2 = r.fwd, r.extra["fwd2"]
+    for f, rf in ((f1, ref["f1"]), (f2, ref["f2"])):
+        assert int(f.n_valid.item()) == rf["n_valid"] and int(f.n_bad.item()) == rf["n_bad"]
+        dl = abs(float(f.loss_sum.item()) - rf["loss_sum"]) / abs(rf["loss_sum"])
+        assert dl <= tol["loss"], dl
+        lse = f.lse.cpu().numpy().astype(np.float64)
+        if tol["lse_abs"] is not None:
+            assert np.abs(lse - rf["lse"]).max() <= tol["lse_abs"]
+        else:
+            assert (np.abs(lse - rf["lse"]) / np.abs(rf["lse"])).max() <= tol["lse_rel"]
+    for name, got, want in (("dh", r.dh, ref["dh"]), ("dW", r.dW, ref["dW"]),
+                            ("dW2", r.extra["dW2"], ref["dW2"])):
+        e = rel_l2(got.cpu().numpy(), want)
+        assert e <= tol["grad"], (name, e)
+    assert not r.extra["dW2"][Vr:].cpu().numpy().any()
+    # the second head's share of dh alone: run the first head only and compare
+    r1 = V.tied_step(torch.from_numpy(inp.ids).to(dev), torch.from_numpy(inp.targets).to(dev),
+                     W, Vr, n)
+    d2 = (r.dh - r1.dh).cpu().numpy()
+    want2 = ref["dh"] - oracle.tied_step(inp.ids, inp.targets, oracle.decode(inp.W, dt), Vr, Vp,
+                                         n)["dh"]
+    assert rel_l2(d2[:T - 1], want2[:T - 1]) <= 5 * tol["grad"]
+    assert not d2[T - 1].any()
+
+
 # ------------------------------------------------------------------ sampled softmax
 
 def test_candidates_bit_exact(V):

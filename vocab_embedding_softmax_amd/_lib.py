@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libvce.so")
 
 VCE_F32, VCE_BF16 = 0, 1
 REDUCE_MEAN, REDUCE_SUM = 0, 1
+ACC_DW, ACC_DH = 1, 2   # flags of vce_bwd's accumulate argument
 
 STATUS = {0: "VCE_OK", 1: "VCE_ERR_NULL", 2: "VCE_ERR_SHAPE", 3: "VCE_ERR_SHARD",
           4: "VCE_ERR_DTYPE", 5: "VCE_ERR_ALIGN", 6: "VCE_ERR_WORKSPACE", 7: "VCE_ERR_HIP"}
@@ -185,9 +186,10 @@ def vce_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.
             grad_loss: torch.Tensor, n_valid: torch.Tensor, V_real: int, num_shards: int,
             ignore_index: int = -100, reduction: int = REDUCE_MEAN, *,
             dh: Optional[torch.Tensor] = None, dW: Optional[torch.Tensor] = None,
-            accumulate_dW: bool = False, ws: Optional[torch.Tensor] = None,
-            stream=None, events=None) -> BwdOut:
-    """Cross-entropy backward: dh [T,H] and dW [V_pad,H] (float32). `events`
+            accumulate_dW: bool = False, accumulate_dh: bool = False,
+            ws: Optional[torch.Tensor] = None, stream=None, events=None) -> BwdOut:
+    """Cross-entropy backward: dh [T,H] and dW [V_pad,H] (float32), overwritten
+    or (accumulate_dW / accumulate_dh) added into. `events`
     (optional): vce_bwd_event_count(...) torch.cuda.Event objects, recorded
     before the first kernel and after each vocabulary chunk's G, dh and dW
     kernels (calls vce_bwd_timed)."""
@@ -201,6 +203,8 @@ def vce_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.
     _need(grad_loss, "grad_loss", torch.float32)
     _need(n_valid, "n_valid", torch.int32)
     dev = h.device
+    if (accumulate_dh and dh is None) or (accumulate_dW and dW is None):
+        raise ValueError("accumulating needs the tensor to add into")
     if dh is None:
         dh = torch.empty(T, H, dtype=torch.float32, device=dev)
     if dW is None:
@@ -211,7 +215,8 @@ def vce_bwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, lse: torch.
     ws = _workspace(need, dev, ws)
     args = (_ptr(h), _ptr(W), _ptr(targets), _ptr(lse), _ptr(grad_loss), _ptr(n_valid),
             reduction, T, H, V_real, V_pad, num_shards, ignore_index, dt, _ptr(dh), _ptr(dW),
-            1 if accumulate_dW else 0, _ptr(ws), ws.numel(), _stream(stream, dev))
+            (ACC_DW if accumulate_dW else 0) | (ACC_DH if accumulate_dh else 0), _ptr(ws),
+            ws.numel(), _stream(stream, dev))
     if events is None:
         _check("vce_bwd", lib.vce_bwd(*args))
     else:

@@ -41,7 +41,7 @@ const char* vce_strerror(vce_status s) {
     case VCE_ERR_NULL: return "a required pointer is NULL";
     case VCE_ERR_SHAPE: return "invalid size argument (T, H, V_real, V_pad, P, capacity or ignore_index)";
     case VCE_ERR_SHARD: return "num_shards must be >= 1 and divide V_pad";
-    case VCE_ERR_DTYPE: return "unknown element type or reduction";
+    case VCE_ERR_DTYPE: return "unknown element type, reduction or accumulate flag";
     case VCE_ERR_ALIGN: return "pointers must be 16-byte aligned and H a multiple of 8";
     case VCE_ERR_WORKSPACE: return "workspace missing or smaller than the size query";
     case VCE_ERR_HIP: return "a HIP kernel launch failed";
@@ -106,9 +106,9 @@ vce_status vce_bwd(const void* h, const void* W, const int32_t* targets, const f
                    const float* grad_loss, const int32_t* n_valid, vce_reduction red, int64_t T,
                    int64_t H, int64_t V_real, int64_t V_pad, int32_t num_shards,
                    int32_t ignore_index, vce_dtype dt, float* dh, float* dW,
-                   int32_t accumulate_dW, void* ws, size_t ws_bytes, void* stream) {
+                   int32_t accumulate, void* ws, size_t ws_bytes, void* stream) {
   return vce_bwd_timed(h, W, targets, lse, grad_loss, n_valid, red, T, H, V_real, V_pad,
-                       num_shards, ignore_index, dt, dh, dW, accumulate_dW, ws, ws_bytes, stream,
+                       num_shards, ignore_index, dt, dh, dW, accumulate, ws, ws_bytes, stream,
                        nullptr, 0);
 }
 
@@ -123,9 +123,10 @@ vce_status vce_bwd_timed(const void* h, const void* W, const int32_t* targets, c
                          const float* grad_loss, const int32_t* n_valid, vce_reduction red,
                          int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t num_shards,
                          int32_t ignore_index, vce_dtype dt, float* dh, float* dW,
-                         int32_t accumulate_dW, void* ws, size_t ws_bytes, void* stream,
+                         int32_t accumulate, void* ws, size_t ws_bytes, void* stream,
                          void* const* events, int64_t n_events) {
   if (!dtype_ok(dt) || (red != VCE_REDUCE_MEAN && red != VCE_REDUCE_SUM)) return VCE_ERR_DTYPE;
+  if (accumulate & ~(VCE_ACC_DW | VCE_ACC_DH)) return VCE_ERR_DTYPE;
   vce_status st = check_table(T, H, V_real, V_pad, num_shards);
   if (st != VCE_OK) return st;
   if ((st = check_ignore(ignore_index, V_real)) != VCE_OK) return st;
@@ -143,7 +144,7 @@ vce_status vce_bwd_timed(const void* h, const void* W, const int32_t* targets, c
   const vce::BwdPlan p = vce::plan_bwd(T, H, V_real, V_pad, num_shards, esize_of(dt), ws);
   if (events && n_events != 1 + 3 * p.n_chunks) return VCE_ERR_SHAPE;
   return hip_status(vce::run_ce_bwd(h, W, targets, lse, grad_loss, n_valid, red, T, H, V_real,
-                                    V_pad, num_shards, dt == VCE_BF16, dh, dW, accumulate_dW ? 1 : 0,
+                                    V_pad, num_shards, dt == VCE_BF16, dh, dW, accumulate,
                                     p, static_cast<hipStream_t>(stream), events));
 }
 

@@ -410,6 +410,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
                               const BwdPlan& p, hipStream_t s, void* const* ev) {
   (void)V_pad;
   (void)n;
+  const bool acc_dw = (accumulate & 1) != 0, acc_dh = (accumulate & 2) != 0;
   hipError_t err;
   int ev_i = 0;
   auto mark = [&]() -> hipError_t {
@@ -433,7 +434,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
     const int64_t kreal = max(min(V_real - c0, Vc), int64_t{0});  // real classes in the chunk
     if (T == 0 || kreal == 0) {
       // no token, or no real class: G is zero, nothing reaches dh, the rows of dW are 0
-      if (!accumulate && (err = zero_rows(c0, c1)) != hipSuccess) return err;
+      if (!acc_dw && (err = zero_rows(c0, c1)) != hipSuccess) return err;
       for (int i = 0; i < 3; ++i)
         if ((err = mark()) != hipSuccess) return err;
       continue;
@@ -500,7 +501,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       e.store.C = dh;
       e.store.ldc = H;
       e.store.split_stride = 0;
-      e.store.accumulate = dh_written ? 1 : 0;
+      e.store.accumulate = (dh_written || acc_dh) ? 1 : 0;
       e.store.m_zero_from = T;
       if ((err = launch_gemm<E, EPI_STORE, false, true>(g, e, s)) != hipSuccess) return err;
       dh_written = true;
@@ -529,13 +530,13 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       e.store.C = dW + c0 * H;
       e.store.ldc = H;
       e.store.split_stride = 0;
-      e.store.accumulate = accumulate;
+      e.store.accumulate = acc_dw ? 1 : 0;
       e.store.m_zero_from = kreal;
       if ((err = launch_gemm<E, EPI_STORE, true, true>(g, e, s)) != hipSuccess) return err;
     }
     if ((err = mark()) != hipSuccess) return err;
   }
-  if (T > 0 && !dh_written) {
+  if (T > 0 && !dh_written && !acc_dh) {
     // no real class at all cannot happen (V_real >= 1), but keep dh defined
     const int64_t n4 = T * H / 4;
     hipLaunchKernelGGL(k_zero_f4, dim3(static_cast<uint32_t>(cdiv(n4, 256))), dim3(256), 0, s,

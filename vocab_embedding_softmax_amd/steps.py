@@ -7,6 +7,9 @@ tied_step     lookup -> cross-entropy forward/backward -> scatter-add of dh
 sampled_step  candidates -> lookup of the candidate rows -> cross-entropy over
               them -> scatter of their gradients into the full table
               ("Sampled Softmax with Over-Tokenized Transformer", Setup)
+ot_h_step     tied_step plus a second, untied head on the hidden rows but the
+              last, scored two tokens ahead and weighted 0.1 (same page, OT-H);
+              its dh is added into the first head's before the scatter
 """
 
 from __future__ import annotations
@@ -93,3 +96,30 @@ def sampled_step(h, W, targets, perm, P, ignore_index=-100, *, grad_loss=None,
                     ws=None if ws is None else ws["emb"], stream=stream)
     return StepOut(f, b.dh, dW, dict(cand=c.cand, pos=c.pos, n_unique=c.n_unique,
                                      n_cand=c.n_cand, Wc=Wc, dWc=b.dW))
+
+
+def ot_h_step(ids, targets1, targets2, W, W2, V_real, num_shards, ignore_index=-100, *,
+              weight=0.1, ws: Optional[Workspaces] = None, ws2: Optional[Workspaces] = None,
+              h=None, dh=None, dW=None, dW2=None, stream=None) -> StepOut:
+    """ids, targets1 [T]; targets2 [T - 1] (the tokens two positions ahead of
+    rows 0..T-2); W the tied table, W2 the second head's table (same shape).
+    ws2 sizes the second head's calls (T - 1 rows)."""
+    dev = W.device
+    T = ids.shape[0]
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    wgt = torch.full((1,), float(weight), dtype=torch.float32, device=dev)
+    h, n_bad_id = L.vemb_fwd(ids, W, V_real, num_shards, out=h, stream=stream)
+    f1 = L.vce_fwd(h, W, targets1, V_real, num_shards, ignore_index,
+                   ws=None if ws is None else ws["fwd"], stream=stream)
+    h2 = h[:T - 1]
+    f2 = L.vce_fwd(h2, W2, targets2, V_real, num_shards, ignore_index,
+                   ws=None if ws2 is None else ws2["fwd"], stream=stream)
+    b1 = L.vce_bwd(h, W, targets1, f1.lse, one, f1.n_valid, V_real, num_shards, ignore_index,
+                   L.REDUCE_MEAN, dh=dh, dW=dW, ws=None if ws is None else ws["bwd"],
+                   stream=stream)
+    b2 = L.vce_bwd(h2, W2, targets2, f2.lse, wgt, f2.n_valid, V_real, num_shards, ignore_index,
+                   L.REDUCE_MEAN, dh=b1.dh[:T - 1], dW=dW2, accumulate_dh=True,
+                   ws=None if ws2 is None else ws2["bwd"], stream=stream)
+    L.vemb_bwd(ids, b1.dh, V_real, W.shape[0], num_shards, dW=b1.dW, accumulate=True,
+               ws=None if ws is None else ws["emb"], stream=stream)
+    return StepOut(f1, b1.dh, b1.dW, dict(h=h, n_bad_id=n_bad_id, fwd2=f2, dW2=b2.dW))
