@@ -350,7 +350,7 @@ hipError_t run_ce_fwd(const void* h, const void* W, const int32_t* targets, int6
   g.k_splits = 1;
   g.k_total = H;
   g.k_per_split = round_up(H, kPadK);
-  g.group_m = 8;
+  g.group_m = kGroupM;
   EpiArgs e{};
   e.fwd.targets = targets;
   e.fwd.T = T;
@@ -388,7 +388,7 @@ hipError_t run_argmax(const void* h, const void* W, int64_t T, int64_t H, int64_
   g.k_splits = 1;
   g.k_total = H;
   g.k_per_split = round_up(H, kPadK);
-  g.group_m = 8;
+  g.group_m = kGroupM;
   EpiArgs e{};
   e.arg.T = T;
   e.arg.val = p.val;
@@ -463,7 +463,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       g.k_splits = 1;
       g.k_total = H;
       g.k_per_split = round_up(H, kPadK);
-      g.group_m = 8;
+      g.group_m = kGroupM;
       EpiArgs e{};
       e.grad.targets = targets;
       e.grad.lse = lse;
@@ -496,7 +496,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       g.k_splits = 1;
       g.k_total = kreal;
       g.k_per_split = round_up(kreal, kPadK);
-      g.group_m = 8;
+      g.group_m = kGroupM;
       EpiArgs e{};
       e.store.C = dh;
       e.store.ldc = H;
@@ -525,7 +525,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       g.k_splits = 1;
       g.k_total = T;
       g.k_per_split = round_up(T, kPadK);
-      g.group_m = 8;
+      g.group_m = kGroupM;
       EpiArgs e{};
       e.store.C = dW + c0 * H;
       e.store.ldc = H;
