@@ -29,3 +29,4 @@ from .sampled import candidates, sampled_step  # noqa: F401
 from .argmax import shard_argmax, merge_shard_argmax, greedy_argmax  # noqa: F401
 from .tied import tied_step  # noqa: F401
 from .oth import OT_H_WEIGHT, ot_h_step  # noqa: F401
+from .ngram import mix64, ngram_backward, ngram_embed, ngram_ids  # noqa: F401

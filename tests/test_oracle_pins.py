@@ -569,3 +569,84 @@ def test_ot_h_step_finite_difference():
     # the second head never sees the last row, and its padded rows stay zero
     assert not r["dW2"][V_real:].any()
     assert r["f2"]["n_bad"] == 1
+
+
+# ------------------------------------------------------------------ hashed n-gram embeddings
+
+def test_ngram_ids_exist_only_for_whole_valid_ngrams():
+    V_real, r2, r3 = 50, 97, 101
+    ids = np.array([3, 7, -1, 8, 9, 10, 50, 11, 12, 13, 3, 7])
+    i2, i3 = oracle.ngram_ids(ids, V_real, r2, r3)
+    ok = [(0 <= x < V_real) for x in ids]
+    for t in range(len(ids)):
+        assert (i2[t] >= 0) == (t >= 1 and ok[t - 1] and ok[t])
+        assert (i3[t] >= 0) == (t >= 2 and ok[t - 2] and ok[t - 1] and ok[t])
+    assert ((i2 >= -1) & (i2 < r2)).all() and ((i3 >= -1) & (i3 < r3)).all()
+    # the same n-gram maps to the same row wherever it occurs, and order matters
+    assert i2[1] == i2[11] and i2[1] >= 0
+    rev, _ = oracle.ngram_ids(np.array([7, 3]), V_real, r2, r3)
+    assert rev[1] != i2[1]
+
+
+def test_ngram_rows_spread_uniformly():
+    # 40000 distinct 2-grams into 64 rows: chi-square of the counts within the
+    # 1e-6 tail of its distribution (63 degrees of freedom: < 140)
+    V_real, rows = 200, 64
+    a = np.repeat(np.arange(200), 200)
+    b = np.tile(np.arange(200), 200)
+    rows_of = np.array([oracle.mix64(int(x) * V_real + int(y)) % rows for x, y in zip(a, b)])
+    counts = np.bincount(rows_of, minlength=rows)
+    expect = len(a) / rows
+    chi2 = ((counts - expect) ** 2 / expect).sum()
+    assert chi2 < 140, chi2
+    # the finaliser is a bijection on 64 bits: no collisions among distinct keys
+    keys = np.arange(1, 200001) * 1000003
+    assert len({oracle.mix64(int(k)) for k in keys}) == len(keys)
+
+
+def test_ngram_embed_bruteforce():
+    rng = np.random.default_rng(21)
+    T, H, V_real, V_pad, r2, r3 = 9, 4, 12, 16, 10, 14
+    E = rng.standard_normal((V_pad, H))
+    E[V_real:] = np.nan                      # padded unigram rows are never read
+    E2 = rng.standard_normal((r2, H))
+    E3 = rng.standard_normal((r3, H))
+    ids = np.array([1, 5, 5, 13, 2, 11, 0, -4, 6])
+    x, i2, i3 = oracle.ngram_embed(ids, E, E2, E3, V_real)
+    for t in range(T):
+        want = [0.0] * H
+        if 0 <= ids[t] < V_real:
+            want = [w + e for w, e in zip(want, E[ids[t]])]
+        if i2[t] >= 0:
+            want = [w + e for w, e in zip(want, E2[i2[t]])]
+        if i3[t] >= 0:
+            want = [w + e for w, e in zip(want, E3[i3[t]])]
+        assert np.allclose(x[t], want, rtol=0, atol=1e-15)
+    assert not np.isnan(x).any()
+
+
+def test_ngram_backward_finite_difference():
+    rng = np.random.default_rng(22)
+    T, H, V_real, V_pad, r2, r3 = 8, 3, 6, 8, 5, 7
+    E = rng.standard_normal((V_pad, H))
+    E2 = rng.standard_normal((r2, H))
+    E3 = rng.standard_normal((r3, H))
+    ids = np.array([1, 2, 1, 2, 7, 3, 1, 2])   # repeated n-grams, a padded ID
+    c = rng.standard_normal((T, H))
+
+    def loss(E_, E2_, E3_):
+        x, _, _ = oracle.ngram_embed(ids, E_, E2_, E3_, V_real)
+        return 0.5 * float((c * x * x).sum())
+
+    x, _, _ = oracle.ngram_embed(ids, E, E2, E3, V_real)
+    dE, dE2, dE3 = oracle.ngram_backward(ids, c * x, V_real, V_pad, r2, r3)
+    eps = 1e-6
+    for which, (tab, grad) in enumerate(((E, dE), (E2, dE2), (E3, dE3))):
+        for v in range(tab.shape[0]):
+            for j in range(H):
+                args_p = [E.copy(), E2.copy(), E3.copy()]
+                args_m = [E.copy(), E2.copy(), E3.copy()]
+                args_p[which][v, j] += eps
+                args_m[which][v, j] -= eps
+                num = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+                assert abs(num - grad[v, j]) < 1e-7, (which, v, j)
