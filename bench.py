@@ -343,6 +343,42 @@ def main():
                             "mfma_frac": 8.0 * H * Vr * (2 * T - 1) / (ms_oth * 1e-3) / PEAK_BF16}
         log(f"[bench] OT-H step {ms_oth:.3f} ms")
         del W2, ws2, dW2
+
+        # Hashed n-gram input embedding (OT input side) over the same IDs, with
+        # two 2^20-row n-gram tables (the pages' tables are billions of
+        # parameters); table contents do not change the time of a gather, so
+        # the n-gram tables are left uninitialised. Forward bytes: the distinct
+        # rows of the three tables read once, the output written once.
+        rows_ng = 1 << 20
+        E2 = torch.empty(rows_ng, H, dtype=torch.bfloat16, device=dev)
+        E3 = torch.empty(rows_ng, H, dtype=torch.bfloat16, device=dev)
+        ng = V.vngram_fwd(ids, W, E2, E3, Vr, n)
+        # distinct rows touched, counted from the rows the kernel reported
+        i2 = ng.ids2.cpu().numpy()
+        i3 = ng.ids3.cpu().numpy()
+        u2 = int(np.unique(i2[i2 >= 0]).shape[0])
+        u3 = int(np.unique(i3[i3 >= 0]).shape[0])
+        ng_bytes = (uniq + u2 + u3) * H * 2 + T * H * 2 + 12 * T
+        ms_ng = per_call(lambda: V.vngram_fwd(ids, W, E2, E3, Vr, n, out=ng))
+        dE2 = torch.empty(rows_ng, H, **f32)
+        dE3 = torch.empty(rows_ng, H, **f32)
+        ws_ng = V.Workspaces(dev, emb=V.vemb_bwd_workspace_bytes(T, H, Vr, Vp),
+                             emb2=V.vemb_bwd_workspace_bytes(T, H, rows_ng, rows_ng),
+                             emb3=V.vemb_bwd_workspace_bytes(T, H, rows_ng, rows_ng))
+        ms_ngb = per_call(lambda: V.ngram_bwd(ids, ng, dh, Vr, Vp, n, dE=dW, dE2=dE2, dE3=dE3,
+                                              accumulate=True, ws=ws_ng))
+        ngb_bytes = 3 * T * H * 4 + 24 * T + 2 * (uniq + u2 + u3) * H * 4
+        res["ngram"] = {
+            "tables_rows": [Vp, rows_ng, rows_ng], "distinct_rows": [uniq, u2, u3],
+            "vngram_fwd": {"bytes": ng_bytes, "ms": ms_ng,
+                           "GB_s": ng_bytes / (ms_ng * 1e-3) / 1e9,
+                           "frac": ng_bytes / (ms_ng * 1e-3) / PEAK_HBM},
+            "ngram_bwd": {"bytes": ngb_bytes, "ms": ms_ngb,
+                          "GB_s": ngb_bytes / (ms_ngb * 1e-3) / 1e9,
+                          "frac": ngb_bytes / (ms_ngb * 1e-3) / PEAK_HBM},
+        }
+        log(f"[bench] n-gram embedding fwd {ms_ng * 1e3:.1f} us, bwd {ms_ngb * 1e3:.1f} us")
+        del E2, E3, dE2, dE3, ws_ng, ng
     if a.copy_probe:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

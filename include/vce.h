@@ -232,6 +232,35 @@ vce_status vemb_bwd(const int32_t* ids, const void* dout, vce_dtype dout_dt,
                     void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * Hashed n-gram input embedding (the Over-Tokenized input side).           *
+ *                                                                           *
+ * [SS] Setup and its loss listing: to the embedding of every input token    *
+ * OT adds a hashed 2-gram and a hashed 3-gram embedding of the n-grams that *
+ * end at that token:                                                        *
+ *   out[t] = E[ids[t]] + E2[row2(t)] + E3[row3(t)]                          *
+ * row2(t) = mix64(ids[t-1]*V_real + ids[t]) mod rows2 and                   *
+ * row3(t) = mix64((ids[t-2]*V_real + ids[t-1])*V_real + ids[t]) mod rows3   *
+ * (unsigned 64-bit; mix64 = the SplitMix64 output finaliser, Steele, Lea &  *
+ * Flood 2014). The page gives no hash; this is the library's choice. An     *
+ * n-gram exists only when t >= n-1 and all its IDs are in [0, V_real); a    *
+ * missing n-gram, like an invalid unigram ID, adds a zero row. The T tokens *
+ * form one sequence. Each table is split into num_shards contiguous equal   *
+ * shards (V_pad, rows2 and rows3 multiples of num_shards) and read by owner *
+ * and local index, as vemb_fwd reads E. The three rows are added in float32 *
+ * in that order and stored in dt (bf16 rounded to nearest-even).            *
+ *                                                                           *
+ * In:  ids [T] int32; E [V_pad,H], E2 [rows2,H], E3 [rows3,H] dt.          *
+ * Out: out [T,H] dt; ids2, ids3 [T] int32: row2(t) / row3(t), -1 where the  *
+ *      n-gram is missing (the backward is vemb_bwd with these as IDs and    *
+ *      rows2 / rows3 as V_real = V_pad); n_bad_id [1] (optional) as vemb_fwd.*
+ * rows2, rows3 in [1, 2^31); errors as for vemb_fwd.                        *
+ * ------------------------------------------------------------------------ */
+vce_status vngram_fwd(const int32_t* ids, const void* E, const void* E2, const void* E3,
+                      int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int64_t rows2,
+                      int64_t rows3, int32_t num_shards, vce_dtype dt, void* out,
+                      int32_t* ids2, int32_t* ids3, int32_t* n_bad_id, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Sampled-softmax candidates.                                               *
  *                                                                           *
  * [SS] Setup (the simplified loss): candidates are the unique targets of    *

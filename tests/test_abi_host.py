@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in vce.SIGNATURES, n
@@ -120,6 +120,22 @@ def test_argmax_argument_errors():
     assert args(ws=NUL) == WORKSPACE
     assert args(T=0, h=NUL, W=NUL, idx=NUL, val=NUL, ws=NUL, wsb=0) == OK  # nothing to do
     assert lib.vce_argmax_workspace_bytes(8, 64, 100, 101, 2, 1) == 0     # 101 % 2 != 0
+
+
+def test_ngram_argument_errors():
+    def call(T=4, H=64, Vr=1000, Vp=1024, r2=4096, r3=8192, n=4, dt=1, ids=A, E=B, E2=C, E3=A,
+             out=B, i2=C, i3=A):
+        return lib.vngram_fwd(ids, E, E2, E3, T, H, Vr, Vp, r2, r3, n, dt, out, i2, i3, NUL,
+                              None)
+    assert call(r2=0) == SHAPE
+    assert call(r3=(1 << 31)) == SHAPE
+    assert call(r2=4098) == SHARD            # not a multiple of num_shards
+    assert call(n=3) == SHARD
+    assert call(dt=5) == DTYPE
+    assert call(E2=NUL) == NULL
+    assert call(i3=NUL) == NULL
+    assert call(H=20) == ALIGN
+    assert call(E3=MIS) == ALIGN
 
 
 def test_candidates_argument_errors():

@@ -50,6 +50,8 @@ SIGNATURES = {
     "vce_argmax_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32, _I32]),
     "vce_argmax": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _SZ,
                           _P]),
+    "vngram_fwd": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I32, _I32, _P, _P,
+                          _P, _P, _P]),
     "vss_candidates_workspace_bytes": (_SZ, [_I64, _I64]),
     "vss_candidates": (_I32, [_P, _I64, _I64, _I32, _P, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _P]),
 }
@@ -279,6 +281,35 @@ def vemb_fwd(ids: torch.Tensor, W: torch.Tensor, V_real: int, num_shards: int, *
                       _ptr(n_bad) if count_bad else None, _stream(stream, dev))
     _check("vemb_fwd", st)
     return out, n_bad
+
+
+NgramOut = namedtuple("NgramOut", "out ids2 ids3 n_bad")
+
+
+def vngram_fwd(ids: torch.Tensor, E: torch.Tensor, E2: torch.Tensor, E3: torch.Tensor,
+               V_real: int, num_shards: int, *, out: Optional[NgramOut] = None,
+               stream=None) -> NgramOut:
+    """Hashed n-gram input embedding: out [T,H] (E's dtype) = unigram + 2-gram +
+    3-gram rows; ids2 / ids3 [T] int32 table rows (-1: missing); n_bad [1]."""
+    T = ids.shape[0]
+    V_pad, H = E.shape
+    dt = _dt(E)
+    _need(ids, "ids", torch.int32, (T,))
+    _need(E, "E")
+    _need(E2, "E2", E.dtype)
+    _need(E3, "E3", E.dtype)
+    if E2.shape[1] != H or E3.shape[1] != H:
+        raise ValueError("E, E2 and E3 must have the same row width")
+    dev = E.device
+    if out is None:
+        i = dict(dtype=torch.int32, device=dev)
+        out = NgramOut(torch.empty(T, H, dtype=E.dtype, device=dev), torch.empty(T, **i),
+                       torch.empty(T, **i), torch.empty(1, **i))
+    st = lib.vngram_fwd(_ptr(ids), _ptr(E), _ptr(E2), _ptr(E3), T, H, V_real, V_pad,
+                        E2.shape[0], E3.shape[0], num_shards, dt, _ptr(out.out), _ptr(out.ids2),
+                        _ptr(out.ids3), _ptr(out.n_bad), _stream(stream, dev))
+    _check("vngram_fwd", st)
+    return out
 
 
 def vemb_bwd(ids: torch.Tensor, dout: torch.Tensor, V_real: int, V_pad: int, num_shards: int,

@@ -184,6 +184,26 @@ vce_status vemb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, int
                                      n_bad_id, static_cast<hipStream_t>(stream)));
 }
 
+vce_status vngram_fwd(const int32_t* ids, const void* E, const void* E2, const void* E3,
+                      int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int64_t rows2,
+                      int64_t rows3, int32_t num_shards, vce_dtype dt, void* out,
+                      int32_t* ids2, int32_t* ids3, int32_t* n_bad_id, void* stream) {
+  if (!dtype_ok(dt)) return VCE_ERR_DTYPE;
+  vce_status st = check_table(T, H, V_real, V_pad, num_shards);
+  if (st != VCE_OK) return st;
+  if (rows2 < 1 || rows3 < 1 || rows2 > kMaxDim || rows3 > kMaxDim) return VCE_ERR_SHAPE;
+  if (rows2 % num_shards != 0 || rows3 % num_shards != 0) return VCE_ERR_SHARD;
+  if (T > 0 && (!ids || !E || !E2 || !E3 || !out || !ids2 || !ids3)) return VCE_ERR_NULL;
+  if (H % 8 != 0) return VCE_ERR_ALIGN;
+  if (T > 0 && (!aligned4(ids) || !aligned16(E) || !aligned16(E2) || !aligned16(E3) ||
+                !aligned16(out) || !aligned4(ids2) || !aligned4(ids3)))
+    return VCE_ERR_ALIGN;
+  if (n_bad_id && !aligned4(n_bad_id)) return VCE_ERR_ALIGN;
+  return hip_status(vce::run_ngram_fwd(ids, E, E2, E3, T, H, V_real, V_pad, rows2, rows3,
+                                       num_shards, dt == VCE_BF16, out, ids2, ids3, n_bad_id,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 vce_status vemb_bwd(const int32_t* ids, const void* dout, vce_dtype dout_dt, int64_t T, int64_t H,
                     int64_t V_real, int64_t V_pad, int32_t num_shards, float* dW,
                     int32_t accumulate, void* ws, size_t ws_bytes, void* stream) {

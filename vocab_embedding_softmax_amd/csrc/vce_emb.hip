@@ -163,6 +163,150 @@ __global__ void k_zero_i32(int32_t* p) {
   if (threadIdx.x == 0) *p = 0;
 }
 
+// ------------------------------------------------------------------ hashed n-grams
+
+// The SplitMix64 output finaliser (Steele, Lea and Flood, OOPSLA 2014).
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+template <typename E>
+struct Piece;  // one 16-byte piece of a row, widened to float
+template <>
+struct Piece<uint16_t> {
+  static constexpr int N = 8;
+  __device__ static void load(const u32x4& v, float (&f)[8]) {
+    f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xFFFF0000u);
+    f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xFFFF0000u);
+  }
+  __device__ static u32x4 store(const float (&f)[8]) {
+    return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                 pack_bf16x2(f[6], f[7])};
+  }
+};
+template <>
+struct Piece<float> {
+  static constexpr int N = 4;
+  __device__ static void load(const u32x4& v, float (&f)[4]) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+  __device__ static u32x4 store(const float (&f)[4]) {
+    return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                 __float_as_uint(f[3])};
+  }
+};
+
+// Input embedding of the Over-Tokenized Transformer's input side ("Sampled
+// Softmax with Over-Tokenized Transformer", Setup): one wave per token t
+//   x[t] = E[id_t] + E2[row2(t)] + E3[row3(t)]
+// where row_n(t) is mix64(key) mod rows_n for the n-gram ending at t (key =
+// its token IDs in base V_real, oldest first), present only when t >= n-1 and
+// all n IDs are valid; a missing part adds nothing. Every table is read by
+// owner shard and local index (contiguous equal shards). The three pieces
+// are added in float32 in that order and the sum is stored in the table
+// type (bf16 rounded to nearest-even). row2 / row3 (-1 if missing) are
+// written for the backward. Workgroup 0 counts invalid token IDs.
+template <typename E>
+__global__ __launch_bounds__(256) void k_ngram_fwd(
+    const int32_t* __restrict__ ids, const char* __restrict__ E0, const char* __restrict__ E2,
+    const char* __restrict__ E3, int64_t T, int64_t row_bytes, int64_t V_real, int64_t S0,
+    int64_t rows2, int64_t S2, int64_t rows3, int64_t S3, char* __restrict__ out,
+    int32_t* __restrict__ ids2, int32_t* __restrict__ ids3, int32_t* n_bad) {
+  constexpr int U = 8;  // pieces per lane and table held at once
+  const int lane = threadIdx.x & 63;
+  if (blockIdx.x == 0 && n_bad) {
+    __shared__ int32_t cnt[4];
+    int32_t bad = 0;
+    for (int64_t t = threadIdx.x; t < T; t += 256) {
+      const int64_t id = ids[t];
+      bad += (id < 0 || id >= V_real) ? 1 : 0;
+    }
+    for (int o = 32; o > 0; o >>= 1) bad += __shfl_xor(bad, o);
+    if (lane == 0) cnt[threadIdx.x >> 6] = bad;
+    __syncthreads();
+    if (threadIdx.x == 0) *n_bad = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+  }
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int64_t a = ids[t];
+  const int64_t b = t >= 1 ? ids[t - 1] : -1;
+  const int64_t c = t >= 2 ? ids[t - 2] : -1;
+  const bool oka = a >= 0 && a < V_real, okb = b >= 0 && b < V_real, okc = c >= 0 && c < V_real;
+  const uint64_t V = static_cast<uint64_t>(V_real);
+  int64_t r2 = -1, r3 = -1;
+  if (oka && okb) r2 = static_cast<int64_t>(mix64(static_cast<uint64_t>(b) * V + a) % rows2);
+  if (oka && okb && okc)
+    r3 = static_cast<int64_t>(mix64((static_cast<uint64_t>(c) * V + b) * V + a) % rows3);
+  if (lane == 0) {
+    ids2[t] = static_cast<int32_t>(r2);
+    ids3[t] = static_cast<int32_t>(r3);
+  }
+  // owner shard, then the local row inside its slice, for each table
+  auto row_ptr = [&](const char* base, int64_t r, int64_t S) -> const u32x4* {
+    const int64_t k = r / S;
+    return reinterpret_cast<const u32x4*>(base + (k * S + (r - k * S)) * row_bytes);
+  };
+  const u32x4* p0 = oka ? row_ptr(E0, a, S0) : nullptr;
+  const u32x4* p2 = r2 >= 0 ? row_ptr(E2, r2, S2) : nullptr;
+  const u32x4* p3 = r3 >= 0 ? row_ptr(E3, r3, S3) : nullptr;
+  u32x4* dst = reinterpret_cast<u32x4*>(out + t * row_bytes);
+  const int64_t nvec = row_bytes >> 4;
+  constexpr u32x4 kZero = {0u, 0u, 0u, 0u};
+  for (int64_t c0 = 0; c0 < nvec; c0 += 64 * U) {
+    u32x4 v0[U], v2[U], v3[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t cc = c0 + lane + 64 * u;
+      const bool in = cc < nvec;
+      v0[u] = (in && p0) ? p0[cc] : kZero;
+      v2[u] = (in && p2) ? p2[cc] : kZero;
+      v3[u] = (in && p3) ? p3[cc] : kZero;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t cc = c0 + lane + 64 * u;
+      if (cc >= nvec) continue;
+      float f0[Piece<E>::N], f2[Piece<E>::N], f3[Piece<E>::N];
+      Piece<E>::load(v0[u], f0);
+      Piece<E>::load(v2[u], f2);
+      Piece<E>::load(v3[u], f3);
+#pragma unroll
+      for (int i = 0; i < Piece<E>::N; ++i) f0[i] = (f0[i] + f2[i]) + f3[i];
+      __builtin_nontemporal_store(Piece<E>::store(f0), dst + cc);
+    }
+  }
+}
+
+hipError_t run_ngram_fwd(const int32_t* ids, const void* E0, const void* E2, const void* E3,
+                         int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int64_t rows2,
+                         int64_t rows3, int32_t n, bool bf16, void* out, int32_t* ids2,
+                         int32_t* ids3, int32_t* n_bad, hipStream_t s) {
+  if (T == 0) {
+    if (!n_bad) return hipSuccess;
+    hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(64), 0, s, n_bad);
+    return hipGetLastError();
+  }
+  const int64_t row_bytes = H * (bf16 ? 2 : 4);
+  const dim3 grid(static_cast<uint32_t>(cdiv(T, 4)));
+  if (bf16)
+    hipLaunchKernelGGL(k_ngram_fwd<uint16_t>, grid, dim3(256), 0, s, ids,
+                       static_cast<const char*>(E0), static_cast<const char*>(E2),
+                       static_cast<const char*>(E3), T, row_bytes, V_real, V_pad / n, rows2,
+                       rows2 / n, rows3, rows3 / n, static_cast<char*>(out), ids2, ids3, n_bad);
+  else
+    hipLaunchKernelGGL(k_ngram_fwd<float>, grid, dim3(256), 0, s, ids,
+                       static_cast<const char*>(E0), static_cast<const char*>(E2),
+                       static_cast<const char*>(E3), T, row_bytes, V_real, V_pad / n, rows2,
+                       rows2 / n, rows3, rows3 / n, static_cast<char*>(out), ids2, ids3, n_bad);
+  return hipGetLastError();
+}
+
+
 // ------------------------------------------------------------------ scan
 
 __global__ __launch_bounds__(kScanThreads) void k_fill_i32(int32_t* __restrict__ p, int64_t n,

@@ -206,6 +206,11 @@ hipError_t run_emb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, 
                        int64_t V_pad, int32_t n, size_t esize, void* out, int32_t* n_bad,
                        hipStream_t s);
 
+hipError_t run_ngram_fwd(const int32_t* ids, const void* E0, const void* E2, const void* E3,
+                         int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int64_t rows2,
+                         int64_t rows3, int32_t n, bool bf16, void* out, int32_t* ids2,
+                         int32_t* ids3, int32_t* n_bad, hipStream_t s);
+
 hipError_t run_emb_bwd(const int32_t* ids, const void* dout, bool dout_bf16, int64_t T, int64_t H,
                        int64_t V_real, int64_t V_pad, float* dW, int32_t accumulate,
                        const EmbBwdPlan& p, hipStream_t s);

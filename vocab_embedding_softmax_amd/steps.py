@@ -7,6 +7,9 @@ tied_step     lookup -> cross-entropy forward/backward -> scatter-add of dh
 sampled_step  candidates -> lookup of the candidate rows -> cross-entropy over
               them -> scatter of their gradients into the full table
               ("Sampled Softmax with Over-Tokenized Transformer", Setup)
+ngram_bwd     backward of vngram_fwd: the scatter-add of dx into the unigram
+              table and, by the rows vngram_fwd reported, into the two n-gram
+              tables (same page, OT input side)
 ot_h_step     tied_step plus a second, untied head on the hidden rows but the
               last, scored two tokens ahead and weighted 0.1 (same page, OT-H);
               its dh is added into the first head's before the scatter
@@ -123,3 +126,20 @@ def ot_h_step(ids, targets1, targets2, W, W2, V_real, num_shards, ignore_index=-
     L.vemb_bwd(ids, b1.dh, V_real, W.shape[0], num_shards, dW=b1.dW, accumulate=True,
                ws=None if ws is None else ws["emb"], stream=stream)
     return StepOut(f1, b1.dh, b1.dW, dict(h=h, n_bad_id=n_bad_id, fwd2=f2, dW2=b2.dW))
+
+
+def ngram_bwd(ids, fwd_out, dx, V_real, V_pad, num_shards, *, dE=None, dE2=None, dE3=None,
+              rows2=None, rows3=None, accumulate=False, ws: Optional[Workspaces] = None,
+              stream=None):
+    """dE [V_pad,H], dE2 [rows2,H], dE3 [rows3,H] (float32) from dx [T,H]; the
+    n-gram rows are the ones vngram_fwd returned (fwd_out.ids2 / ids3)."""
+    rows2 = dE2.shape[0] if rows2 is None else rows2
+    rows3 = dE3.shape[0] if rows3 is None else rows3
+    w = None if ws is None else ws["emb"]
+    dE = L.vemb_bwd(ids, dx, V_real, V_pad, num_shards, dW=dE, accumulate=accumulate, ws=w,
+                    stream=stream)
+    dE2 = L.vemb_bwd(fwd_out.ids2, dx, rows2, rows2, num_shards, dW=dE2, accumulate=accumulate,
+                     ws=None if ws is None else ws["emb2"], stream=stream)
+    dE3 = L.vemb_bwd(fwd_out.ids3, dx, rows3, rows3, num_shards, dW=dE3, accumulate=accumulate,
+                     ws=None if ws is None else ws["emb3"], stream=stream)
+    return dE, dE2, dE3
