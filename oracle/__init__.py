@@ -19,7 +19,7 @@ tests/test_oracle_pins.py holds it to something other than itself.
 """
 
 from .bits import decode  # noqa: F401
-from .geometry import shard_size, owner_and_local  # noqa: F401
+from .geometry import shard_size, shard_bounds, owner_and_local, remap  # noqa: F401
 from .embedding import gather_direct, gather_masked_shards, scatter_add  # noqa: F401
 from .ce import (  # noqa: F401
     target_status, logits, lse_rows, shard_stats, merge_shard_stats, lse_two_phase,

@@ -25,19 +25,18 @@ from __future__ import annotations
 import numpy as np
 
 from .ce import logits
-from .geometry import shard_size
+from .geometry import shard_bounds
 
 
-def shard_argmax(z, V_real: int, V_pad: int, num_shards: int):
+def shard_argmax(z, V_real: int, V_pad: int, num_shards: int, shard_rows=None):
     """Per shard k over the real columns it owns: (value, index) of the largest
     logit, the lowest index on ties; (-inf, -1) for a shard without real rows.
     z holds the real columns [0, V_real) only."""
-    S = shard_size(V_pad, num_shards)
     T = z.shape[0]
     val = np.full((num_shards, T), -np.inf)
     idx = np.full((num_shards, T), -1, dtype=np.int64)
-    for k in range(num_shards):
-        lo, hi = k * S, min((k + 1) * S, V_real)
+    for k, (lo, hi) in enumerate(shard_bounds(V_pad, num_shards, shard_rows)):
+        hi = min(hi, V_real)
         if hi <= lo:
             continue
         zk = z[:, lo:hi]
@@ -60,7 +59,8 @@ def merge_shard_argmax(val, idx):
     return best_v, best_i
 
 
-def greedy_argmax(h, W, V_real: int, V_pad: int, num_shards: int, chunk: int = 256) -> dict:
+def greedy_argmax(h, W, V_real: int, V_pad: int, num_shards: int, chunk: int = 256,
+                  shard_rows=None) -> dict:
     """index [T] and value [T] of the global argmax over the real rows, plus the
     per-shard reports (shard_value, shard_index [num_shards, T]). h [T, H] and
     W [V_pad, H] are float64; rows of W at or past V_real are never read."""
@@ -70,6 +70,6 @@ def greedy_argmax(h, W, V_real: int, V_pad: int, num_shards: int, chunk: int = 2
     for t0 in range(0, T, chunk):
         t1 = min(T, t0 + chunk)
         z = logits(h[t0:t1], W, V_real)
-        sv[:, t0:t1], si[:, t0:t1] = shard_argmax(z, V_real, V_pad, num_shards)
+        sv[:, t0:t1], si[:, t0:t1] = shard_argmax(z, V_real, V_pad, num_shards, shard_rows)
     value, index = merge_shard_argmax(sv, si)
     return dict(index=index, value=value, shard_value=sv, shard_index=si)

@@ -22,7 +22,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .geometry import owner_and_local, shard_size
+from .geometry import owner_and_local, shard_bounds
 
 MEAN, SUM = 0, 1
 
@@ -50,17 +50,16 @@ def lse_rows(z) -> np.ndarray:
     return m + np.log(np.exp(z - m[:, None]).sum(axis=1))
 
 
-def shard_stats(z, V_real: int, V_pad: int, num_shards: int):
+def shard_stats(z, V_real: int, V_pad: int, num_shards: int, shard_rows=None):
     """Per shard k: m_k = max of the logits of the real rows k owns, and
     s_k = sum of exp(z - m_k) over them; a shard owning no real row gives
     (-inf, 0). z holds the real columns [0, V_real) only.
     Pinned by test_sharded_lse_equals_unsharded."""
-    S = shard_size(V_pad, num_shards)
     T = z.shape[0]
     m = np.full((num_shards, T), -np.inf)
     s = np.zeros((num_shards, T))
-    for k in range(num_shards):
-        lo, hi = k * S, min((k + 1) * S, V_real)
+    for k, (lo, hi) in enumerate(shard_bounds(V_pad, num_shards, shard_rows)):
+        hi = min(hi, V_real)
         if hi <= lo:
             continue
         zk = z[:, lo:hi]
@@ -81,14 +80,13 @@ def merge_shard_stats(m, s) -> np.ndarray:
     return M + np.log(total)
 
 
-def lse_two_phase(z, V_real: int, V_pad: int, num_shards: int) -> np.ndarray:
+def lse_two_phase(z, V_real: int, V_pad: int, num_shards: int, shard_rows=None) -> np.ndarray:
     """The schedule as [VS] paragraph 3 orders it: first the global maximum
     over valid entries (the maximum of the shards' own maxima), then each
     shard's sum of exp(z - global max) over its owned real rows, then the
     global sum. Pinned by test_sharded_lse_equals_unsharded."""
-    S = shard_size(V_pad, num_shards)
     T = z.shape[0]
-    parts = [(k * S, min((k + 1) * S, V_real)) for k in range(num_shards)]
+    parts = [(lo, min(hi, V_real)) for lo, hi in shard_bounds(V_pad, num_shards, shard_rows)]
     local_max = np.full((num_shards, T), -np.inf)
     for k, (lo, hi) in enumerate(parts):
         if hi > lo:
@@ -112,17 +110,17 @@ def grad_scale(grad_loss: float, n_valid: int, reduction: int) -> float:
 
 
 def ce_forward(h, W, targets, V_real: int, V_pad: int, num_shards: int,
-               ignore_index: int = -100, chunk: int = 256) -> dict:
+               ignore_index: int = -100, chunk: int = 256, shard_rows=None) -> dict:
     """Per-token lse, loss and target logit; loss_sum, n_valid, n_bad; and the
     per-shard (m_k, s_k). h [T, H] and W [V_pad, H] are float64; rows of W at
     or past V_real are never read. Ignored and bad tokens still get lse but
     loss 0. Pinned by test_bruteforce_tiny, test_binomial_page_numbers,
     test_lse_closed_forms and test_padded_rows_do_not_matter."""
     T = h.shape[0]
-    S = shard_size(V_pad, num_shards)
+    bounds = shard_bounds(V_pad, num_shards, shard_rows)
     valid, ignored, bad = target_status(targets, V_real, ignore_index)
     y = np.asarray(targets, dtype=np.int64)
-    owner, local = owner_and_local(y, V_real, V_pad, num_shards)
+    owner, local = owner_and_local(y, V_real, V_pad, num_shards, shard_rows)
     lse = np.zeros(T)
     zt = np.zeros(T)
     sm = np.full((num_shards, T), -np.inf)
@@ -131,13 +129,13 @@ def ce_forward(h, W, targets, V_real: int, V_pad: int, num_shards: int,
         t1 = min(T, t0 + chunk)
         z = logits(h[t0:t1], W, V_real)
         lse[t0:t1] = lse_rows(z)
-        m, s = shard_stats(z, V_real, V_pad, num_shards)
+        m, s = shard_stats(z, V_real, V_pad, num_shards, shard_rows)
         sm[:, t0:t1], ss[:, t0:t1] = m, s
         for i in range(t1 - t0):
             t = t0 + i
             if valid[t]:
                 # the owning shard reads its own column at the local index
-                zt[t] = z[i, owner[t] * S + local[t]]
+                zt[t] = z[i, bounds[owner[t]][0] + local[t]]
     loss = np.where(valid, lse - zt, 0.0)
     return dict(lse=lse, loss=loss, zt=zt, loss_sum=float(loss.sum()),
                 n_valid=int(valid.sum()), n_bad=int(bad.sum()), valid=valid,
@@ -171,10 +169,10 @@ def ce_backward(h, W, targets, lse, V_real: int, V_pad: int, scale: float,
 
 def cross_entropy(h, W, targets, V_real: int, V_pad: int, num_shards: int,
                   ignore_index: int = -100, grad_loss: float = 1.0,
-                  reduction: int = MEAN, chunk: int = 256) -> dict:
+                  reduction: int = MEAN, chunk: int = 256, shard_rows=None) -> dict:
     """Forward, then backward with the loss scaling of ``reduction``.
     Adds loss (the reduced value), scale, dh and dW to the forward's dict."""
-    f = ce_forward(h, W, targets, V_real, V_pad, num_shards, ignore_index, chunk)
+    f = ce_forward(h, W, targets, V_real, V_pad, num_shards, ignore_index, chunk, shard_rows)
     scale = grad_scale(grad_loss, f["n_valid"], reduction)
     dh, dW = ce_backward(h, W, targets, f["lse"], V_real, V_pad, scale, ignore_index, chunk)
     if reduction == MEAN:

@@ -10,7 +10,7 @@ adopted: an ID outside [0, V_real) yields a zero row and no gradient.
 
 import numpy as np
 
-from .geometry import owner_and_local, shard_size
+from .geometry import owner_and_local, shard_bounds
 
 
 def gather_direct(ids, W, V_real: int) -> np.ndarray:
@@ -25,16 +25,16 @@ def gather_direct(ids, W, V_real: int) -> np.ndarray:
     return out
 
 
-def gather_masked_shards(ids, W, V_real: int, V_pad: int, num_shards: int) -> np.ndarray:
+def gather_masked_shards(ids, W, V_real: int, V_pad: int, num_shards: int,
+                         shard_rows=None) -> np.ndarray:
     """The sharded form: every shard looks up only IDs it owns, at their local
     index in its own slice of the table, contributes zeros elsewhere, and the
     contributions are summed over shards. Pinned against gather_direct."""
     ids = np.asarray(ids, dtype=np.int64)
-    S = shard_size(V_pad, num_shards)
-    owner, local = owner_and_local(ids, V_real, V_pad, num_shards)
+    owner, local = owner_and_local(ids, V_real, V_pad, num_shards, shard_rows)
     out = np.zeros((ids.shape[0], W.shape[1]), dtype=np.float64)
-    for k in range(num_shards):
-        Wk = W[k * S:(k + 1) * S]
+    for k, (lo, hi) in enumerate(shard_bounds(V_pad, num_shards, shard_rows)):
+        Wk = W[lo:hi]
         mine = owner == k
         contrib = np.zeros_like(out)
         contrib[mine] = Wk[local[mine]]

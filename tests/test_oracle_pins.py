@@ -650,3 +650,86 @@ def test_ngram_backward_finite_difference():
                 args_m[which][v, j] -= eps
                 num = (loss(*args_p) - loss(*args_m)) / (2 * eps)
                 assert abs(num - grad[v, j]) < 1e-7, (which, v, j)
+
+
+# ------------------------------------------------------------------ uneven and mapped shards
+
+UNEVEN = [
+    (1000, 1024, [0, 100, 100, 613, 1000, 1024]),    # an empty shard, the padding its own shard
+    (1000, 1024, [0, 1, 2, 900, 1024]),               # one-row shards, padding inside the last
+    (37, 64, [0, 64]),                                # one shard
+    (50, 64, [0, 10, 20, 30, 40, 50, 60, 64]),        # uneven tail
+]
+
+
+@pytest.mark.parametrize("V_real,V_pad,rows", UNEVEN)
+def test_uneven_owner_and_gather(V_real, V_pad, rows):
+    n = len(rows) - 1
+    ids = np.arange(-3, V_pad + 3)
+    owner, local = oracle.owner_and_local(ids, V_real, V_pad, n, shard_rows=rows)
+    for i, o, l in zip(ids, owner, local):
+        if 0 <= i < V_real:
+            assert rows[o] <= i < rows[o + 1] and rows[o] + l == i
+        else:
+            assert o == -1 and l == 0
+    W = np.random.default_rng(3).standard_normal((V_pad, 5))
+    W[V_real:] = np.nan
+    a = oracle.gather_masked_shards(ids, W, V_real, V_pad, n, shard_rows=rows)
+    b = oracle.gather_direct(ids, W, V_real)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("V_real,V_pad,rows", UNEVEN)
+def test_uneven_sharded_lse_and_argmax_equal_unsharded(V_real, V_pad, rows):
+    n = len(rows) - 1
+    rng = np.random.default_rng(V_real + n)
+    z = rng.standard_normal((7, V_real)) * 3
+    ref = oracle.lse_rows(z)
+    m, s = oracle.shard_stats(z, V_real, V_pad, n, shard_rows=rows)
+    assert np.allclose(oracle.merge_shard_stats(m, s), ref, rtol=1e-12, atol=0)
+    assert np.allclose(oracle.lse_two_phase(z, V_real, V_pad, n, shard_rows=rows), ref,
+                       rtol=1e-12, atol=0)
+    for k in range(n):
+        if min(rows[k + 1], V_real) <= rows[k]:
+            assert np.isneginf(m[k]).all() and not s[k].any()
+    v, i = oracle.merge_shard_argmax(*oracle.shard_argmax(z, V_real, V_pad, n, shard_rows=rows))
+    assert np.array_equal(i, np.argmax(z, axis=1)) and np.array_equal(v, z.max(axis=1))
+
+
+def test_uneven_layout_rejected_when_malformed():
+    for rows in ([0, 10, 5, 16], [1, 8, 16], [0, 8, 15], [0, 16, 16, 16, 17]):
+        with pytest.raises(ValueError):
+            oracle.shard_bounds(16, len(rows) - 1, rows)
+
+
+def test_mapped_ownership_is_a_relabelling():
+    """Classes placed at physical rows by a permutation: the table stored in
+    physical order with remapped targets and IDs gives the same losses, the
+    same lookups and the gradient rows of the same classes; the argmax maps
+    back to the same class."""
+    rng = np.random.default_rng(31)
+    T, H, V_real, V_pad = 9, 6, 40, 48
+    rows = [0, 7, 7, 30, 48]
+    n = len(rows) - 1
+    W = rng.standard_normal((V_pad, H))
+    h = rng.standard_normal((T, H))
+    y = rng.integers(0, V_real, T)
+    y[2] = -100
+    row_of = rng.permutation(V_real)
+    class_of = np.argsort(row_of)
+    Wp = W.copy()
+    Wp[row_of] = W[:V_real]
+    yp = oracle.remap(y, row_of, V_real)
+    assert yp[2] == -100
+    a = oracle.cross_entropy(h, W, y, V_real, V_pad, 1)
+    b = oracle.cross_entropy(h, Wp, yp, V_real, V_pad, n, shard_rows=rows)
+    assert np.allclose(a["lse"], b["lse"], rtol=1e-13, atol=0)
+    assert np.allclose(a["loss"], b["loss"], rtol=1e-12, atol=1e-14)
+    assert np.allclose(a["dh"], b["dh"], rtol=1e-12, atol=1e-14)
+    assert np.allclose(a["dW"][:V_real], b["dW"][row_of], rtol=1e-12, atol=1e-14)
+    ids = np.array([3, 39, -1, 40, 0])
+    assert np.array_equal(oracle.gather_direct(ids, W, V_real),
+                          oracle.gather_direct(oracle.remap(ids, row_of, V_real), Wp, V_real))
+    ga = oracle.greedy_argmax(h, W, V_real, V_pad, 1)
+    gb = oracle.greedy_argmax(h, Wp, V_real, V_pad, n, shard_rows=rows)
+    assert np.array_equal(class_of[gb["index"]], ga["index"])
