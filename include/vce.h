@@ -51,8 +51,9 @@ typedef enum {
   VCE_ERR_SHAPE = 2,     /* T < 0, H <= 0, V_real not in [1, V_pad], ignore_index
                             inside [0, V_real), P < 1, capacity too small, or a
                             size too large for 32-bit indexing of one dimension  */
-  VCE_ERR_SHARD = 3,     /* num_shards < 1 or V_pad not a multiple of num_shards */
-  VCE_ERR_DTYPE = 4,     /* unknown element type or reduction                    */
+  VCE_ERR_SHARD = 3,     /* num_shards not in [1, 128], V_pad not a multiple of
+                            num_shards, or a malformed shard_rows list          */
+  VCE_ERR_DTYPE = 4,     /* unknown element type, reduction or accumulate flag   */
   VCE_ERR_ALIGN = 5,     /* a pointer not 16-byte aligned, or H % 8 != 0         */
   VCE_ERR_WORKSPACE = 6, /* workspace NULL or smaller than the query returned    */
   VCE_ERR_HIP = 7        /* a HIP launch failed (hipGetLastError != success)     */
@@ -259,6 +260,59 @@ vce_status vngram_fwd(const int32_t* ids, const void* E, const void* E2, const v
                       int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int64_t rows2,
                       int64_t rows3, int32_t num_shards, vce_dtype dt, void* out,
                       int32_t* ids2, int32_t* ids3, int32_t* n_bad_id, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Explicit (uneven) shard layouts and mapped class ownership.               *
+ *                                                                           *
+ * [VS] paragraph 1 describes the equal split; [SP] paragraph 5 notes that   *
+ * uneven layouts need explicit support. The _ex entry points take the       *
+ * layout as shard_rows: a HOST array of num_shards + 1 int64 row offsets,   *
+ * 0 first, V_pad last, nondecreasing; shard k owns the physical rows         *
+ * [shard_rows[k], shard_rows[k+1]) (an empty shard owns none; V_pad need    *
+ * not be a multiple of num_shards). The array is read during the call only. *
+ * Everything else (arguments, outputs, rules, errors) is as for the entry   *
+ * point without _ex: a shard's maxima/sums and argmax report cover its own  *
+ * real rows, an empty shard or one wholly past V_real reports (-inf, 0) and *
+ * (-inf, -1). num_shards in [1, 128]; a malformed list gives VCE_ERR_SHARD,  *
+ * shard_rows == NULL gives VCE_ERR_NULL. Tiles never cross a shard end.     *
+ * The backward does not depend on the layout (every shard's rows receive    *
+ * their own gradient rows): call vce_bwd / vemb_bwd with num_shards = 1.    *
+ * ------------------------------------------------------------------------ */
+size_t vce_fwd_workspace_bytes_ex(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                                  int32_t num_shards, const int64_t* shard_rows, vce_dtype dt);
+
+vce_status vce_fwd_ex(const void* h, const void* W, const int32_t* targets,
+                      int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                      int32_t num_shards, const int64_t* shard_rows, int32_t ignore_index,
+                      vce_dtype dt, float* lse, float* loss, float* loss_sum,
+                      int32_t* n_valid, int32_t* n_bad_target, float* shard_stats,
+                      void* ws, size_t ws_bytes, void* stream);
+
+size_t vce_argmax_workspace_bytes_ex(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                                     int32_t num_shards, const int64_t* shard_rows,
+                                     vce_dtype dt);
+
+vce_status vce_argmax_ex(const void* h, const void* W, int64_t T, int64_t H, int64_t V_real,
+                         int64_t V_pad, int32_t num_shards, const int64_t* shard_rows,
+                         vce_dtype dt, int32_t* index, float* value, float* shard_value,
+                         int32_t* shard_index, void* ws, size_t ws_bytes, void* stream);
+
+vce_status vemb_fwd_ex(const int32_t* ids, const void* W, int64_t T, int64_t H,
+                       int64_t V_real, int64_t V_pad, int32_t num_shards,
+                       const int64_t* shard_rows, vce_dtype dt, void* out,
+                       int32_t* n_bad_id, void* stream);
+
+/* Mapped ownership: when classes are placed on physical rows by a           *
+ * permutation (class c stored at row map[c], map a permutation of           *
+ * [0, V_real), the table kept in physical order), IDs and targets are       *
+ * translated once before the lookups and the loss:                          *
+ *   out[t] = map[in[t]] for in[t] in [0, V_real), else in[t] unchanged      *
+ * (so ignore_index and invalid values keep their meaning). The results by   *
+ * class are then those of the unmapped table; an argmax index is a physical *
+ * row (its class is the inverse map's entry). in and out may be the same    *
+ * array. In: in [T], map [V_real] int32.  Out: out [T] int32.               */
+vce_status vce_remap(const int32_t* in, int64_t T, const int32_t* map, int64_t V_real,
+                     int32_t* out, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * Sampled-softmax candidates.                                               *

@@ -16,5 +16,7 @@ from .gen import (  # noqa: F401
     make_tied_inputs,
     make_oth_inputs,
     make_sampled_inputs,
+    make_layout,
+    make_row_map,
 )
 from .configs import CONFIGS, config_inputs  # noqa: F401

@@ -280,3 +280,31 @@ def make_sampled_inputs(T: int, H: int, V: int, P: int, dtype: str = "bf16",
     return CEInputs(T=T, H=H, V_real=V, V_pad=V, num_shards=1, dtype=dtype,
                     ignore_index=ignore_index, h=h, W=W, targets=tgt.astype(np.int32),
                     perm=perm, P=P, name=name)
+
+
+def make_layout(V_pad: int, num_shards: int, seed: int, n_empty: int = 0,
+                n_single: int = 0) -> np.ndarray:
+    """A seeded uneven shard layout: num_shards + 1 int64 row offsets from 0 to
+    V_pad, nondecreasing. n_empty shards own no row and n_single shards own one
+    row (chosen at seeded positions); the rest split the remaining rows at
+    uniformly drawn cut points."""
+    rng = np.random.default_rng(seed)
+    kinds = np.zeros(num_shards, dtype=np.int64)          # 0 free, 1 empty, 2 one row
+    pick = rng.permutation(num_shards)
+    kinds[pick[:n_empty]] = 1
+    kinds[pick[n_empty:n_empty + n_single]] = 2
+    free = int((kinds == 0).sum())
+    rest = V_pad - n_single
+    if free == 0 and rest != 0:
+        raise ValueError("no shard left for the remaining rows")
+    cuts = np.sort(rng.integers(0, rest + 1, size=max(free - 1, 0)))
+    sizes_free = np.diff(np.concatenate([[0], cuts, [rest]]))
+    sizes = np.zeros(num_shards, dtype=np.int64)
+    sizes[kinds == 2] = 1
+    sizes[kinds == 0] = sizes_free
+    return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+
+
+def make_row_map(V_real: int, seed: int) -> np.ndarray:
+    """A seeded permutation of [0, V_real) (class -> physical row), int32."""
+    return np.random.default_rng(seed).permutation(V_real).astype(np.int32)

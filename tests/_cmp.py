@@ -6,6 +6,16 @@ Tolerances:
     embedding-gradient tensor);
   fp32 inputs: 1e-5 relative on loss, lse (per element) and the gradients (rel-L2).
   Integer and byte results (gathers, counts, candidate lists): bit-exact.
+
+Argmax (floating point decides the index): the kernel's logits carry float32
+accumulation error, bounded for a row v by
+    e(t, v) = gamma * sum_j |h[t, j] W[v, j]|,  gamma = (K + 2) u / (1 - (K + 2) u),
+u = 2^-24 (products of bf16 inputs are exact in float32; float32 inputs add
+one rounding per product). When the oracle's best row beats every other row
+by more than the two rows' bounds, the kernel must return exactly that index;
+otherwise (a near tie) the kernel's row must be within those bounds of the
+maximum. The returned value must lie within the chosen row's bound of that
+row's exact logit.
 """
 
 import numpy as np
@@ -60,3 +70,33 @@ def oracle_ce(inp, grad_loss=1.0, reduction=MEAN, num_shards=None):
     n = inp.num_shards if num_shards is None else num_shards
     return oracle.cross_entropy(h, W, inp.targets, inp.V_real, inp.V_pad, n,
                                 inp.ignore_index, grad_loss, reduction)
+
+
+U = 2.0 ** -24
+
+
+def _bound(h64, W64, K):
+    g = (K + 2) * U / (1 - (K + 2) * U)
+    return g * (np.abs(h64) @ np.abs(W64).T)          # [T, V_real]
+
+
+def check_argmax(idx, val, h64, W64, V_real, what):
+    """idx, val: kernel results for the rows of h64; W64 holds the real rows."""
+    z = h64 @ W64[:V_real].T
+    e = _bound(h64, W64[:V_real], h64.shape[1])
+    T = z.shape[0]
+    o = np.argmax(z, axis=1)
+    zmax = z[np.arange(T), o]
+    # a row can overtake the oracle's best only if its upper bound reaches the
+    # best row's lower bound
+    reach = (z + e) >= (zmax - e[np.arange(T), o])[:, None]
+    reach[np.arange(T), o] = False
+    clear = ~reach.any(axis=1)
+    assert (idx >= 0).all() and (idx < V_real).all(), what
+    assert np.array_equal(idx[clear], o[clear]), (what, np.nonzero(idx[clear] != o[clear]))
+    amb = ~clear
+    zi = z[np.arange(T), idx]
+    ei = e[np.arange(T), idx]
+    assert (zi[amb] + ei[amb] >= zmax[amb] - e[np.arange(T), o][amb]).all(), what
+    assert (np.abs(val - zi) <= ei + 1e-30).all(), (what, np.abs(val - zi).max())
+    return int(clear.sum())

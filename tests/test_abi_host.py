@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in vce.SIGNATURES, n
@@ -120,6 +120,57 @@ def test_argmax_argument_errors():
     assert args(ws=NUL) == WORKSPACE
     assert args(T=0, h=NUL, W=NUL, idx=NUL, val=NUL, ws=NUL, wsb=0) == OK  # nothing to do
     assert lib.vce_argmax_workspace_bytes(8, 64, 100, 101, 2, 1) == 0     # 101 % 2 != 0
+
+
+def _rows(*r):
+    return (ctypes.c_int64 * len(r))(*r)
+
+
+def test_uneven_layout_argument_errors():
+    good = _rows(0, 100, 100, 601, 1000)            # one empty shard, V_pad not a multiple of 4
+    need = lib.vce_fwd_workspace_bytes_ex(4, 64, 990, 1000, 4, good, 1)
+    assert need > 0
+    assert lib.vce_fwd_workspace_bytes_ex(4, 64, 990, 1000, 4, _rows(0, 600, 500, 900, 1000),
+                                          1) == 0     # decreasing
+    assert lib.vce_fwd_workspace_bytes_ex(4, 64, 990, 1000, 4, NUL, 1) == 0
+
+    def fwd(rows=good, n=4, Vr=990, Vp=1000, h=A, ws=A, wsb=need):
+        return lib.vce_fwd_ex(h, B, C, 4, 64, Vr, Vp, n, rows, -100, 1, A, B, C, A, B, NUL, ws,
+                              wsb, None)
+    assert fwd(rows=NUL) == NULL
+    assert fwd(rows=_rows(0, 100, 100, 601, 999)) == SHARD    # does not end at V_pad
+    assert fwd(rows=_rows(1, 100, 100, 601, 1000)) == SHARD   # does not start at 0
+    assert fwd(rows=_rows(0, 700, 600, 900, 1000)) == SHARD   # decreasing
+    assert fwd(n=129, rows=_rows(*[min(7 * i, 1000) for i in range(129)], 1000)) == SHARD
+    assert fwd(Vr=1001) == SHAPE
+    assert fwd(h=NUL) == NULL
+    assert fwd(wsb=need - 1) == WORKSPACE
+
+    aneed = lib.vce_argmax_workspace_bytes_ex(4, 64, 990, 1000, 4, good, 1)
+    assert aneed > 0
+    assert lib.vce_argmax_ex(A, B, 4, 64, 990, 1000, 4, NUL, 1, C, A, NUL, NUL, A, aneed,
+                             None) == NULL
+    assert lib.vce_argmax_ex(A, B, 4, 64, 990, 1000, 4, _rows(0, 1, 2, 3, 4), 1, C, A, NUL, NUL,
+                             A, aneed, None) == SHARD
+    assert lib.vce_argmax_ex(A, B, 4, 64, 990, 1000, 4, good, 1, C, A, NUL, NUL, A, aneed - 1,
+                             None) == WORKSPACE
+    assert lib.vemb_fwd_ex(A, B, 4, 64, 990, 1000, 4, NUL, 1, C, NUL, None) == NULL
+    assert lib.vemb_fwd_ex(A, B, 4, 64, 990, 1000, 4, _rows(0, 5, 4, 6, 1000), 1, C, NUL,
+                           None) == SHARD
+    assert lib.vemb_fwd_ex(A, MIS, 4, 64, 990, 1000, 4, good, 1, C, NUL, None) == ALIGN
+    assert lib.vemb_fwd_ex(A, B, 0, 64, 990, 1000, 4, good, 1, NUL, NUL, None) == OK
+    # the even layout written out is accepted wherever the even call is
+    even = _rows(0, 256, 512, 768, 1024)
+    assert lib.vce_fwd_workspace_bytes_ex(4, 64, 1000, 1024, 4, even, 1) > 0
+
+
+def test_remap_argument_errors():
+    assert lib.vce_remap(A, 4, B, 0, C, None) == SHAPE
+    assert lib.vce_remap(A, -1, B, 10, C, None) == SHAPE
+    assert lib.vce_remap(NUL, 4, B, 10, C, None) == NULL
+    assert lib.vce_remap(A, 4, NUL, 10, C, None) == NULL
+    assert lib.vce_remap(ctypes.c_void_p(0x10002), 4, B, 10, C, None) == ALIGN
+    assert lib.vce_remap(NUL, 0, NUL, 10, NUL, None) == OK     # nothing to do
 
 
 def test_ngram_argument_errors():

@@ -19,12 +19,11 @@ import pytest
 
 import oracle
 from synth import config_inputs
+from tests._cmp import check_argmax
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-
-U = 2.0 ** -24
 
 
 @pytest.fixture(scope="module")
@@ -38,33 +37,6 @@ def V():
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
-
-
-def _bound(h64, W64, K):
-    g = (K + 2) * U / (1 - (K + 2) * U)
-    return g * (np.abs(h64) @ np.abs(W64).T)          # [T, V_real]
-
-
-def check_argmax(idx, val, h64, W64, V_real, what):
-    """idx, val: kernel results for the rows of h64; W64 holds the real rows."""
-    z = h64 @ W64[:V_real].T
-    e = _bound(h64, W64[:V_real], h64.shape[1])
-    T = z.shape[0]
-    o = np.argmax(z, axis=1)
-    zmax = z[np.arange(T), o]
-    # a row can overtake the oracle's best only if its upper bound reaches the
-    # best row's lower bound
-    reach = (z + e) >= (zmax - e[np.arange(T), o])[:, None]
-    reach[np.arange(T), o] = False
-    clear = ~reach.any(axis=1)
-    assert (idx >= 0).all() and (idx < V_real).all(), what
-    assert np.array_equal(idx[clear], o[clear]), (what, np.nonzero(idx[clear] != o[clear]))
-    amb = ~clear
-    zi = z[np.arange(T), idx]
-    ei = e[np.arange(T), idx]
-    assert (zi[amb] + ei[amb] >= zmax[amb] - e[np.arange(T), o][amb]).all(), what
-    assert (np.abs(val - zi) <= ei + 1e-30).all(), (what, np.abs(val - zi).max())
-    return int(clear.sum())
 
 
 def _run(V, inp, n=None, W_bits=None):

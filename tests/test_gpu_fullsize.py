@@ -168,7 +168,7 @@ def test_c3_full_size_argmax_sampled_tokens(V):
     """Greedy argmax at the large-vocabulary shape (T=8192, H=3072, V=201088,
     8 shards), in the launch configuration the bench times; sampled tokens
     against the oracle, every token against properties of the merge."""
-    from tests.test_gpu_argmax import check_argmax
+    from tests._cmp import check_argmax
     say("case c3 full-size argmax")
     inp = config_inputs("c3")
     dev = "cuda"

@@ -52,6 +52,14 @@ SIGNATURES = {
                           _P]),
     "vngram_fwd": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I32, _I32, _P, _P,
                           _P, _P, _P]),
+    "vce_fwd_workspace_bytes_ex": (_SZ, [_I64, _I64, _I64, _I64, _I32, _P, _I32]),
+    "vce_fwd_ex": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _I32, _I32,
+                          _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "vce_argmax_workspace_bytes_ex": (_SZ, [_I64, _I64, _I64, _I64, _I32, _P, _I32]),
+    "vce_argmax_ex": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I32, _P, _I32, _P, _P, _P, _P, _P,
+                             _SZ, _P]),
+    "vemb_fwd_ex": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I32, _P, _I32, _P, _P, _P]),
+    "vce_remap": (_I32, [_P, _I64, _P, _I64, _P, _P]),
     "vss_candidates_workspace_bytes": (_SZ, [_I64, _I64]),
     "vss_candidates": (_I32, [_P, _I64, _I64, _I32, _P, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _P]),
 }
@@ -116,6 +124,16 @@ def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+def _layout(shard_rows, num_shards: int):
+    """Host int64 array of an explicit shard layout (num_shards + 1 offsets), or None."""
+    if shard_rows is None:
+        return None
+    rows = [int(x) for x in shard_rows]
+    if len(rows) != num_shards + 1:
+        raise ValueError(f"shard_rows must hold num_shards + 1 = {num_shards + 1} offsets")
+    return (ctypes.c_int64 * len(rows))(*rows)
+
+
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
     if ws is not None:
         return ws
@@ -124,7 +142,11 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
 
 # ------------------------------------------------------------------ sizes
 
-def vce_fwd_workspace_bytes(T, H, V_real, V_pad, num_shards, dtype=VCE_BF16) -> int:
+def vce_fwd_workspace_bytes(T, H, V_real, V_pad, num_shards, dtype=VCE_BF16,
+                            shard_rows=None) -> int:
+    rows = _layout(shard_rows, num_shards)
+    if rows is not None:
+        return int(lib.vce_fwd_workspace_bytes_ex(T, H, V_real, V_pad, num_shards, rows, dtype))
     return int(lib.vce_fwd_workspace_bytes(T, H, V_real, V_pad, num_shards, dtype))
 
 
@@ -136,7 +158,12 @@ def vce_bwd_event_count(T, H, V_real, V_pad, num_shards, dt) -> int:
     return int(lib.vce_bwd_event_count(T, H, V_real, V_pad, num_shards, dt))
 
 
-def vce_argmax_workspace_bytes(T, H, V_real, V_pad, num_shards, dtype=VCE_BF16) -> int:
+def vce_argmax_workspace_bytes(T, H, V_real, V_pad, num_shards, dtype=VCE_BF16,
+                               shard_rows=None) -> int:
+    rows = _layout(shard_rows, num_shards)
+    if rows is not None:
+        return int(lib.vce_argmax_workspace_bytes_ex(T, H, V_real, V_pad, num_shards, rows,
+                                                     dtype))
     return int(lib.vce_argmax_workspace_bytes(T, H, V_real, V_pad, num_shards, dtype))
 
 
@@ -155,9 +182,11 @@ FwdOut = namedtuple("FwdOut", "lse loss loss_sum n_valid n_bad shard_stats")
 
 def vce_fwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, V_real: int,
             num_shards: int, ignore_index: int = -100, *, shard_stats: bool = False,
-            out: Optional[FwdOut] = None, ws: Optional[torch.Tensor] = None,
+            shard_rows=None, out: Optional[FwdOut] = None, ws: Optional[torch.Tensor] = None,
             stream=None) -> FwdOut:
-    """Cross-entropy forward. h [T,H], W [V_pad,H] (same dtype), targets [T] int32."""
+    """Cross-entropy forward. h [T,H], W [V_pad,H] (same dtype), targets [T] int32.
+    shard_rows (optional): num_shards + 1 row offsets of an explicit layout
+    (calls vce_fwd_ex)."""
     T, H = h.shape
     V_pad = W.shape[0]
     dt = _dt(h)
@@ -171,13 +200,19 @@ def vce_fwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, V_real: int
         out = FwdOut(torch.empty(T, **f), torch.empty(T, **f), torch.empty(1, **f),
                      torch.empty(1, **i), torch.empty(1, **i),
                      torch.empty(2, num_shards, T, **f) if shard_stats else None)
-    need = vce_fwd_workspace_bytes(T, H, V_real, V_pad, num_shards, dt)
+    rows = _layout(shard_rows, num_shards)
+    need = vce_fwd_workspace_bytes(T, H, V_real, V_pad, num_shards, dt, shard_rows)
     ws = _workspace(need, dev, ws)
-    st = lib.vce_fwd(_ptr(h), _ptr(W), _ptr(targets), T, H, V_real, V_pad, num_shards,
-                     ignore_index, dt, _ptr(out.lse), _ptr(out.loss), _ptr(out.loss_sum),
-                     _ptr(out.n_valid), _ptr(out.n_bad), _ptr(out.shard_stats), _ptr(ws),
-                     ws.numel(), _stream(stream, dev))
-    _check("vce_fwd", st)
+    outs = (_ptr(out.lse), _ptr(out.loss), _ptr(out.loss_sum), _ptr(out.n_valid),
+            _ptr(out.n_bad), _ptr(out.shard_stats), _ptr(ws), ws.numel(), _stream(stream, dev))
+    if rows is None:
+        st = lib.vce_fwd(_ptr(h), _ptr(W), _ptr(targets), T, H, V_real, V_pad, num_shards,
+                         ignore_index, dt, *outs)
+        _check("vce_fwd", st)
+    else:
+        st = lib.vce_fwd_ex(_ptr(h), _ptr(W), _ptr(targets), T, H, V_real, V_pad, num_shards,
+                            rows, ignore_index, dt, *outs)
+        _check("vce_fwd_ex", st)
     return out
 
 
@@ -237,10 +272,11 @@ ArgOut = namedtuple("ArgOut", "index value shard_value shard_index")
 
 
 def vce_argmax(h: torch.Tensor, W: torch.Tensor, V_real: int, num_shards: int, *,
-               shard_reports: bool = False, out: Optional[ArgOut] = None,
+               shard_reports: bool = False, shard_rows=None, out: Optional[ArgOut] = None,
                ws: Optional[torch.Tensor] = None, stream=None) -> ArgOut:
     """Greedy argmax over the real rows: index [T] int32, value [T] float32, and
-    (shard_reports=True) each shard's (value, index) [num_shards, T]."""
+    (shard_reports=True) each shard's (value, index) [num_shards, T].
+    shard_rows (optional): an explicit layout (calls vce_argmax_ex)."""
     T, H = h.shape
     V_pad = W.shape[0]
     dt = _dt(h)
@@ -253,19 +289,26 @@ def vce_argmax(h: torch.Tensor, W: torch.Tensor, V_real: int, num_shards: int, *
         out = ArgOut(torch.empty(T, **i), torch.empty(T, **f),
                      torch.empty(num_shards, T, **f) if shard_reports else None,
                      torch.empty(num_shards, T, **i) if shard_reports else None)
-    need = vce_argmax_workspace_bytes(T, H, V_real, V_pad, num_shards, dt)
+    rows = _layout(shard_rows, num_shards)
+    need = vce_argmax_workspace_bytes(T, H, V_real, V_pad, num_shards, dt, shard_rows)
     ws = _workspace(need, dev, ws)
-    st = lib.vce_argmax(_ptr(h), _ptr(W), T, H, V_real, V_pad, num_shards, dt, _ptr(out.index),
-                        _ptr(out.value), _ptr(out.shard_value), _ptr(out.shard_index), _ptr(ws),
-                        ws.numel(), _stream(stream, dev))
-    _check("vce_argmax", st)
+    outs = (_ptr(out.index), _ptr(out.value), _ptr(out.shard_value), _ptr(out.shard_index),
+            _ptr(ws), ws.numel(), _stream(stream, dev))
+    if rows is None:
+        st = lib.vce_argmax(_ptr(h), _ptr(W), T, H, V_real, V_pad, num_shards, dt, *outs)
+        _check("vce_argmax", st)
+    else:
+        st = lib.vce_argmax_ex(_ptr(h), _ptr(W), T, H, V_real, V_pad, num_shards, rows, dt,
+                               *outs)
+        _check("vce_argmax_ex", st)
     return out
 
 
 def vemb_fwd(ids: torch.Tensor, W: torch.Tensor, V_real: int, num_shards: int, *,
              out: Optional[torch.Tensor] = None, n_bad: Optional[torch.Tensor] = None,
-             count_bad: bool = True, stream=None):
-    """Masked lookup: returns (out [T,H] in W's dtype, n_bad [1] int32 or None)."""
+             count_bad: bool = True, shard_rows=None, stream=None):
+    """Masked lookup: returns (out [T,H] in W's dtype, n_bad [1] int32 or None).
+    shard_rows (optional): an explicit layout (calls vemb_fwd_ex)."""
     T = ids.shape[0]
     V_pad, H = W.shape
     dt = _dt(W)
@@ -277,10 +320,33 @@ def vemb_fwd(ids: torch.Tensor, W: torch.Tensor, V_real: int, num_shards: int, *
     _need(out, "out", W.dtype, (T, H))
     if count_bad and n_bad is None:
         n_bad = torch.empty(1, dtype=torch.int32, device=dev)
-    st = lib.vemb_fwd(_ptr(ids), _ptr(W), T, H, V_real, V_pad, num_shards, dt, _ptr(out),
-                      _ptr(n_bad) if count_bad else None, _stream(stream, dev))
-    _check("vemb_fwd", st)
+    rows = _layout(shard_rows, num_shards)
+    tail = (_ptr(out), _ptr(n_bad) if count_bad else None, _stream(stream, dev))
+    if rows is None:
+        st = lib.vemb_fwd(_ptr(ids), _ptr(W), T, H, V_real, V_pad, num_shards, dt, *tail)
+        _check("vemb_fwd", st)
+    else:
+        st = lib.vemb_fwd_ex(_ptr(ids), _ptr(W), T, H, V_real, V_pad, num_shards, rows, dt,
+                             *tail)
+        _check("vemb_fwd_ex", st)
     return out, n_bad
+
+
+def vce_remap(ids: torch.Tensor, row_of: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """Mapped ownership: out[t] = row_of[ids[t]] for IDs in [0, V_real), else
+    ids[t] (V_real = row_of's length). out may be ids itself."""
+    T = ids.shape[0]
+    V_real = row_of.shape[0]
+    _need(ids, "ids", torch.int32, (T,))
+    _need(row_of, "row_of", torch.int32, (V_real,))
+    dev = ids.device
+    if out is None:
+        out = torch.empty(T, dtype=torch.int32, device=dev)
+    _need(out, "out", torch.int32, (T,))
+    _check("vce_remap", lib.vce_remap(_ptr(ids), T, _ptr(row_of), V_real, _ptr(out),
+                                      _stream(stream, dev)))
+    return out
 
 
 NgramOut = namedtuple("NgramOut", "out ids2 ids3 n_bad")

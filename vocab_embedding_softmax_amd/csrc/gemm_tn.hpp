@@ -37,8 +37,8 @@
 // in whole 16-byte chunks (a row must therefore be readable up to its valid
 // length rounded up to 16 bytes), so garbage never enters a valid sum.
 //
-// The M side can be cut into equal segments (the vocabulary shards): tiles
-// never cross a segment end, so every tile computes with one shard's rows.
+// The M side can be cut into segments (the vocabulary shards, equal or not):
+// tiles never cross a segment end, so every tile computes with one shard's rows.
 #pragma once
 
 #include <type_traits>
@@ -54,9 +54,7 @@ struct GemmShape {
   int64_t lda;          // elements between consecutive rows of A's storage
   const void* B;
   int64_t ldb;
-  int64_t seg_len;      // M positions per segment
-  int32_t n_seg;        // number of M segments
-  int32_t tiles_per_seg;
+  SegTable seg;         // M segments (vocabulary shards) and their tiles
   int64_t m_total;      // tile ends are clipped to this
   int64_t m_load_end;   // A positions at or past this are never read
   int64_t n_total;      // B positions at or past this are never read
@@ -431,7 +429,7 @@ struct TileGeom {
 // (checked on the host), so the divisions are 32-bit.
 template <int BM, int BN>
 __device__ __forceinline__ TileGeom decode_tile(const GemmShape& g, uint32_t L) {
-  const uint32_t tiles_m = static_cast<uint32_t>(g.n_seg) * static_cast<uint32_t>(g.tiles_per_seg);
+  const uint32_t tiles_m = static_cast<uint32_t>(g.seg.tile[g.seg.n]);
   const uint32_t tiles_n = static_cast<uint32_t>(g.tiles_n);
   const uint32_t group_m = static_cast<uint32_t>(g.group_m);
   const uint32_t per_split = tiles_m * tiles_n;
@@ -445,12 +443,12 @@ __device__ __forceinline__ TileGeom decode_tile(const GemmShape& g, uint32_t L) 
   const uint32_t r_in = rem - grp * in_group;
   const uint32_t tn = r_in / gsz;
   const uint32_t tm = first_m + (r_in - tn * gsz);
-  const uint32_t seg = tm / static_cast<uint32_t>(g.tiles_per_seg);
-  const uint32_t tj = tm - seg * static_cast<uint32_t>(g.tiles_per_seg);
+  const int seg = shard_of_tile(g.seg, tm);
+  const uint32_t tj = tm - static_cast<uint32_t>(g.seg.tile[seg]);
   t.ks = ks;
   t.tm = tm;
-  t.m0 = static_cast<int64_t>(seg) * g.seg_len + static_cast<int64_t>(tj) * BM;
-  t.m_end = min(min(t.m0 + BM, static_cast<int64_t>(seg + 1) * g.seg_len), g.m_total);
+  t.m0 = g.seg.row[seg] + static_cast<int64_t>(tj) * BM;
+  t.m_end = min(min(t.m0 + BM, g.seg.row[seg + 1]), g.m_total);
   t.m_load = min(t.m_end, g.m_load_end);
   t.n0 = static_cast<int64_t>(tn) * BN;
   t.n_end = min(t.n0 + static_cast<int64_t>(BN), g.n_total);
@@ -483,7 +481,9 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
   static_assert(NS >= 2 && SS >= 2 && SS % 2 == 0, "stages");
   static_assert(!SPREAD || NS >= 3, "spread issue needs a free stage ahead");
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
-  __shared__ float2 red[(MODE == EPI_FWD || MODE == EPI_ARGMAX) && WAVES_M > 1 ? (WAVES_M - 1) * BN : 1];
+  __shared__ float2 red[MODE == EPI_FWD && WAVES_M > 1    ? (WAVES_M - 1) * BN
+                      : MODE == EPI_ARGMAX && WAVES_M > 1 ? WAVES_M * BN
+                                                          : 1];
 
   using SA = Stager<E, BM, NW, RB, AKM>;
   using SB = Stager<E, BN, NW, RB, BKM>;
@@ -502,7 +502,7 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
   const int half = lane >> 5, l32 = lane & 31;
 
   // ---- this workgroup's tiles: L = start + wi, start + wi + per_xcd, ... < end
-  const uint32_t total = static_cast<uint32_t>(g.n_seg) * static_cast<uint32_t>(g.tiles_per_seg) *
+  const uint32_t total = static_cast<uint32_t>(g.seg.tile[g.seg.n]) *
                          static_cast<uint32_t>(g.tiles_n) * static_cast<uint32_t>(g.k_splits);
   const uint32_t xcd = blockIdx.x & 7;
   const uint32_t wi = blockIdx.x >> 3;
@@ -868,8 +868,6 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       const int lim = static_cast<int>(max(min(t.m_load - vbase, static_cast<int64_t>(WM)),
                                            static_cast<int64_t>(0)));
       const int lim_l = lim - 4 * half;
-      float bvj[NI];
-      int bij[NI];
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         // this lane's rows in increasing order; strict > keeps the lowest row on ties
@@ -892,32 +890,42 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
           bv = ov;
           bi = oi;
         }
-        bvj[j] = bv;
-        bij[j] = bi < 0 ? -1 : wm * WM + bi;  // row within the tile
         const int col = wn * WN + j * 32 + l32;
-        if (wm > 0 && half == 0) red[(wm - 1) * BN + col] = make_float2(bv, __int_as_float(bij[j]));
-      }
-      if constexpr (WAVES_M > 1) lds_barrier();
-      // the first wave along M merges in wave order (rows increase with the wave)
-      if (wm == 0 && half == 0) {
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-          const int col = wn * WN + j * 32 + l32;
-          float bv = bvj[j];
-          int bi = bij[j];
-#pragma unroll
-          for (int w = 1; w < WAVES_M; ++w) {
-            const float2 o = red[(w - 1) * BN + col];
-            const int oi = __float_as_int(o.y);
-            if (o.x > bv || (o.x == bv && oi >= 0 && (bi < 0 || oi < bi))) {
-              bv = o.x;
-              bi = oi;
-            }
-          }
+        const int tile_row = bi < 0 ? -1 : wm * WM + bi;
+        if constexpr (WAVES_M > 1) {
+          // every wave along M leaves its pair in LDS: nothing is held across the barrier
+          if (half == 0) red[wm * BN + col] = make_float2(bv, __int_as_float(tile_row));
+        } else if (half == 0) {
           const int64_t tt = t.n0 + col;
           if (tt < a.T) {
             a.val[t.tm * a.T + tt] = bv;
-            a.idx[t.tm * a.T + tt] = bi < 0 ? -1 : static_cast<int32_t>(t.m0 + bi);
+            a.idx[t.tm * a.T + tt] = tile_row < 0 ? -1 : static_cast<int32_t>(t.m0 + tile_row);
+          }
+        }
+      }
+      if constexpr (WAVES_M > 1) {
+        lds_barrier();
+        // the first wave along M merges in wave order (rows increase with the wave)
+        if (wm == 0 && half == 0) {
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            const int col = wn * WN + j * 32 + l32;
+            float bv = -INFINITY;
+            int bi = -1;
+#pragma unroll
+            for (int w = 0; w < WAVES_M; ++w) {
+              const float2 o = red[w * BN + col];
+              const int oi = __float_as_int(o.y);
+              if (o.x > bv || (o.x == bv && oi >= 0 && (bi < 0 || oi < bi))) {
+                bv = o.x;
+                bi = oi;
+              }
+            }
+            const int64_t tt = t.n0 + col;
+            if (tt < a.T) {
+              a.val[t.tm * a.T + tt] = bv;
+              a.idx[t.tm * a.T + tt] = bi < 0 ? -1 : static_cast<int32_t>(t.m0 + bi);
+            }
           }
         }
       }

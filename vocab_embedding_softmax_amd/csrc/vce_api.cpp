@@ -19,7 +19,20 @@ bool dtype_ok(int dt) { return dt == VCE_F32 || dt == VCE_BF16; }
 vce_status check_table(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n) {
   if (T < 0 || H <= 0 || V_real < 1 || V_real > V_pad) return VCE_ERR_SHAPE;
   if (T > kMaxDim || H > kMaxDim || V_pad > kMaxDim) return VCE_ERR_SHAPE;
-  if (n < 1 || V_pad % n != 0) return VCE_ERR_SHARD;
+  if (n < 1 || n > vce::kMaxShards || V_pad % n != 0) return VCE_ERR_SHARD;
+  return VCE_OK;
+}
+
+// An explicit layout (shard_rows, num_shards + 1 host values): 0 first,
+// V_pad last, nondecreasing.
+vce_status check_layout(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
+                        const int64_t* rows) {
+  if (T < 0 || H <= 0 || V_real < 1 || V_real > V_pad) return VCE_ERR_SHAPE;
+  if (T > kMaxDim || H > kMaxDim || V_pad > kMaxDim) return VCE_ERR_SHAPE;
+  if (!rows) return VCE_ERR_NULL;
+  if (n < 1 || n > vce::kMaxShards || rows[0] != 0 || rows[n] != V_pad) return VCE_ERR_SHARD;
+  for (int32_t k = 0; k < n; ++k)
+    if (rows[k + 1] < rows[k]) return VCE_ERR_SHARD;
   return VCE_OK;
 }
 
@@ -40,7 +53,9 @@ const char* vce_strerror(vce_status s) {
     case VCE_OK: return "ok";
     case VCE_ERR_NULL: return "a required pointer is NULL";
     case VCE_ERR_SHAPE: return "invalid size argument (T, H, V_real, V_pad, P, capacity or ignore_index)";
-    case VCE_ERR_SHARD: return "num_shards must be >= 1 and divide V_pad";
+    case VCE_ERR_SHARD:
+      return "num_shards must be in [1, 128] and divide V_pad, or shard_rows must run from 0 "
+             "to V_pad without decreasing";
     case VCE_ERR_DTYPE: return "unknown element type, reduction or accumulate flag";
     case VCE_ERR_ALIGN: return "pointers must be 16-byte aligned and H a multiple of 8";
     case VCE_ERR_WORKSPACE: return "workspace missing or smaller than the size query";
@@ -52,7 +67,14 @@ const char* vce_strerror(vce_status s) {
 size_t vce_fwd_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
                                int32_t num_shards, vce_dtype dt) {
   if (check_table(T, H, V_real, V_pad, num_shards) != VCE_OK || !dtype_ok(dt)) return 0;
-  return vce::plan_fwd(T, H, V_real, V_pad, num_shards, nullptr).bytes;
+  return vce::plan_fwd(T, H, V_real, V_pad, num_shards, nullptr, nullptr).bytes;
+}
+
+size_t vce_fwd_workspace_bytes_ex(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                                  int32_t num_shards, const int64_t* shard_rows, vce_dtype dt) {
+  if (check_layout(T, H, V_real, V_pad, num_shards, shard_rows) != VCE_OK || !dtype_ok(dt))
+    return 0;
+  return vce::plan_fwd(T, H, V_real, V_pad, num_shards, shard_rows, nullptr).bytes;
 }
 
 size_t vce_bwd_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
@@ -64,7 +86,15 @@ size_t vce_bwd_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_p
 size_t vce_argmax_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
                                   int32_t num_shards, vce_dtype dt) {
   if (check_table(T, H, V_real, V_pad, num_shards) != VCE_OK || !dtype_ok(dt)) return 0;
-  return vce::plan_argmax(T, H, V_real, V_pad, num_shards, nullptr).bytes;
+  return vce::plan_argmax(T, H, V_real, V_pad, num_shards, nullptr, nullptr).bytes;
+}
+
+size_t vce_argmax_workspace_bytes_ex(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
+                                     int32_t num_shards, const int64_t* shard_rows,
+                                     vce_dtype dt) {
+  if (check_layout(T, H, V_real, V_pad, num_shards, shard_rows) != VCE_OK || !dtype_ok(dt))
+    return 0;
+  return vce::plan_argmax(T, H, V_real, V_pad, num_shards, shard_rows, nullptr).bytes;
 }
 
 size_t vemb_bwd_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_pad) {
@@ -77,13 +107,15 @@ size_t vss_candidates_workspace_bytes(int64_t T, int64_t V) {
   return vce::plan_cand(T, V, nullptr).bytes;
 }
 
-vce_status vce_fwd(const void* h, const void* W, const int32_t* targets, int64_t T, int64_t H,
-                   int64_t V_real, int64_t V_pad, int32_t num_shards, int32_t ignore_index,
-                   vce_dtype dt, float* lse, float* loss, float* loss_sum, int32_t* n_valid,
-                   int32_t* n_bad_target, float* shard_stats, void* ws, size_t ws_bytes,
-                   void* stream) {
+static vce_status fwd_impl(const void* h, const void* W, const int32_t* targets, int64_t T,
+                           int64_t H, int64_t V_real, int64_t V_pad, int32_t num_shards,
+                           const int64_t* shard_rows, int32_t ignore_index, vce_dtype dt,
+                           float* lse, float* loss, float* loss_sum, int32_t* n_valid,
+                           int32_t* n_bad_target, float* shard_stats, void* ws, size_t ws_bytes,
+                           void* stream) {
   if (!dtype_ok(dt)) return VCE_ERR_DTYPE;
-  vce_status st = check_table(T, H, V_real, V_pad, num_shards);
+  vce_status st = shard_rows ? check_layout(T, H, V_real, V_pad, num_shards, shard_rows)
+                             : check_table(T, H, V_real, V_pad, num_shards);
   if (st != VCE_OK) return st;
   if ((st = check_ignore(ignore_index, V_real)) != VCE_OK) return st;
   if (!loss_sum || !n_valid || !n_bad_target) return VCE_ERR_NULL;
@@ -93,13 +125,32 @@ vce_status vce_fwd(const void* h, const void* W, const int32_t* targets, int64_t
                 !aligned4(loss) || (shard_stats && !aligned4(shard_stats))))
     return VCE_ERR_ALIGN;
   if (!aligned4(loss_sum) || !aligned4(n_valid) || !aligned4(n_bad_target)) return VCE_ERR_ALIGN;
-  const vce::FwdPlan probe = vce::plan_fwd(T, H, V_real, V_pad, num_shards, nullptr);
+  const vce::FwdPlan probe = vce::plan_fwd(T, H, V_real, V_pad, num_shards, shard_rows, nullptr);
   if (T > 0 && (!ws || ws_bytes < probe.bytes)) return VCE_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return VCE_ERR_ALIGN;
-  const vce::FwdPlan p = vce::plan_fwd(T, H, V_real, V_pad, num_shards, ws);
+  const vce::FwdPlan p = vce::plan_fwd(T, H, V_real, V_pad, num_shards, shard_rows, ws);
   return hip_status(vce::run_ce_fwd(h, W, targets, T, H, V_real, V_pad, num_shards, ignore_index,
                                     dt == VCE_BF16, lse, loss, loss_sum, n_valid, n_bad_target,
                                     shard_stats, p, static_cast<hipStream_t>(stream)));
+}
+
+vce_status vce_fwd(const void* h, const void* W, const int32_t* targets, int64_t T, int64_t H,
+                   int64_t V_real, int64_t V_pad, int32_t num_shards, int32_t ignore_index,
+                   vce_dtype dt, float* lse, float* loss, float* loss_sum, int32_t* n_valid,
+                   int32_t* n_bad_target, float* shard_stats, void* ws, size_t ws_bytes,
+                   void* stream) {
+  return fwd_impl(h, W, targets, T, H, V_real, V_pad, num_shards, nullptr, ignore_index, dt, lse,
+                  loss, loss_sum, n_valid, n_bad_target, shard_stats, ws, ws_bytes, stream);
+}
+
+vce_status vce_fwd_ex(const void* h, const void* W, const int32_t* targets, int64_t T, int64_t H,
+                      int64_t V_real, int64_t V_pad, int32_t num_shards,
+                      const int64_t* shard_rows, int32_t ignore_index, vce_dtype dt, float* lse,
+                      float* loss, float* loss_sum, int32_t* n_valid, int32_t* n_bad_target,
+                      float* shard_stats, void* ws, size_t ws_bytes, void* stream) {
+  if (!shard_rows) return VCE_ERR_NULL;
+  return fwd_impl(h, W, targets, T, H, V_real, V_pad, num_shards, shard_rows, ignore_index, dt,
+                  lse, loss, loss_sum, n_valid, n_bad_target, shard_stats, ws, ws_bytes, stream);
 }
 
 vce_status vce_bwd(const void* h, const void* W, const int32_t* targets, const float* lse,
@@ -148,12 +199,14 @@ vce_status vce_bwd_timed(const void* h, const void* W, const int32_t* targets, c
                                     p, static_cast<hipStream_t>(stream), events));
 }
 
-vce_status vce_argmax(const void* h, const void* W, int64_t T, int64_t H, int64_t V_real,
-                      int64_t V_pad, int32_t num_shards, vce_dtype dt, int32_t* index,
-                      float* value, float* shard_value, int32_t* shard_index, void* ws,
-                      size_t ws_bytes, void* stream) {
+static vce_status argmax_impl(const void* h, const void* W, int64_t T, int64_t H,
+                              int64_t V_real, int64_t V_pad, int32_t num_shards,
+                              const int64_t* shard_rows, vce_dtype dt, int32_t* index,
+                              float* value, float* shard_value, int32_t* shard_index, void* ws,
+                              size_t ws_bytes, void* stream) {
   if (!dtype_ok(dt)) return VCE_ERR_DTYPE;
-  vce_status st = check_table(T, H, V_real, V_pad, num_shards);
+  vce_status st = shard_rows ? check_layout(T, H, V_real, V_pad, num_shards, shard_rows)
+                             : check_table(T, H, V_real, V_pad, num_shards);
   if (st != VCE_OK) return st;
   if (T > 0 && (!h || !W || !index || !value)) return VCE_ERR_NULL;
   if (H % 8 != 0) return VCE_ERR_ALIGN;
@@ -161,27 +214,72 @@ vce_status vce_argmax(const void* h, const void* W, int64_t T, int64_t H, int64_
                 (shard_value && !aligned4(shard_value)) ||
                 (shard_index && !aligned4(shard_index))))
     return VCE_ERR_ALIGN;
-  const vce::ArgPlan probe = vce::plan_argmax(T, H, V_real, V_pad, num_shards, nullptr);
+  const vce::ArgPlan probe =
+      vce::plan_argmax(T, H, V_real, V_pad, num_shards, shard_rows, nullptr);
   if (T > 0 && (!ws || ws_bytes < probe.bytes)) return VCE_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return VCE_ERR_ALIGN;
-  const vce::ArgPlan p = vce::plan_argmax(T, H, V_real, V_pad, num_shards, ws);
+  const vce::ArgPlan p = vce::plan_argmax(T, H, V_real, V_pad, num_shards, shard_rows, ws);
   return hip_status(vce::run_argmax(h, W, T, H, V_real, V_pad, num_shards, dt == VCE_BF16, index,
                                     value, shard_value, shard_index, p,
                                     static_cast<hipStream_t>(stream)));
 }
 
-vce_status vemb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, int64_t V_real,
-                    int64_t V_pad, int32_t num_shards, vce_dtype dt, void* out, int32_t* n_bad_id,
-                    void* stream) {
+vce_status vce_argmax(const void* h, const void* W, int64_t T, int64_t H, int64_t V_real,
+                      int64_t V_pad, int32_t num_shards, vce_dtype dt, int32_t* index,
+                      float* value, float* shard_value, int32_t* shard_index, void* ws,
+                      size_t ws_bytes, void* stream) {
+  return argmax_impl(h, W, T, H, V_real, V_pad, num_shards, nullptr, dt, index, value,
+                     shard_value, shard_index, ws, ws_bytes, stream);
+}
+
+vce_status vce_argmax_ex(const void* h, const void* W, int64_t T, int64_t H, int64_t V_real,
+                         int64_t V_pad, int32_t num_shards, const int64_t* shard_rows,
+                         vce_dtype dt, int32_t* index, float* value, float* shard_value,
+                         int32_t* shard_index, void* ws, size_t ws_bytes, void* stream) {
+  if (!shard_rows) return VCE_ERR_NULL;
+  return argmax_impl(h, W, T, H, V_real, V_pad, num_shards, shard_rows, dt, index, value,
+                     shard_value, shard_index, ws, ws_bytes, stream);
+}
+
+static vce_status emb_fwd_impl(const int32_t* ids, const void* W, int64_t T, int64_t H,
+                               int64_t V_real, int64_t V_pad, int32_t num_shards,
+                               const int64_t* shard_rows, vce_dtype dt, void* out,
+                               int32_t* n_bad_id, void* stream) {
   if (!dtype_ok(dt)) return VCE_ERR_DTYPE;
-  vce_status st = check_table(T, H, V_real, V_pad, num_shards);
+  vce_status st = shard_rows ? check_layout(T, H, V_real, V_pad, num_shards, shard_rows)
+                             : check_table(T, H, V_real, V_pad, num_shards);
   if (st != VCE_OK) return st;
   if (T > 0 && (!ids || !W || !out)) return VCE_ERR_NULL;
   if (H % 8 != 0) return VCE_ERR_ALIGN;
   if (T > 0 && (!aligned4(ids) || !aligned16(W) || !aligned16(out))) return VCE_ERR_ALIGN;
   if (n_bad_id && !aligned4(n_bad_id)) return VCE_ERR_ALIGN;
-  return hip_status(vce::run_emb_fwd(ids, W, T, H, V_real, V_pad, num_shards, esize_of(dt), out,
-                                     n_bad_id, static_cast<hipStream_t>(stream)));
+  return hip_status(vce::run_emb_fwd(ids, W, T, H, V_real,
+                                     vce::shard_segments(num_shards, shard_rows, V_pad),
+                                     esize_of(dt), out, n_bad_id,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+vce_status vemb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, int64_t V_real,
+                    int64_t V_pad, int32_t num_shards, vce_dtype dt, void* out, int32_t* n_bad_id,
+                    void* stream) {
+  return emb_fwd_impl(ids, W, T, H, V_real, V_pad, num_shards, nullptr, dt, out, n_bad_id,
+                      stream);
+}
+
+vce_status vemb_fwd_ex(const int32_t* ids, const void* W, int64_t T, int64_t H, int64_t V_real,
+                       int64_t V_pad, int32_t num_shards, const int64_t* shard_rows,
+                       vce_dtype dt, void* out, int32_t* n_bad_id, void* stream) {
+  if (!shard_rows) return VCE_ERR_NULL;
+  return emb_fwd_impl(ids, W, T, H, V_real, V_pad, num_shards, shard_rows, dt, out, n_bad_id,
+                      stream);
+}
+
+vce_status vce_remap(const int32_t* in, int64_t T, const int32_t* map, int64_t V_real,
+                     int32_t* out, void* stream) {
+  if (T < 0 || T > kMaxDim || V_real < 1 || V_real > kMaxDim) return VCE_ERR_SHAPE;
+  if (T > 0 && (!in || !map || !out)) return VCE_ERR_NULL;
+  if (T > 0 && (!aligned4(in) || !aligned4(map) || !aligned4(out))) return VCE_ERR_ALIGN;
+  return hip_status(vce::run_remap(in, T, map, V_real, out, static_cast<hipStream_t>(stream)));
 }
 
 vce_status vngram_fwd(const int32_t* ids, const void* E, const void* E2, const void* E3,

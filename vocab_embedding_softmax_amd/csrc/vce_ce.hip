@@ -23,15 +23,38 @@ namespace vce {
 
 // ------------------------------------------------------------------ planning
 
-static int64_t tiles_per_shard(int64_t S) { return cdiv(S, kTileM); }
+SegTable shard_segments(int32_t n, const int64_t* rows, int64_t V_pad) {
+  SegTable sg{};
+  sg.n = n;
+  int32_t tiles = 0;
+  for (int32_t k = 0; k <= n; ++k) {
+    sg.row[k] = rows ? rows[k] : (V_pad / n) * k;
+    sg.tile[k] = tiles;
+    if (k < n) {
+      const int64_t len = (rows ? rows[k + 1] : (V_pad / n) * (k + 1)) - sg.row[k];
+      tiles += static_cast<int32_t>(cdiv(len, kTileM));
+    }
+  }
+  return sg;
+}
 
-FwdPlan plan_fwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, void* ws) {
+SegTable one_segment(int64_t rows) {
+  SegTable sg{};
+  sg.n = 1;
+  sg.row[0] = 0;
+  sg.row[1] = rows;
+  sg.tile[0] = 0;
+  sg.tile[1] = static_cast<int32_t>(cdiv(rows, kTileM));
+  return sg;
+}
+
+FwdPlan plan_fwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
+                 const int64_t* rows, void* ws) {
   (void)H;
   (void)V_real;
   FwdPlan p{};
-  p.S = V_pad / n;
-  p.tiles_per_seg = tiles_per_shard(p.S);
-  p.tiles_m = p.tiles_per_seg * n;
+  p.seg = shard_segments(n, rows, V_pad);
+  p.tiles_m = p.seg.tile[n];
   p.tiles_n = cdiv(T, kTileN);
   p.merge_blocks = cdiv(T, kMergeTok);
   Carve c(ws);
@@ -44,13 +67,13 @@ FwdPlan plan_fwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
   return p;
 }
 
-ArgPlan plan_argmax(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, void* ws) {
+ArgPlan plan_argmax(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
+                    const int64_t* rows, void* ws) {
   (void)H;
   (void)V_real;
   ArgPlan p{};
-  p.S = V_pad / n;
-  p.tiles_per_seg = tiles_per_shard(p.S);
-  p.tiles_m = p.tiles_per_seg * n;
+  p.seg = shard_segments(n, rows, V_pad);
+  p.tiles_m = p.seg.tile[n];
   p.tiles_n = cdiv(T, kTileN);
   Carve c(ws);
   p.val = c.take<float>(static_cast<size_t>(p.tiles_m * T));
@@ -104,7 +127,7 @@ BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
 __global__ __launch_bounds__(256) void k_ce_merge(
     const float2* __restrict__ stats, const float* __restrict__ zt,
     const int32_t* __restrict__ targets, int64_t T, int64_t V_real, int32_t ignore_index,
-    int32_t n_seg, int64_t tiles_per_seg, float* __restrict__ lse, float* __restrict__ loss,
+    const SegTable sg, float* __restrict__ lse, float* __restrict__ loss,
     float* __restrict__ shard_stats, float* __restrict__ part_loss,
     int32_t* __restrict__ part_nv, int32_t* __restrict__ part_nb) {
   constexpr int NSUB = 256 / kMergeTok;
@@ -115,10 +138,12 @@ __global__ __launch_bounds__(256) void k_ce_merge(
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kMergeTok + tok;
   const bool tin = t < T;
   float M = -INFINITY, Ssum = 0.0f;
+  const int32_t n_seg = sg.n;
   for (int32_t k = 0; k < n_seg; ++k) {
     float mk = -INFINITY, sk = 0.0f;
+    const int64_t tiles_per_seg = sg.tile[k + 1] - sg.tile[k];
     if (tin) {
-      const float2* st = stats + (static_cast<int64_t>(k) * tiles_per_seg) * T + t;
+      const float2* st = stats + static_cast<int64_t>(sg.tile[k]) * T + t;
       int64_t j = sub;
       for (; j + 3 * NSUB < tiles_per_seg; j += 4 * NSUB) {
         const float2 v0 = st[j * T];
@@ -221,8 +246,8 @@ __device__ __forceinline__ void argmax_merge(float& bv, int32_t& bi, float v, in
 // (what one rank would hold), then the shard reports into the global argmax.
 // 32 tokens per workgroup, 8 lane groups over every 8th tile of a shard.
 __global__ __launch_bounds__(256) void k_argmax_merge(
-    const float* __restrict__ val, const int32_t* __restrict__ idx, int64_t T, int32_t n_seg,
-    int64_t tiles_per_seg, int32_t* __restrict__ index, float* __restrict__ value,
+    const float* __restrict__ val, const int32_t* __restrict__ idx, int64_t T,
+    const SegTable sg, int32_t* __restrict__ index, float* __restrict__ value,
     float* __restrict__ shard_value, int32_t* __restrict__ shard_index) {
   constexpr int NSUB = 256 / kMergeTok;
   __shared__ float rv[NSUB][kMergeTok];
@@ -234,11 +259,12 @@ __global__ __launch_bounds__(256) void k_argmax_merge(
   const bool tin = t < T;
   float gv = -INFINITY;
   int32_t gi = -1;
-  for (int32_t k = 0; k < n_seg; ++k) {
+  for (int32_t k = 0; k < sg.n; ++k) {
     float bv = -INFINITY;
     int32_t bi = -1;
+    const int64_t tiles_per_seg = sg.tile[k + 1] - sg.tile[k];
     if (tin) {
-      const int64_t base = static_cast<int64_t>(k) * tiles_per_seg * T + t;
+      const int64_t base = static_cast<int64_t>(sg.tile[k]) * T + t;
       for (int64_t j = sub; j < tiles_per_seg; j += NSUB)
         argmax_merge(bv, bi, val[base + j * T], idx[base + j * T]);
     }
@@ -314,7 +340,7 @@ constexpr Staging staging() {
 
 template <typename E, int MODE, bool AKM = false, bool BKM = false>
 static hipError_t launch_gemm(const GemmShape& g, const EpiArgs& e, hipStream_t s) {
-  const int64_t tiles = static_cast<int64_t>(g.n_seg) * g.tiles_per_seg * g.tiles_n * g.k_splits;
+  const int64_t tiles = static_cast<int64_t>(g.seg.tile[g.seg.n]) * g.tiles_n * g.k_splits;
   if (tiles <= 0) return hipSuccess;
   if (tiles >= (int64_t{1} << 31)) return hipErrorInvalidValue;
   const int64_t blocks = persistent_blocks(tiles);
@@ -340,9 +366,7 @@ hipError_t run_ce_fwd(const void* h, const void* W, const int32_t* targets, int6
   g.lda = H;
   g.B = h;
   g.ldb = H;
-  g.seg_len = p.S;
-  g.n_seg = n;
-  g.tiles_per_seg = static_cast<int32_t>(p.tiles_per_seg);
+  g.seg = p.seg;
   g.m_total = V_pad;
   g.m_load_end = V_real;
   g.n_total = T;
@@ -360,7 +384,7 @@ hipError_t run_ce_fwd(const void* h, const void* W, const int32_t* targets, int6
   hipError_t err = bf16 ? launch_gemm<uint16_t, EPI_FWD>(g, e, s) : launch_gemm<float, EPI_FWD>(g, e, s);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_ce_merge, dim3(static_cast<uint32_t>(p.merge_blocks)), dim3(256), 0, s,
-                     p.stats, p.zt, targets, T, V_real, ignore_index, n, p.tiles_per_seg, lse,
+                     p.stats, p.zt, targets, T, V_real, ignore_index, p.seg, lse,
                      loss, shard_stats, p.part_loss, p.part_nv, p.part_nb);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(k_ce_finalize, dim3(1), dim3(256), 0, s, p.part_loss, p.part_nv, p.part_nb,
@@ -378,9 +402,7 @@ hipError_t run_argmax(const void* h, const void* W, int64_t T, int64_t H, int64_
   g.lda = H;
   g.B = h;
   g.ldb = H;
-  g.seg_len = p.S;
-  g.n_seg = n;
-  g.tiles_per_seg = static_cast<int32_t>(p.tiles_per_seg);
+  g.seg = p.seg;
   g.m_total = V_pad;
   g.m_load_end = V_real;
   g.n_total = T;
@@ -397,7 +419,7 @@ hipError_t run_argmax(const void* h, const void* W, int64_t T, int64_t H, int64_
       bf16 ? launch_gemm<uint16_t, EPI_ARGMAX>(g, e, s) : launch_gemm<float, EPI_ARGMAX>(g, e, s);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_argmax_merge, dim3(static_cast<uint32_t>(cdiv(T, kMergeTok))), dim3(256), 0,
-                     s, p.val, p.idx, T, n, p.tiles_per_seg, index, value, shard_value,
+                     s, p.val, p.idx, T, p.seg, index, value, shard_value,
                      shard_index);
   return hipGetLastError();
 }
@@ -453,9 +475,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       g.lda = H;
       g.B = h;
       g.ldb = H;
-      g.seg_len = Vc;
-      g.n_seg = 1;
-      g.tiles_per_seg = static_cast<int32_t>(cdiv(Vc, kTileM));
+      g.seg = one_segment(Vc);
       g.m_total = Vc;
       g.m_load_end = kreal;
       g.n_total = T;
@@ -486,9 +506,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       g.lda = p.ldC;
       g.B = Wp + c0 * H;
       g.ldb = H;
-      g.seg_len = T;
-      g.n_seg = 1;
-      g.tiles_per_seg = static_cast<int32_t>(cdiv(T, kTileM));
+      g.seg = one_segment(T);
       g.m_total = T;
       g.m_load_end = T;
       g.n_total = H;
@@ -515,9 +533,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       g.lda = p.ldC;
       g.B = h;
       g.ldb = H;
-      g.seg_len = Vc;
-      g.n_seg = 1;
-      g.tiles_per_seg = static_cast<int32_t>(cdiv(Vc, kTileM));
+      g.seg = one_segment(Vc);
       g.m_total = Vc;
       g.m_load_end = Vc;
       g.n_total = H;

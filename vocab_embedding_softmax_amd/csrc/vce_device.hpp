@@ -13,6 +13,38 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
+
+// Vocabulary shards of one table: shard k owns rows [row[k], row[k+1]) of the
+// table (contiguous, in order, possibly empty), and its GEMM tiles are
+// tile[k] .. tile[k+1]-1 (tiles never cross a shard end). Passed by value to
+// the kernels (launch arguments), so the library keeps no state.
+constexpr int kMaxShards = 128;
+struct SegTable {
+  int64_t row[kMaxShards + 1];
+  int32_t tile[kMaxShards + 1];
+  int32_t n;
+};
+
+// Shard of a row r (0 <= r < row[n]) by binary search over the offsets: the
+// last k with row[k] <= r (empty shards are skipped).
+__device__ __forceinline__ int shard_of_row(const SegTable& sg, int64_t r) {
+  int lo = 0, hi = sg.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (sg.row[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Shard of a tile t (0 <= t < tile[n]): the last k with tile[k] <= t.
+__device__ __forceinline__ int shard_of_tile(const SegTable& sg, int64_t t) {
+  int lo = 0, hi = sg.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (sg.tile[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

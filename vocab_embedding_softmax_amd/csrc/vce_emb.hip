@@ -104,8 +104,9 @@ CandPlan plan_cand(int64_t T, int64_t V, void* ws) {
 constexpr int kRowsPerWave = 1;
 __global__ __launch_bounds__(256) void k_vemb_fwd(const int32_t* __restrict__ ids,
                                                   const char* __restrict__ W, int64_t T,
-                                                  int64_t row_bytes, int64_t V_real, int64_t S,
-                                                  char* __restrict__ out, int32_t* n_bad) {
+                                                  int64_t row_bytes, int64_t V_real,
+                                                  const SegTable sg, char* __restrict__ out,
+                                                  int32_t* n_bad) {
   constexpr int U = 8;  // pieces per lane and row held at once
   constexpr int RW = kRowsPerWave;
   const int lane = threadIdx.x & 63;
@@ -133,9 +134,9 @@ __global__ __launch_bounds__(256) void k_vemb_fwd(const int32_t* __restrict__ id
     const int64_t id = ids[t];
     // owner test, then the local index within the owner's slice
     owned[r] = (t0 + r < T) && (id >= 0) && (id < V_real);
-    const int64_t k = owned[r] ? id / S : 0;
-    const int64_t local = owned[r] ? id - k * S : 0;
-    src[r] = reinterpret_cast<const u32x4*>(W + (k * S + local) * row_bytes);
+    const int k = owned[r] ? shard_of_row(sg, id) : 0;
+    const int64_t local = owned[r] ? id - sg.row[k] : 0;
+    src[r] = reinterpret_cast<const u32x4*>(W + (sg.row[k] + local) * row_bytes);
     dst[r] = reinterpret_cast<u32x4*>(out + t * row_bytes);
   }
   for (int64_t c0 = 0; c0 < nvec; c0 += 64 * U) {
@@ -161,6 +162,25 @@ __global__ __launch_bounds__(256) void k_vemb_fwd(const int32_t* __restrict__ id
 
 __global__ void k_zero_i32(int32_t* p) {
   if (threadIdx.x == 0) *p = 0;
+}
+
+// out[t] = map[in[t]] for in[t] in [0, V_real); any other value passes through
+// (explicitly mapped class ownership: class -> physical row, or back).
+__global__ __launch_bounds__(256) void k_remap(const int32_t* __restrict__ in, int64_t T,
+                                               const int32_t* __restrict__ map, int64_t V_real,
+                                               int32_t* __restrict__ out) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= T) return;
+  const int64_t v = in[t];
+  out[t] = (v >= 0 && v < V_real) ? map[v] : static_cast<int32_t>(v);
+}
+
+hipError_t run_remap(const int32_t* in, int64_t T, const int32_t* map, int64_t V_real,
+                     int32_t* out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_remap, dim3(static_cast<uint32_t>(cdiv(T, 256))), dim3(256), 0, s, in, T,
+                     map, V_real, out);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ hashed n-grams
@@ -897,18 +917,17 @@ __global__ void k_cand_counts(const int32_t* __restrict__ uidx, int64_t V, int64
 // ------------------------------------------------------------------ launchers
 
 hipError_t run_emb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, int64_t V_real,
-                       int64_t V_pad, int32_t n, size_t esize, void* out, int32_t* n_bad,
+                       const SegTable& sg, size_t esize, void* out, int32_t* n_bad,
                        hipStream_t s) {
   if (T == 0) {
     if (!n_bad) return hipSuccess;
     hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(64), 0, s, n_bad);
     return hipGetLastError();
   }
-  const int64_t S = V_pad / n;
   const int64_t row_bytes = H * static_cast<int64_t>(esize);
   const int64_t blocks = cdiv(T, 4 * kRowsPerWave);
   hipLaunchKernelGGL(k_vemb_fwd, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, ids,
-                     static_cast<const char*>(W), T, row_bytes, V_real, S,
+                     static_cast<const char*>(W), T, row_bytes, V_real, sg,
                      static_cast<char*>(out), n_bad);
   return hipGetLastError();
 }

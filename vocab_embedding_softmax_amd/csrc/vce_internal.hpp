@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "vce_device.hpp"
+
 namespace vce {
 
 #ifndef VCE_WAVES_M
@@ -95,9 +97,17 @@ struct Carve {
   }
 };
 
+// Segments of a table: the given shard row offsets (num_shards + 1 values,
+// validated by the caller) or, with none, equal shards of V_pad / n rows;
+// tiles of kTileM rows per shard, never crossing a shard end.
+SegTable shard_segments(int32_t n, const int64_t* rows, int64_t V_pad);
+// One segment of `rows` rows.
+SegTable one_segment(int64_t rows);
+
 // Forward cross-entropy plan: vocabulary tiles per shard, token tiles.
 struct FwdPlan {
-  int64_t S, tiles_per_seg, tiles_m, tiles_n, merge_blocks;
+  SegTable seg;
+  int64_t tiles_m, tiles_n, merge_blocks;
   float2* stats;
   float* zt;
   float* part_loss;
@@ -105,17 +115,20 @@ struct FwdPlan {
   int32_t* part_nb;
   size_t bytes;
 };
-FwdPlan plan_fwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, void* ws);
+FwdPlan plan_fwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
+                 const int64_t* rows, void* ws);
 
 // Greedy argmax plan: per-tile reports (largest logit, its row) of every
 // vocabulary tile of every shard, [tiles_m][T] each.
 struct ArgPlan {
-  int64_t S, tiles_per_seg, tiles_m, tiles_n;
+  SegTable seg;
+  int64_t tiles_m, tiles_n;
   float* val;
   int32_t* idx;
   size_t bytes;
 };
-ArgPlan plan_argmax(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, void* ws);
+ArgPlan plan_argmax(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
+                    const int64_t* rows, void* ws);
 
 // Backward plan: the vocabulary is processed in chunks; only one chunk's
 // G = [T][chunk] is staged. A chunk is a group of whole shards, or a piece of
@@ -203,8 +216,11 @@ hipError_t run_argmax(const void* h, const void* W, int64_t T, int64_t H, int64_
                       float* shard_value, int32_t* shard_index, const ArgPlan& p, hipStream_t s);
 
 hipError_t run_emb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, int64_t V_real,
-                       int64_t V_pad, int32_t n, size_t esize, void* out, int32_t* n_bad,
+                       const SegTable& sg, size_t esize, void* out, int32_t* n_bad,
                        hipStream_t s);
+
+hipError_t run_remap(const int32_t* in, int64_t T, const int32_t* map, int64_t V_real,
+                     int32_t* out, hipStream_t s);
 
 hipError_t run_ngram_fwd(const int32_t* ids, const void* E0, const void* E2, const void* E3,
                          int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int64_t rows2,
