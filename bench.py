@@ -315,6 +315,32 @@ def main():
                      "achieved_TFLOP_s": flop_gemm / (ms_arg * 1e-3) / 1e12,
                      "frac": flop_gemm / (ms_arg * 1e-3) / PEAK_BF16}
     log(f"[bench] argmax {ms_arg:.3f} ms/call")
+    # The forward under an explicit uneven layout of the same table (seeded:
+    # one empty and one one-row shard among n, random cut points elsewhere),
+    # timed beside the even layout on the same inputs.
+    from synth import make_layout
+    rows = [int(x) for x in make_layout(Vp, n, seed=8, n_empty=1, n_single=1)]
+    ws_u = torch.empty(V.vce_fwd_workspace_bytes(T, H, Vr, Vp, n, dt_code, shard_rows=rows),
+                       dtype=torch.uint8, device=dev)
+
+    def time_fwd(**kw):
+        V.vce_fwd(h, W, tg, Vr, n, inp.ignore_index, out=fo, **kw)
+        e0.record(stream)
+        for _ in range(reps):
+            V.vce_fwd(h, W, tg, Vr, n, inp.ignore_index, out=fo, **kw)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_even = time_fwd(ws=ws["fwd"])
+    ms_unev = time_fwd(ws=ws_u, shard_rows=rows)
+    sizes = np.diff(np.asarray(rows))
+    res["uneven_layout"] = {
+        "call": "vce_fwd_ex", "shard_rows_min_max": [int(sizes.min()), int(sizes.max())],
+        "ms": ms_unev, "ms_even_layout": ms_even,
+        "achieved_TFLOP_s": flop_gemm / (ms_unev * 1e-3) / 1e12,
+        "frac": flop_gemm / (ms_unev * 1e-3) / PEAK_BF16}
+    log(f"[bench] forward, uneven layout {ms_unev:.3f} ms (even {ms_even:.3f} ms)")
     if tied:
         # OT-H step: the tied step plus a second, untied head two tokens ahead
         # at weight 0.1 (its own table of the same shape, drawn on the device:
