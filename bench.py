@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4", choices=["c3", "c4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sampled", action="store_true",
+                    help="skip the sampled-softmax field (its own T=16384, H=1536 workload)")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens in the oracle's CPU-baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
@@ -415,6 +417,45 @@ def main():
         del src, dst
     del ws, dh, dW, W, h, ws_arg, out_arg
     torch.cuda.empty_cache()
+    if not a.no_sampled:
+        # Sampled-softmax step on its own workload (T=16384, H=1536, V=131072,
+        # P=16384): candidates, gather of W[cand], CE fwd+bwd over the
+        # candidates, scatter of dW[cand] back into the full table (written
+        # whole). MFMA work = 8*T*H*n_cand.
+        inp5 = config_inputs("c5")
+        T5, H5, V5, P5 = inp5.T, inp5.H, inp5.V_real, inp5.P
+        h5 = V.from_bits(inp5.h, inp5.dtype, dev)
+        W5 = V.from_bits(inp5.W, inp5.dtype, dev)
+        tg5 = torch.from_numpy(inp5.targets).to(dev)
+        perm5 = torch.from_numpy(inp5.perm).to(dev)
+        ws5 = V.Workspaces(dev, cand=V.vss_candidates_workspace_bytes(T5, V5),
+                           fwd=V.vce_fwd_workspace_bytes(T5, H5, P5, P5, 1, dt_code),
+                           bwd=V.vce_bwd_workspace_bytes(T5, H5, P5, P5, 1, dt_code),
+                           emb=V.vemb_bwd_workspace_bytes(P5, H5, V5, V5))
+        dW5 = torch.empty(V5, H5, **f32)
+
+        def samp():
+            return V.sampled_step(h5, W5, tg5, perm5, P5, inp5.ignore_index, ws=ws5, dW=dW5)
+
+        r5 = samp()
+        torch.cuda.synchronize()
+        n_cand = int(r5.extra["n_cand"].item())
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps5 = 5
+        e0.record(stream)
+        for _ in range(reps5):
+            samp()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms5 = e0.elapsed_time(e1) / reps5
+        res["sampled_softmax"] = {
+            "workload": f"T={T5}, H={H5}, V={V5}, P={P5}, Zipf(1.1) targets",
+            "n_cand": n_cand, "ms": ms5, "tokens_s": T5 / (ms5 * 1e-3),
+            "mfma_frac": 8.0 * T5 * H5 * n_cand / (ms5 * 1e-3) / PEAK_BF16}
+        log(f"[bench] sampled-softmax step {ms5:.3f} ms")
+        del h5, W5, ws5, dW5, r5
+        torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
         log(f"[bench] CPU baseline: oracle on {a.cpu_tokens} tokens")
         res["cpu_baseline"] = cpu_baseline(inp, a.cpu_tokens)

@@ -82,7 +82,7 @@ struct GradArgs {
   const int32_t* n_valid;
   int64_t v_off;        // vocabulary row of the GEMM's row 0
   int32_t reduction;    // 0 mean over valid tokens, 1 sum
-  int32_t vec_store;    // 1 if every tile start is a multiple of 4 columns
+  int32_t vec_store;    // 1 if tile rows start at multiples of 8 and ldG is one (16-byte stores)
   void* G;              // [T][ldG]
   int64_t ldG;
 };
@@ -953,41 +953,72 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
         const float nl = lv[j] * kLog2e;
         E* grow = Gp + tt * gr.ldG + vb;
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MI; ++i) {
+          float gv[16];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r0 = i * 32 + 8 * q;
-            float gv[4];
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
+              const int r = i * 32 + 8 * q + c;
               const float p = fast_exp2(fmaf(acc[i][j][4 * q + c], kLog2e, -nl));
-              const float oh = (r0 + c == y_l) ? 1.0f : 0.0f;
+              const float oh = (r == y_l) ? 1.0f : 0.0f;
               // select, never multiply, so a non-finite p of a discarded entry cannot leak
-              gv[c] = (r0 + c < lim_l) ? scale * (p - oh) : 0.0f;
+              gv[4 * q + c] = (r < lim_l) ? scale * (p - oh) : 0.0f;
             }
-            if (!tin) continue;
-            if constexpr (sizeof(E) == 2) {
-              if (gr.vec_store && r0 + 3 < end_l) {
-                u32x2 pk;
-                pk.x = pack_bf16x2(gv[0], gv[1]);
-                pk.y = pack_bf16x2(gv[2], gv[3]);
-                *reinterpret_cast<u32x2*>(grow + r0) = pk;
+          if constexpr (sizeof(E) == 2) {
+            // the 32-row block lies inside the tile for both lanes of the pair
+            if (gr.vec_store && tin && i * 32 + 32 <= end_l + 4 * half) {
+              // lane pairs (l, l^32) trade quarter-blocks so that each lane
+              // holds 8 consecutive rows twice: 16-byte stores
+              u32x2 P[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                P[q].x = pack_bf16x2(gv[4 * q], gv[4 * q + 1]);
+                P[q].y = pack_bf16x2(gv[4 * q + 2], gv[4 * q + 3]);
+              }
+              const u32x2 sa = half ? P[0] : P[1];
+              const u32x2 sb = half ? P[2] : P[3];
+              u32x2 ra, rb;
+              ra.x = __shfl_xor(sa.x, 32);
+              ra.y = __shfl_xor(sa.y, 32);
+              rb.x = __shfl_xor(sb.x, 32);
+              rb.y = __shfl_xor(sb.y, 32);
+              u32x4 p0, p1;
+              if (half) {
+                p0 = u32x4{ra.x, ra.y, P[1].x, P[1].y};
+                p1 = u32x4{rb.x, rb.y, P[3].x, P[3].y};
               } else {
+                p0 = u32x4{P[0].x, P[0].y, ra.x, ra.y};
+                p1 = u32x4{P[2].x, P[2].y, rb.x, rb.y};
+              }
+              E* base = Gp + tt * gr.ldG + vbase + i * 32 + 8 * half;
+              *reinterpret_cast<u32x4*>(base) = p0;
+              *reinterpret_cast<u32x4*>(base + 16) = p1;
+            } else if (tin) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int r0 = i * 32 + 8 * q;
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                  if (r0 + c < end_l) grow[r0 + c] = f32_to_bf16(gv[c]);
+                  if (r0 + c < end_l) grow[r0 + c] = f32_to_bf16(gv[4 * q + c]);
               }
-            } else {
+            }
+          } else {
+            if (!tin) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int r0 = i * 32 + 8 * q;
               if (gr.vec_store && r0 + 3 < end_l) {
-                f32x4 pk = {gv[0], gv[1], gv[2], gv[3]};
+                f32x4 pk = {gv[4 * q], gv[4 * q + 1], gv[4 * q + 2], gv[4 * q + 3]};
                 *reinterpret_cast<f32x4*>(grow + r0) = pk;
               } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                  if (r0 + c < end_l) grow[r0 + c] = gv[c];
+                  if (r0 + c < end_l) grow[r0 + c] = gv[4 * q + c];
               }
             }
           }
+        }
       }
     } else {  // EPI_STORE
       const StoreArgs& st = e.store;

@@ -493,7 +493,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       e.grad.n_valid = n_valid;
       e.grad.v_off = c0;
       e.grad.reduction = reduction;
-      e.grad.vec_store = 1;  // tile rows start at multiples of 4 inside the chunk
+      e.grad.vec_store = 1;  // tiles start at multiples of 256 rows; ldC is a multiple of 64
       e.grad.G = Gc;
       e.grad.ldG = p.ldC;
       if ((err = launch_gemm<E, EPI_GRAD>(g, e, s)) != hipSuccess) return err;
