@@ -97,6 +97,35 @@ def test_c3_full_size_sampled_tokens(V):
     _check_sampled(g, inp, h64, W64, sample, nv)
 
 
+def test_max_tokens_sampled(V):
+    """Four times c3's tokens (T = 65536) on the same table: the staged G chunk
+    holds T x 100544 = 6.6e9 elements and the per-tile statistics 51e6 pairs,
+    so any 32-bit element index in the backward would wrap."""
+    say("case T=65536 (c3 recipe) full size")
+    inp = config_inputs("c3", T=65536)
+    dev = "cuda"
+    h = V.from_bits(inp.h, "bf16", dev)
+    W = V.from_bits(inp.W, "bf16", dev)
+    tg = torch.from_numpy(inp.targets).to(dev)
+    r = V.ce_step(h, W, tg, inp.V_real, inp.num_shards, inp.ignore_index)
+    torch.cuda.synchronize()
+    nv, nb = _counts(inp)
+    assert int(r.fwd.n_valid.item()) == nv and int(r.fwd.n_bad.item()) == nb
+    dW = r.dW
+    colsum = dW.double().sum(dim=0).abs().max().item()
+    scale = dW.double().abs().sum(dim=0).max().item()
+    assert colsum <= 1e-3 * scale, (colsum, scale)
+    g = dict(lse=r.fwd.lse.cpu().numpy(), loss=r.fwd.loss.cpu().numpy(),
+             dh=r.dh.cpu().numpy())
+    del r, dW, h
+    torch.cuda.empty_cache()
+    sample = _sample_tokens(inp.targets, inp.V_real, 24, 5)
+    sample = np.union1d(sample, [16383, 16384, 32767, 32768, 65535])
+    W64 = oracle.decode(inp.W, "bf16")
+    h64 = oracle.decode(inp.h[sample], "bf16")
+    _check_sampled(g, inp, h64, W64, sample, nv)
+
+
 def test_c4_full_size_tied_step(V):
     say("case c4 full size")
     inp = config_inputs("c4")
