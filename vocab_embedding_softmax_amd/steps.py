@@ -128,18 +128,57 @@ def ot_h_step(ids, targets1, targets2, W, W2, V_real, num_shards, ignore_index=-
     return StepOut(f1, b1.dh, b1.dW, dict(h=h, n_bad_id=n_bad_id, fwd2=f2, dW2=b2.dW))
 
 
+_SIDE = {}
+
+
+def _side_streams(device, n):
+    """n extra streams of this device (default priority), made once."""
+    key = (torch.device(device).index, n)
+    if key not in _SIDE:
+        _SIDE[key] = [torch.cuda.Stream(device=device) for _ in range(n)]
+    return _SIDE[key]
+
+
 def ngram_bwd(ids, fwd_out, dx, V_real, V_pad, num_shards, *, dE=None, dE2=None, dE3=None,
               rows2=None, rows3=None, accumulate=False, ws: Optional[Workspaces] = None,
               stream=None):
     """dE [V_pad,H], dE2 [rows2,H], dE3 [rows3,H] (float32) from dx [T,H]; the
-    n-gram rows are the ones vngram_fwd returned (fwd_out.ids2 / ids3)."""
+    n-gram rows are the ones vngram_fwd returned (fwd_out.ids2 / ids3).
+
+    The three scatters are independent: the n-gram tables' run on two side
+    streams that fork from and join back into the caller's stream, so one
+    table's single-workgroup sort overlaps another's row sums. Every buffer is
+    allocated on the caller's stream before the fork and the join is enqueued
+    before return, so later work on that stream is ordered after all three."""
+    dev = dx.device
+    T, H = dx.shape
+    main = torch.cuda.current_stream(dev) if stream is None else stream
     rows2 = dE2.shape[0] if rows2 is None else rows2
     rows3 = dE3.shape[0] if rows3 is None else rows3
-    w = None if ws is None else ws["emb"]
-    dE = L.vemb_bwd(ids, dx, V_real, V_pad, num_shards, dW=dE, accumulate=accumulate, ws=w,
-                    stream=stream)
-    dE2 = L.vemb_bwd(fwd_out.ids2, dx, rows2, rows2, num_shards, dW=dE2, accumulate=accumulate,
-                     ws=None if ws is None else ws["emb2"], stream=stream)
-    dE3 = L.vemb_bwd(fwd_out.ids3, dx, rows3, rows3, num_shards, dW=dE3, accumulate=accumulate,
-                     ws=None if ws is None else ws["emb3"], stream=stream)
+    f32 = dict(dtype=torch.float32, device=dev)
+    if dE is None:
+        dE = torch.empty(V_pad, H, **f32)
+    if dE2 is None:
+        dE2 = torch.empty(rows2, H, **f32)
+    if dE3 is None:
+        dE3 = torch.empty(rows3, H, **f32)
+    if ws is None:
+        ws = Workspaces(dev, emb=L.vemb_bwd_workspace_bytes(T, H, V_real, V_pad),
+                        emb2=L.vemb_bwd_workspace_bytes(T, H, rows2, rows2),
+                        emb3=L.vemb_bwd_workspace_bytes(T, H, rows3, rows3))
+    s2, s3 = _side_streams(dev, 2)
+    fork = torch.cuda.Event()
+    fork.record(main)
+    s2.wait_event(fork)
+    s3.wait_event(fork)
+    L.vemb_bwd(fwd_out.ids2, dx, rows2, rows2, num_shards, dW=dE2, accumulate=accumulate,
+               ws=ws["emb2"], stream=s2)
+    L.vemb_bwd(fwd_out.ids3, dx, rows3, rows3, num_shards, dW=dE3, accumulate=accumulate,
+               ws=ws["emb3"], stream=s3)
+    L.vemb_bwd(ids, dx, V_real, V_pad, num_shards, dW=dE, accumulate=accumulate, ws=ws["emb"],
+               stream=main)
+    for s in (s2, s3):
+        j = torch.cuda.Event()
+        j.record(s)
+        main.wait_event(j)
     return dE, dE2, dE3
