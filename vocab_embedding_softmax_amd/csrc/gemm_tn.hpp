@@ -90,8 +90,9 @@ struct GradArgs {
 struct StoreArgs {
   float* C;
   int64_t ldc;
-  int64_t split_stride; // elements between split-K partial planes
-  int32_t accumulate;   // 1: C += result, 0: C = result
+  float* P;             // K splits 1, 2, ...: partial planes [k_splits - 1][M][ldc], overwritten
+  int64_t split_stride; // elements between partial planes
+  int32_t accumulate;   // split 0: 1: C += result, 0: C = result
   int64_t m_zero_from;  // rows at or past this receive 0 (or are left alone when accumulating)
 };
 
@@ -1022,7 +1023,12 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       }
     } else {  // EPI_STORE
       const StoreArgs& st = e.store;
-      float* Cp = st.C + t.ks * st.split_stride;
+      // split 0 writes (or adds into) C; every later K split overwrites its
+      // own partial plane, which a fixed-order pass adds into C afterwards
+      const bool first = t.ks == 0;
+      float* Cp = first ? st.C : st.P + (t.ks - 1) * st.split_stride;
+      const int64_t ldc = st.ldc;
+      const bool accum = first && st.accumulate;
       // element (i, r) of this lane: row vb + i*32 + 8*(r/4) + r%4
       const int64_t vb = vbase + 4 * half;
       auto rel = [&](int64_t x) {
@@ -1034,7 +1040,7 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       for (int j = 0; j < NI; ++j) {
         const int64_t n = t.n0 + wn * WN + j * 32 + l32;
         if (n >= t.n_end) continue;
-        float* col = Cp + vb * st.ldc + n;
+        float* col = Cp + vb * ldc + n;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -1042,10 +1048,10 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
             const int rr = i * 32 + 8 * (r >> 2) + (r & 3);
             if (rr >= end_l) continue;
             const bool zero_row = rr >= zero_l;
-            if (zero_row && st.accumulate) continue;
-            float* dst = col + rr * st.ldc;
+            if (zero_row && accum) continue;
+            float* dst = col + rr * ldc;
             const float v = zero_row ? 0.0f : acc[i][j][r];
-            if (st.accumulate)  // the only writer of this element in this launch
+            if (accum)  // the only writer of this element in this launch
               __hip_atomic_fetch_add(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             else
               *dst = v;

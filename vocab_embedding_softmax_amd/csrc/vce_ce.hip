@@ -82,9 +82,30 @@ ArgPlan plan_argmax(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t
   return p;
 }
 
+int32_t k_splits_for(int64_t tiles, int64_t K) {
+  constexpr int64_t kCUs = 256;
+  constexpr int32_t kMaxSplit = 8;
+  if (tiles <= 0) return 1;
+  auto busy = [&](int64_t s) {  // fraction of CU-rounds that hold a tile
+    const int64_t t = tiles * s;
+    return static_cast<double>(t) / static_cast<double>(cdiv(t, kCUs) * kCUs);
+  };
+  if (busy(1) >= 0.85) return 1;
+  int32_t best = 1;
+  double best_busy = busy(1);
+  for (int32_t s = 2; s <= kMaxSplit; ++s) {
+    if (cdiv(K, s) < 1024) break;
+    const double b = busy(s);
+    if (b > best_busy + 1e-9) {
+      best = s;
+      best_busy = b;
+    }
+  }
+  return best;
+}
+
 BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, size_t esize,
                  void* ws) {
-  (void)H;
   (void)V_real;
   BwdPlan p{};
   p.S = V_pad / n;
@@ -110,8 +131,15 @@ BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
   }
   p.ldC = round_up(p.chunk_rows, kPadK);
   p.esize = esize;
+  // K splits: dh has cdiv(T, 256) x cdiv(H, 256) tiles over the chunk's
+  // classes, dW cdiv(chunk, 256) x cdiv(H, 256) tiles over the tokens
+  const int64_t tiles_h = cdiv(H, kTileN);
+  p.split_dh = k_splits_for(cdiv(T, kTileM) * tiles_h, p.chunk_rows);
+  p.split_dw = k_splits_for(cdiv(p.chunk_rows, kTileM) * tiles_h, T);
   Carve c(ws);
   p.G = c.take<char>(static_cast<size_t>(T * p.ldC) * esize);
+  p.Pdh = c.take<float>(static_cast<size_t>((p.split_dh - 1) * T * H));
+  p.Pdw = c.take<float>(static_cast<size_t>((p.split_dw - 1) * p.chunk_rows * H));
   p.bytes = c.used;
   return p;
 }
@@ -302,6 +330,27 @@ __global__ void k_zero_cols(E* G, int64_t rows, int64_t ld, int64_t c0, int64_t 
   if (i < rows * w) G[(i / w) * ld + c0 + i % w] = E(0);
 }
 
+// C[r][:] += P[0][r][:] + P[1][r][:] + ... for rows r < rows, planes in order
+// (the partial sums of the later K splits; deterministic).
+__global__ __launch_bounds__(256) void k_split_add(float* __restrict__ C, int64_t ldc,
+                                                   const float* __restrict__ P, int64_t ldp,
+                                                   int64_t plane, int32_t nplanes, int64_t rows,
+                                                   int64_t cols4) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= rows * cols4) return;
+  const int64_t r = i / cols4, c = (i - r * cols4) * 4;
+  float4* dst = reinterpret_cast<float4*>(C + r * ldc + c);
+  float4 v = *dst;
+  for (int32_t k = 0; k < nplanes; ++k) {
+    const float4 a = *reinterpret_cast<const float4*>(P + k * plane + r * ldp + c);
+    v.x += a.x;
+    v.y += a.y;
+    v.z += a.z;
+    v.w += a.w;
+  }
+  *dst = v;
+}
+
 __global__ __launch_bounds__(256) void k_zero_f4(float4* __restrict__ p, int64_t n4) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -445,6 +494,16 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
                        reinterpret_cast<float4*>(dW + r0 * H), n4);
     return hipGetLastError();
   };
+  // adds the partial planes of K splits 1.. into rows [0, rows_real) of C
+  auto split_add = [&](float* C, const float* P, int32_t ks, int64_t rows,
+                       int64_t rows_real) -> hipError_t {
+    if (ks <= 1 || rows_real <= 0) return hipSuccess;
+    const int64_t cols4 = H / 4;
+    const int64_t n = rows_real * cols4;
+    hipLaunchKernelGGL(k_split_add, dim3(static_cast<uint32_t>(cdiv(n, 256))), dim3(256), 0, s, C,
+                       H, P, H, rows * H, ks - 1, rows_real, cols4);
+    return hipGetLastError();
+  };
   if ((err = mark()) != hipSuccess) return err;
   const E* Wp = static_cast<const E*>(W);
   E* Gc = static_cast<E*>(p.G);
@@ -511,17 +570,20 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       g.m_load_end = T;
       g.n_total = H;
       g.tiles_n = static_cast<int32_t>(cdiv(H, kTileN));
-      g.k_splits = 1;
+      const int32_t ks = min(k_splits_for(cdiv(T, kTileM) * g.tiles_n, kreal), p.split_dh);
+      g.k_splits = ks;
       g.k_total = kreal;
-      g.k_per_split = round_up(kreal, kPadK);
+      g.k_per_split = round_up(cdiv(kreal, ks), kPadK);
       g.group_m = kGroupM;
       EpiArgs e{};
       e.store.C = dh;
       e.store.ldc = H;
-      e.store.split_stride = 0;
+      e.store.P = p.Pdh;
+      e.store.split_stride = T * H;
       e.store.accumulate = (dh_written || acc_dh) ? 1 : 0;
       e.store.m_zero_from = T;
       if ((err = launch_gemm<E, EPI_STORE, false, true>(g, e, s)) != hipSuccess) return err;
+      if ((err = split_add(dh, p.Pdh, ks, T, T)) != hipSuccess) return err;
       dh_written = true;
     }
     if ((err = mark()) != hipSuccess) return err;
@@ -538,17 +600,20 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       g.m_load_end = Vc;
       g.n_total = H;
       g.tiles_n = static_cast<int32_t>(cdiv(H, kTileN));
-      g.k_splits = 1;
+      const int32_t ks = min(k_splits_for(cdiv(Vc, kTileM) * g.tiles_n, T), p.split_dw);
+      g.k_splits = ks;
       g.k_total = T;
-      g.k_per_split = round_up(T, kPadK);
+      g.k_per_split = round_up(cdiv(T, ks), kPadK);
       g.group_m = kGroupM;
       EpiArgs e{};
       e.store.C = dW + c0 * H;
       e.store.ldc = H;
-      e.store.split_stride = 0;
+      e.store.P = p.Pdw;
+      e.store.split_stride = Vc * H;
       e.store.accumulate = acc_dw ? 1 : 0;
       e.store.m_zero_from = kreal;
       if ((err = launch_gemm<E, EPI_STORE, true, true>(g, e, s)) != hipSuccess) return err;
+      if ((err = split_add(dW + c0 * H, p.Pdw, ks, Vc, kreal)) != hipSuccess) return err;
     }
     if ((err = mark()) != hipSuccess) return err;
   }

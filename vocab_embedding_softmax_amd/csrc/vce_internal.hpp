@@ -144,6 +144,10 @@ struct BwdPlan {
   int64_t ldC;               // leading dimension of the staged G chunk
   size_t esize;
   void* G;                   // [T][ldC]
+  int32_t split_dh;          // most K splits of the dh GEMM (1: none)
+  int32_t split_dw;          // most K splits of the dW GEMM
+  float* Pdh;                // [split_dh - 1][T][H] partial planes
+  float* Pdw;                // [split_dw - 1][chunk_rows][H]
   size_t bytes;
   void chunk(int64_t c, int64_t& c0, int64_t& c1) const {
     if (group > 0) {
@@ -156,6 +160,11 @@ struct BwdPlan {
     c1 = (k + 1) * S < c0 + piece_rows ? (k + 1) * S : c0 + piece_rows;
   }
 };
+// K splits for a GEMM of `tiles` output tiles over K positions: 1 while one
+// pass of tiles keeps at least 85 % of the GPU's 256 CUs busy through its
+// rounds, else the count in 2..8 (each split >= 1024 K positions) that does
+// best, the smallest on ties.
+int32_t k_splits_for(int64_t tiles, int64_t K);
 BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, size_t esize,
                  void* ws);
 
