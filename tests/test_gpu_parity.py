@@ -244,15 +244,18 @@ def test_scatter_add_heavy_repeats(V):
 
 
 @pytest.mark.parametrize("T,H,Vr,label", [
-    (20000, 64, 3000, "T above the one-workgroup sort"),
-    (4000, 72, (1 << 20) + 5, "packed (ID, token) key wider than 32 bits"),
-    (16384, 40, 262143, "largest ID range of the one-workgroup sort at T = 16384"),
+    (20000, 64, 3000, "20 sorted runs, the last one partial"),
+    (4000, 72, (1 << 20) + 5, "IDs of 21 bits (four radix passes)"),
+    (16384, 40, 262143, "16 runs, 18-bit IDs"),
+    (32768, 16, 70000, "32 runs, the most the merge holds"),
+    (40000, 16, 3000, "T above the sorted runs: block sorts and ID scans"),
     (1, 8, 10, "one token"),
     (777, 8, 5, "five IDs, long runs over many chunks"),
 ])
 def test_scatter_add_sort_paths(V, T, H, Vr, label):
-    """Both ways the library sorts tokens by ID (one workgroup, or block-local
-    sorts + scans) against the oracle, with repeats that cross chunk ends."""
+    """Both ways the library sorts tokens by ID (sorted runs + merge, or
+    block-local sorts + ID scans) against the oracle, with repeats that cross
+    chunk ends and runs."""
     say(f"case scatter sort path T={T} H={H} V={Vr}: {label}")
     dev = "cuda"
     rng = np.random.default_rng(T + H)

@@ -9,10 +9,10 @@
 //
 // Backward (same page, ¶2): repeated IDs add into their one owned row.
 // Deterministic, one writer per row, no atomics on the table:
-//   1. the valid tokens are sorted by (ID, token): up to 16384 tokens whose
-//      packed (ID, token) key fits 32 bits are radix-sorted in the LDS of one
-//      workgroup (one launch); larger inputs use block-local LDS sorts, per-
-//      block ID counts and scans;
+//   1. the valid tokens are sorted by (ID, token): up to 32768 tokens are cut
+//      into runs of 1024 that workgroups radix-sort by ID in LDS, then each
+//      workgroup places its run by ranking its IDs in all runs (two launches);
+//      larger inputs use block-local LDS sorts, per-block ID counts and scans;
 //   2. the sorted list is cut into chunks of kSegC positions; each chunk sums
 //      the dout rows of its runs (tokens of one ID) in sorted order and writes
 //      the sum of every run that lies wholly inside it into its row of dW;
@@ -30,8 +30,8 @@ constexpr int kScanBlock = kScanThreads * kScanPerThread;  // 4096 values per bl
 constexpr int kSegC = 16;                                  // sorted positions per chunk
 constexpr int kSegBatch = 16;                              // dout rows in flight per lane
 constexpr int kSegCols = 256;                              // dW columns per wave (64 lanes x 4)
-constexpr int kPlanThreads = 1024;                         // the one-workgroup sort
-constexpr int kPlanMaxT = 16384;                           // tokens it holds in LDS
+constexpr int kRun = 1024;                                 // tokens per sorted run (one workgroup)
+constexpr int kRunMaxRuns = 32;                            // runs the merge holds in LDS
 constexpr int kPlanDigit = 6;                              // ID bits per radix pass
 constexpr int kSortBlock = 1024;                           // tokens per local sort
 constexpr int kSortThreads = 512;
@@ -52,17 +52,17 @@ static int32_t bit_width(int64_t x) {
 EmbBwdPlan plan_emb_bwd(int64_t T, int64_t H, int64_t V_real, void* ws) {
   EmbBwdPlan p{};
   const int64_t Tp = T < 1 ? 1 : T;
-  p.tbits = bit_width(Tp - 1);
   p.vbits = bit_width(V_real);
-  // IDs < V_real < 2^vbits never have all ID bits set, which the sort
-  // reserves for tokens without a valid ID
-  p.one_wg = Tp <= kPlanMaxT && p.tbits + p.vbits <= 32;
+  // runs of kRun tokens sorted by workgroups, then merged (IDs < V_real <
+  // 2^vbits stay below the all-ones value that marks tokens without a valid ID)
+  p.nruns = cdiv(Tp, kRun);
+  p.runs = p.nruns <= kRunMaxRuns;
   p.nblocks = cdiv(Tp, kSortBlock);
   p.nchunks = cdiv(Tp, kSegC);
   p.nslices = cdiv(H, kSegCols);
   p.scan_blocks = scan_blocks(V_real);
   Carve c(ws);
-  if (!p.one_wg) {
+  if (!p.runs) {
     p.bcnt = c.take<int32_t>(static_cast<size_t>(p.nblocks * V_real));
     p.counts = c.take<int32_t>(static_cast<size_t>(V_real));
     p.offs = c.take<int32_t>(static_cast<size_t>(V_real + 1));
@@ -71,6 +71,9 @@ EmbBwdPlan plan_emb_bwd(int64_t T, int64_t H, int64_t V_real, void* ws) {
     p.scan_tmp = c.take<int32_t>(static_cast<size_t>(p.scan_blocks + 1));
   } else {
     p.n_sorted = c.take<int32_t>(1);
+    p.rid = c.take<uint32_t>(static_cast<size_t>(p.nruns * kRun));
+    p.rtok = c.take<int32_t>(static_cast<size_t>(p.nruns * kRun));
+    p.rvalid = c.take<int32_t>(static_cast<size_t>(p.nruns));
   }
   p.sorted = c.take<int32_t>(static_cast<size_t>(Tp));
   p.skey = c.take<int32_t>(static_cast<size_t>(Tp));
@@ -569,77 +572,51 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d) {
   return eq;
 }
 
-// Sorts the tokens of one call by (ID, token) in the LDS of one workgroup.
-// Token t with a valid ID gets the key (ID << tbits) | t; the others get
-// all bits set and sort last. A least-significant-digit radix sort over the
-// ID bits keeps equal IDs in token order. Each pass: every wave ranks its
-// contiguous span of positions, 64 at a time, among equal digits (ballot
-// match + a per-wave running count per digit); one block-wide scan over
-// (digit, wave) counts gives every key its place.
-// Writes sorted tokens and IDs for the n valid tokens, n, and for every
-// chunk of kSegC sorted positions the first position of the ID found at the
-// chunk's first position.
-__global__ __launch_bounds__(kPlanThreads) void k_emb_plan(
-    const int32_t* __restrict__ ids, int64_t T, int64_t V_real, int32_t tbits, int32_t vbits,
-    int32_t* __restrict__ sorted, int32_t* __restrict__ skey, int32_t* __restrict__ n_sorted,
-    int32_t* __restrict__ chunk_start) {
-  constexpr int NW = kPlanThreads / 64;
+// Sort of the tokens of one call by (ID, token), in two steps.
+// k_run_sort: workgroup r sorts the run of tokens [r*kRun, (r+1)*kRun) by ID,
+// stably (least-significant-digit radix passes of kPlanDigit ID bits; within
+// a wave, lanes with the same digit are found bit by bit through ballots and
+// ranked by lane; across waves, counts are scanned in (digit, wave) order).
+// Tokens without a valid ID carry all bits set and end their run.
+__global__ __launch_bounds__(kRun) void k_run_sort(const int32_t* __restrict__ ids, int64_t T,
+                                                   int64_t V_real, int32_t vbits,
+                                                   uint32_t* __restrict__ rid,
+                                                   int32_t* __restrict__ rtok,
+                                                   int32_t* __restrict__ rvalid) {
+  constexpr int NW = kRun / 64;
   constexpr int ND = 1 << kPlanDigit;
-  constexpr int MAXR = kPlanMaxT / kPlanThreads;  // rounds of 64 positions per wave
-  static_assert(NW * ND == kPlanThreads, "one thread per (wave, digit) count");
-  __shared__ uint32_t kb[2][kPlanMaxT];
+  static_assert(NW * ND == kRun, "one thread per (wave, digit) count");
+  __shared__ uint32_t kid[2][kRun];
+  __shared__ int32_t ktok[2][kRun];
   __shared__ uint32_t wrun[NW][ND];
   __shared__ uint32_t wtot[NW];
   __shared__ int32_t s_n;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int R = static_cast<int>((T + kPlanThreads - 1) / kPlanThreads);  // 1..MAXR
-  const int span = R * 64;
   const uint64_t lt = (1ull << lane) - 1ull;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRun + tid;
+  uint32_t id = ~0u;
+  if (t < T) {
+    const int64_t v = ids[t];
+    if (v >= 0 && v < V_real) id = static_cast<uint32_t>(v);
+  }
   if (tid == 0) s_n = 0;
+  kid[0][tid] = id;
+  ktok[0][tid] = static_cast<int32_t>(t);
   __syncthreads();
-
-  // all loads of the IDs in flight at once (clamped indices, results selected)
-  int nv = 0;
-  int32_t idv[MAXR];
-#pragma unroll
-  for (int r = 0; r < MAXR; ++r) {
-    const int p = w * span + r * 64 + lane;
-    idv[r] = ids[min(p, static_cast<int>(T) - 1)];
-  }
-#pragma unroll
-  for (int r = 0; r < MAXR; ++r) {
-    const int p = w * span + r * 64 + lane;
-    const int64_t id = idv[r];
-    uint32_t key = ~0u;
-    if (r < R && p < T && id >= 0 && id < V_real) {
-      key = (static_cast<uint32_t>(id) << tbits) | static_cast<uint32_t>(p);
-      ++nv;
-    }
-    if (r < R) kb[0][p] = key;
-  }
-  for (int o = 32; o > 0; o >>= 1) nv += __shfl_xor(nv, o);
-  if (lane == 0) atomicAdd(&s_n, nv);
+  const uint64_t vb = __ballot(id != ~0u);
+  if (lane == 0) atomicAdd(&s_n, static_cast<int32_t>(__popcll(vb)));
 
   int src = 0;
   const int npass = (vbits + kPlanDigit - 1) / kPlanDigit;
   for (int pass = 0; pass < npass; ++pass) {
-    const int shift = tbits + kPlanDigit * pass;
+    const int shift = kPlanDigit * pass;
     wrun[w][lane] = 0u;  // this wave's counters; only this wave touches them until the barrier
-    uint32_t keys[MAXR];
-    uint32_t rank[MAXR];
-#pragma unroll
-    for (int r = 0; r < MAXR; ++r) {
-      if (r < R) {
-        const uint32_t key = kb[src][w * span + r * 64 + lane];
-        const uint32_t d = (key >> shift) & (ND - 1);
-        const uint64_t eq = match_digit(d);
-        const uint32_t below = static_cast<uint32_t>(__popcll(eq & lt));
-        const uint32_t prev = wrun[w][d];
-        if (below == 0) wrun[w][d] = prev + static_cast<uint32_t>(__popcll(eq));
-        keys[r] = key;
-        rank[r] = prev + below;
-      }
-    }
+    const uint32_t key = kid[src][tid];
+    const int32_t tk = ktok[src][tid];
+    const uint32_t d = (key >> shift) & (ND - 1);
+    const uint64_t eq = match_digit(d);
+    const uint32_t below = static_cast<uint32_t>(__popcll(eq & lt));
+    if (below == 0) wrun[w][d] = static_cast<uint32_t>(__popcll(eq));
     __syncthreads();
     // exclusive scan of the counts in (digit, wave) order: thread i holds
     // digit i / NW, wave i % NW
@@ -657,39 +634,101 @@ __global__ __launch_bounds__(kPlanThreads) void k_emb_plan(
     for (int k = 0; k < w; ++k) base += wtot[k];
     wrun[wi][di] = base + x - v;  // every thread has read its count above
     __syncthreads();
-#pragma unroll
-    for (int r = 0; r < MAXR; ++r) {
-      if (r < R) {
-        const uint32_t d = (keys[r] >> shift) & (ND - 1);
-        kb[src ^ 1][wrun[w][d] + rank[r]] = keys[r];
-      }
-    }
+    const uint32_t pos = wrun[w][d] + below;
+    kid[src ^ 1][pos] = key;
+    ktok[src ^ 1][pos] = tk;
     __syncthreads();
     src ^= 1;
   }
+  const int64_t o = static_cast<int64_t>(blockIdx.x) * kRun + tid;
+  rid[o] = kid[src][tid];
+  rtok[o] = ktok[src][tid];
+  if (tid == 0) rvalid[blockIdx.x] = s_n;
+}
 
-  const int n = s_n;
-  const uint32_t tmask = (tbits >= 32) ? ~0u : ((1u << tbits) - 1u);
-  for (int p = tid; p < n; p += kPlanThreads) {
-    const uint32_t key = kb[src][p];
-    sorted[p] = static_cast<int32_t>(key & tmask);
-    skey[p] = static_cast<int32_t>(key >> tbits);
+// Summed over runs k < U (those below nruns, other than skip): the number of
+// the kRun ascending IDs of run k that are below x, or at most x for runs
+// before le_before (x < 2^31, so "at most x" is "below x + 1"). The U binary
+// searches advance together with no branches (a run that does not count
+// searches the last run and adds nothing), so the U LDS reads of a step are
+// in flight at once.
+template <int U>
+__device__ __forceinline__ int32_t run_ranks(const uint32_t* all, int nruns, int skip,
+                                             int le_before, uint32_t x) {
+  const uint32_t* base[U];
+  uint32_t lim[U];
+  int32_t c[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    base[u] = all + (u < nruns ? u : nruns - 1) * kRun;
+    lim[u] = x + (u < le_before ? 1u : 0u);
+    c[u] = 0;
   }
-  if (tid == 0) *n_sorted = n;
+#pragma unroll
+  for (int step = kRun / 2; step > 0; step >>= 1) {
+    uint32_t y[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) y[u] = base[u][c[u] + step - 1];
+#pragma unroll
+    for (int u = 0; u < U; ++u) c[u] += y[u] < lim[u] ? step : 0;
+  }
+  int32_t sum = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    // c <= kRun - 1 here: element c is the last one left to test
+    const int32_t r = c[u] + (base[u][c[u]] < lim[u] ? 1 : 0);
+    sum += (u < nruns && u != skip) ? r : 0;
+  }
+  return sum;
+}
 
-  // for every chunk: the first sorted position of the ID found at the
-  // chunk's first position (binary search; the keys are ascending)
-  const int nch = (n + kSegC - 1) / kSegC;
-  for (int ch = tid; ch < nch; ch += kPlanThreads) {
-    const int q0 = ch * kSegC;
-    const uint32_t first = (kb[src][q0] >> tbits) << tbits;  // smallest key of that ID
-    int lo = 0, hi = q0;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (kb[src][mid] < first) lo = mid + 1; else hi = mid;
-    }
-    chunk_start[ch] = lo;
+// k_run_merge: kMergeSplit workgroups per run place its tokens. With the
+// runs' IDs in LDS, a token at index i of run r with ID v goes to
+//   i + (tokens with ID <= v in runs before r) + (tokens with ID < v in runs after r),
+// which is its rank in (ID, token) order, since run r holds tokens
+// [r*kRun, (r+1)*kRun). A token that starts a chunk of kSegC sorted positions
+// also records where its ID's tokens start (tokens with ID < v in all runs).
+constexpr int kMergeSplit = 4;
+constexpr int kMergeThreads = kRun / kMergeSplit;
+static_assert(kRunMaxRuns <= 64, "one wave sums the run counts");
+__global__ __launch_bounds__(kMergeThreads) void k_run_merge(
+    const uint32_t* __restrict__ rid, const int32_t* __restrict__ rtok,
+    const int32_t* __restrict__ rvalid, int32_t nruns, int32_t* __restrict__ sorted,
+    int32_t* __restrict__ skey, int32_t* __restrict__ n_sorted,
+    int32_t* __restrict__ chunk_start) {
+  __shared__ __attribute__((aligned(16))) uint32_t all[kRunMaxRuns * kRun];
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x / kMergeSplit;
+  const int i = (blockIdx.x % kMergeSplit) * kMergeThreads + tid;  // index in run r
+  // nruns * kRun IDs = nruns 16-byte pieces per thread, eight loads in flight
+  const u32x4* src = reinterpret_cast<const u32x4*>(rid);
+  u32x4* dst = reinterpret_cast<u32x4*>(all);
+  for (int j0 = 0; j0 < nruns; j0 += 8) {
+    u32x4 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < nruns) x[u] = src[(j0 + u) * kMergeThreads + tid];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < nruns) dst[(j0 + u) * kMergeThreads + tid] = x[u];
   }
+  if (blockIdx.x == 0 && tid < 64) {  // nruns <= 64: one load per lane, one wave sum
+    int32_t n = tid < nruns ? rvalid[tid] : 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+    if (tid == 0) *n_sorted = n;
+  }
+  __syncthreads();
+  const uint32_t v = all[r * kRun + i];
+  if (v == ~0u) return;
+  const bool small = nruns <= kRunMaxRuns / 2;  // uniform
+  const int32_t pos = i + (small ? run_ranks<kRunMaxRuns / 2>(all, nruns, r, r, v)
+                                 : run_ranks<kRunMaxRuns>(all, nruns, r, r, v));
+  sorted[pos] = rtok[r * kRun + i];
+  skey[pos] = static_cast<int32_t>(v);
+  if (pos % kSegC == 0)
+    chunk_start[pos / kSegC] = small ? run_ranks<kRunMaxRuns / 2>(all, nruns, -1, 0, v)
+                                     : run_ranks<kRunMaxRuns>(all, nruns, -1, 0, v);
 }
 
 // General sort: the first sorted position of the ID at every chunk's start.
@@ -944,9 +983,14 @@ hipError_t run_emb_bwd(const int32_t* ids, const void* dout, bool dout_bf16, int
   }
   if (T == 0) return hipSuccess;
   // 1. stable sort of the tokens by ID
-  if (p.one_wg) {
-    hipLaunchKernelGGL(k_emb_plan, dim3(1), dim3(kPlanThreads), 0, s, ids, T, V_real, p.tbits,
-                       p.vbits, p.sorted, p.skey, p.n_sorted, p.chunk_start);
+  if (p.runs) {
+    hipLaunchKernelGGL(k_run_sort, dim3(static_cast<uint32_t>(p.nruns)), dim3(kRun), 0, s, ids, T,
+                       V_real, p.vbits, p.rid, p.rtok, p.rvalid);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_run_merge, dim3(static_cast<uint32_t>(p.nruns * kMergeSplit)),
+                       dim3(kMergeThreads), 0, s, p.rid,
+                       p.rtok, p.rvalid, static_cast<int32_t>(p.nruns), p.sorted, p.skey,
+                       p.n_sorted, p.chunk_start);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   } else {
     const int64_t ncnt = p.nblocks * V_real;

@@ -175,9 +175,9 @@ BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
 //     bits are radix-sorted in one workgroup's LDS (one launch);
 //   general: block-local LDS sorts + per-block counts + scans (any size).
 struct EmbBwdPlan {
-  bool one_wg;         // the one-workgroup sort applies
-  int32_t tbits;       // bits of a token index in a packed key (one-workgroup sort)
-  int32_t vbits;       // bits of an ID (one-workgroup sort)
+  bool runs;           // sorted runs + merge (T <= 32 runs of 1024 tokens), else general
+  int32_t vbits;       // bits of an ID
+  int64_t nruns;       // runs of 1024 tokens
   int64_t nblocks;     // token blocks of the local sort (general)
   int64_t nchunks, nslices, scan_blocks;
   int32_t* bcnt;       // [nblocks][V_real] per-block occurrences -> per-block offsets (general)
@@ -188,7 +188,10 @@ struct EmbBwdPlan {
   int32_t* scan_tmp;   // [scan_blocks + 1] (general)
   int32_t* sorted;     // [T] token indices sorted by (ID, token)
   int32_t* skey;       // [T] the ID of each sorted position
-  int32_t* n_sorted;   // [1] number of valid tokens (one-workgroup sort; general: offs + V_real)
+  uint32_t* rid;       // [nruns * 1024] IDs of each sorted run (all bits set: no valid ID)
+  int32_t* rtok;       // [nruns * 1024] their tokens
+  int32_t* rvalid;     // [nruns] valid tokens per run
+  int32_t* n_sorted;   // [1] number of valid tokens (runs; general: offs + V_real)
   int32_t* chunk_start;// [nchunks] first sorted position of the ID at each chunk's first position
   float* partial;      // [nchunks][2][H] partial sums of IDs that cross chunk ends
   size_t bytes;
