@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4", choices=["c3", "c4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-c3", action="store_true",
+                    help="skip the CE-only field on the T=8192 workload")
     ap.add_argument("--no-sampled", action="store_true",
                     help="skip the sampled-softmax field (its own T=16384, H=1536 workload)")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
@@ -56,9 +58,13 @@ def parse():
     return ap.parse_args()
 
 
+# the sources the cross-entropy GEMM kernels are compiled from
+GEMM_SOURCES = ("gemm_tn.hpp", "vce_ce.hip", "vce_device.hpp", "vce_internal.hpp")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in GEMM_SOURCES:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -417,6 +423,41 @@ def main():
         del src, dst
     del ws, dh, dW, W, h, ws_arg, out_arg
     torch.cuda.empty_cache()
+    if tied and not a.no_c3:
+        # The LM-head cross-entropy alone (forward + backward, the metric's
+        # own operation) on the T=8192, H=3072, V=201088 workload with
+        # RMS-normalised hidden rows: tokens/s and MFMA fraction (8*T*H*V_real).
+        inp3 = config_inputs("c3")
+        T3, H3, V3, n3 = inp3.T, inp3.H, inp3.V_real, inp3.num_shards
+        h3 = V.from_bits(inp3.h, inp3.dtype, dev)
+        W3 = V.from_bits(inp3.W, inp3.dtype, dev)
+        tg3 = torch.from_numpy(inp3.targets).to(dev)
+        ws3 = V.Workspaces(dev, fwd=V.vce_fwd_workspace_bytes(T3, H3, V3, inp3.V_pad, n3, dt_code),
+                           bwd=V.vce_bwd_workspace_bytes(T3, H3, V3, inp3.V_pad, n3, dt_code))
+        dh3 = torch.empty(T3, H3, **f32)
+        dW3 = torch.empty(inp3.V_pad, H3, **f32)
+
+        def ce3():
+            return V.ce_step(h3, W3, tg3, V3, n3, inp3.ignore_index, ws=ws3, dh=dh3, dW=dW3)
+
+        ce3()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps3 = 3
+        e0.record(stream)
+        for _ in range(reps3):
+            ce3()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms3 = e0.elapsed_time(e1) / reps3
+        res["ce_fwd_bwd_T8192"] = {
+            "workload": f"T={T3}, H={H3}, V_real={V3}, {n3} shards, bf16, Zipf(1.1) targets",
+            "ms": ms3, "tokens_s": T3 / (ms3 * 1e-3),
+            "mfma_frac": 8.0 * T3 * H3 * V3 / (ms3 * 1e-3) / PEAK_BF16}
+        log(f"[bench] CE fwd+bwd at T={T3}: {ms3:.3f} ms")
+        del h3, W3, ws3, dh3, dW3
+        torch.cuda.empty_cache()
     if not a.no_sampled:
         # Sampled-softmax step on its own workload (T=16384, H=1536, V=131072,
         # P=16384): candidates, gather of W[cand], CE fwd+bwd over the
