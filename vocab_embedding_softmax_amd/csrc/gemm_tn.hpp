@@ -941,6 +941,7 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
         return static_cast<int>(max(min(x - vb, static_cast<int64_t>(WM)), static_cast<int64_t>(-1)));
       };
       const int real_l = rel(min(t.m_end, gr.V_real - gr.v_off));  // rows below are real classes
+      const bool rows_real = real_l + 4 * half >= WM;  // the same for every lane of the wave
       const int end_l = rel(t.m_end);                                 // rows below exist
       E* Gp = static_cast<E*>(gr.G);
 #pragma unroll
@@ -952,20 +953,34 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
         const int y_l = valid ? rel(y - gr.v_off) : -1;
         const int lim_l = valid ? real_l : -1;
         const float nl = lv[j] * kLog2e;
+        const float sj = valid ? scale : 0.0f;
         E* grow = Gp + tt * gr.ldG + vb;
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
           float gv[16];
+          if (rows_real) {
+            // every row of the wave's tile is a real class: p <= 1 is finite,
+            // and sj = 0 zeroes the rows of an ignored token
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const int r = i * 32 + 8 * q + c;
-              const float p = fast_exp2(fmaf(acc[i][j][4 * q + c], kLog2e, -nl));
-              const float oh = (r == y_l) ? 1.0f : 0.0f;
-              // select, never multiply, so a non-finite p of a discarded entry cannot leak
-              gv[4 * q + c] = (r < lim_l) ? scale * (p - oh) : 0.0f;
-            }
+              for (int c = 0; c < 4; ++c) {
+                const int r = i * 32 + 8 * q + c;
+                const float p = fast_exp2(fmaf(acc[i][j][4 * q + c], kLog2e, -nl));
+                gv[4 * q + c] = fmaf(sj, p, (r == y_l) ? -sj : 0.0f);
+              }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                const int r = i * 32 + 8 * q + c;
+                const float p = fast_exp2(fmaf(acc[i][j][4 * q + c], kLog2e, -nl));
+                const float oh = (r == y_l) ? 1.0f : 0.0f;
+                // select, never multiply, so a non-finite p of a discarded entry cannot leak
+                gv[4 * q + c] = (r < lim_l) ? scale * (p - oh) : 0.0f;
+              }
+          }
           if constexpr (sizeof(E) == 2) {
             // the 32-row block lies inside the tile for both lanes of the pair
             if (gr.vec_store && tin && i * 32 + 32 <= end_l + 4 * half) {
