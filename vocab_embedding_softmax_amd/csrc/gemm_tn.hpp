@@ -871,20 +871,35 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       const int lim_l = lim - 4 * half;
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
-        // this lane's rows in increasing order; strict > keeps the lowest row on ties
         float bv = -INFINITY;
         int bi = -1;
+        if (lim == WM) {
+          // every row is real (the same for the whole wave): the largest value,
+          // then the lowest of this lane's rows holding it (rows visited in
+          // decreasing order, the last match kept)
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+          for (int i = 0; i < MI; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rl = i * 32 + 8 * (r >> 2) + (r & 3);  // row - 4*half
-            const float v = acc[i][j][r];
-            if (rl < lim_l && v > bv) {
-              bv = v;
-              bi = rl + 4 * half;
+            for (int r = 0; r < 16; ++r) bv = fmaxf(bv, acc[i][j][r]);
+#pragma unroll
+          for (int i = MI - 1; i >= 0; --i)
+#pragma unroll
+            for (int r = 15; r >= 0; --r)
+              bi = (acc[i][j][r] == bv) ? i * 32 + 8 * (r >> 2) + (r & 3) + 4 * half : bi;
+        } else {
+          // this lane's rows in increasing order; strict > keeps the lowest row on ties
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int rl = i * 32 + 8 * (r >> 2) + (r & 3);  // row - 4*half
+              const float v = acc[i][j][r];
+              if (rl < lim_l && v > bv) {
+                bv = v;
+                bi = rl + 4 * half;
+              }
             }
-          }
+        }
         const float ov = __shfl_xor(bv, 32);
         const int oi = __shfl_xor(bi, 32);
         if (ov > bv || (ov == bv && oi >= 0 && (bi < 0 || oi < bi))) {
@@ -962,13 +977,16 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
             // every row of the wave's tile is a real class: p <= 1 is finite,
             // and sj = 0 zeroes the rows of an ignored token
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 16; ++q)
+              gv[q] = sj * fast_exp2(fmaf(acc[i][j][q], kLog2e, -nl));
+            // the target row, if this block holds it for this lane (rare)
+            if (static_cast<unsigned>(y_l - i * 32) < 32u) {
 #pragma unroll
-              for (int c = 0; c < 4; ++c) {
-                const int r = i * 32 + 8 * q + c;
-                const float p = fast_exp2(fmaf(acc[i][j][4 * q + c], kLog2e, -nl));
-                gv[4 * q + c] = fmaf(sj, p, (r == y_l) ? -sj : 0.0f);
-              }
+              for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                  if (i * 32 + 8 * q + c == y_l) gv[4 * q + c] -= sj;
+            }
           } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
