@@ -351,17 +351,24 @@ def test_ot_h_step(V, dt, T, H, Vr, Vp, n):
 
 # ------------------------------------------------------------------ sampled softmax
 
-def test_candidates_bit_exact(V):
-    say("case candidates")
+@pytest.mark.parametrize("T,Vc,P", [
+    (3000, 20000, 2048),      # one workgroup, bit maps in LDS
+    (3000, 20001, 2048),      # a partial last word of the bit maps
+    (500, 1000, 3000),        # P above V: every non-target row is a negative
+    (3000, 300000, 4096),     # past the LDS bit maps: flags, scans and emits in several launches
+])
+def test_candidates_bit_exact(V, T, Vc, P):
+    say(f"case candidates T={T} V={Vc} P={P}")
     dev = "cuda"
-    inp = make_sampled_inputs(3000, 64, 20000, 2048, "bf16", seed=9, ignore_frac=0.03)
-    inp.targets[5] = 25000  # out of range: keeps its value as position
+    inp = make_sampled_inputs(T, 64, Vc, P, "bf16", seed=9, ignore_frac=0.03)
+    inp.targets[5] = Vc + 5000  # out of range: keeps its value as position
     c = V.vss_candidates(torch.from_numpy(inp.targets).to(dev), inp.V_real,
                          torch.from_numpy(inp.perm).to(dev), inp.P)
     torch.cuda.synchronize()
     cand, pos, nu = oracle.candidates(inp.targets, inp.V_real, -100, inp.perm, inp.P)
     assert int(c.n_unique.item()) == nu
-    assert int(c.n_cand.item()) == cand.shape[0]
+    assert int(c.n_cand.item()) == max(inp.P, nu)
+    # with P above V only V - |U| negatives exist: the list holds those
     assert np.array_equal(c.cand.cpu().numpy()[:cand.shape[0]], cand.astype(np.int32))
     assert np.array_equal(c.pos.cpu().numpy(), pos.astype(np.int32))
 

@@ -953,6 +953,122 @@ __global__ void k_cand_counts(const int32_t* __restrict__ uidx, int64_t V, int64
   }
 }
 
+// One workgroup builds the candidate list for vocabularies up to kCandMaxV
+// rows, with bit maps in LDS: the targets' flags, then the not-in map of the
+// permutation; word prefixes of their popcounts give every unique target its
+// position and every negative its rank. Same results as the multi-launch
+// path below (unique targets ascending, then the first P - |U| entries of
+// perm that are not unique targets).
+constexpr int kCandThreads = 1024;
+constexpr int64_t kCandMaxV = 262144;
+
+// exclusive prefix of popc(bits[w]) over w < nw into pre[w]; returns the total
+__device__ uint32_t cand_word_scan(const uint32_t* bits, uint32_t* pre, int nw, uint32_t* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int per = (nw + kCandThreads - 1) / kCandThreads;
+  const int w0 = tid * per;
+  uint32_t own = 0;
+  for (int k = 0; k < per; ++k)
+    if (w0 + k < nw) own += static_cast<uint32_t>(__popc(bits[w0 + k]));
+  uint32_t x = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  uint32_t base = 0, total = 0;
+  for (int k = 0; k < kCandThreads / 64; ++k) {
+    if (k < w) base += wsum[k];
+    total += wsum[k];
+  }
+  uint32_t run = base + x - own;
+  for (int k = 0; k < per; ++k)
+    if (w0 + k < nw) {
+      pre[w0 + k] = run;
+      run += static_cast<uint32_t>(__popc(bits[w0 + k]));
+    }
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kCandThreads) void k_cand_one(const int32_t* __restrict__ targets,
+                                                           int64_t T, int64_t V,
+                                                           const int32_t* __restrict__ perm,
+                                                           int64_t P, int32_t* __restrict__ cand,
+                                                           int32_t* __restrict__ pos,
+                                                           int32_t* __restrict__ n_unique,
+                                                           int32_t* __restrict__ n_cand) {
+  constexpr int MAXW = static_cast<int>(kCandMaxV / 32);
+  __shared__ uint32_t fbits[MAXW], fpre[MAXW], nbits[MAXW], npre[MAXW];
+  __shared__ uint32_t wsum[kCandThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nw = static_cast<int>((V + 31) / 32);
+  for (int k = tid; k < nw; k += kCandThreads) {
+    fbits[k] = 0u;
+    nbits[k] = 0u;
+  }
+  __syncthreads();
+  for (int64_t t = tid; t < T; t += kCandThreads) {
+    const int64_t y = targets[t];
+    if (y >= 0 && y < V) atomicOr(&fbits[y >> 5], 1u << (y & 31));
+  }
+  __syncthreads();
+  const uint32_t nu = cand_word_scan(fbits, fpre, nw, wsum);
+  // unique targets, ascending
+  for (int k = tid; k < nw; k += kCandThreads) {
+    uint32_t b = fbits[k];
+    uint32_t at = fpre[k];
+    while (b) {
+      cand[at++] = k * 32 + (__ffs(b) - 1);
+      b &= b - 1u;
+    }
+  }
+  // each target's position among the candidates (other values unchanged)
+  for (int64_t t = tid; t < T; t += kCandThreads) {
+    const int64_t y = targets[t];
+    int32_t pt = static_cast<int32_t>(y);
+    if (y >= 0 && y < V) {
+      const uint32_t b = static_cast<uint32_t>(y & 31);
+      pt = static_cast<int32_t>(fpre[y >> 5] + __popc(fbits[y >> 5] & ((1u << b) - 1u)));
+    }
+    pos[t] = pt;
+  }
+  // not-in map of the permutation, 64 entries per wave step
+  for (int64_t i0 = static_cast<int64_t>(w) * 64; i0 < V; i0 += kCandThreads) {
+    const int64_t i = i0 + lane;
+    bool ni = false;
+    if (i < V) {
+      const int64_t r = perm[i];
+      ni = r >= 0 && r < V && !((fbits[r >> 5] >> (r & 31)) & 1u);
+    }
+    const uint64_t m = __ballot(ni);
+    if (lane == 0) {
+      const int k = static_cast<int>(i0 >> 5);
+      nbits[k] = static_cast<uint32_t>(m);
+      if (k + 1 < nw) nbits[k + 1] = static_cast<uint32_t>(m >> 32);
+    }
+  }
+  __syncthreads();
+  cand_word_scan(nbits, npre, nw, wsum);
+  // the first P - |U| of them, in permutation order
+  const int64_t need = P > nu ? P - nu : 0;
+  for (int k = tid; k < nw; k += kCandThreads) {
+    uint32_t b = nbits[k];
+    int64_t at = npre[k];
+    while (b && at < need) {
+      cand[nu + at] = perm[static_cast<int64_t>(k) * 32 + (__ffs(b) - 1)];
+      ++at;
+      b &= b - 1u;
+    }
+  }
+  if (tid == 0) {
+    *n_unique = static_cast<int32_t>(nu);
+    *n_cand = static_cast<int32_t>(P > nu ? P : nu);
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 
 hipError_t run_emb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, int64_t V_real,
@@ -1038,6 +1154,11 @@ hipError_t run_candidates(const int32_t* targets, int64_t T, int64_t V, const in
                           int64_t P, int32_t* cand, int32_t* pos, int32_t* n_unique,
                           int32_t* n_cand, const CandPlan& p, hipStream_t s) {
   hipError_t err;
+  if (V <= kCandMaxV) {
+    hipLaunchKernelGGL(k_cand_one, dim3(1), dim3(kCandThreads), 0, s, targets, T, V, perm, P,
+                       cand, pos, n_unique, n_cand);
+    return hipGetLastError();
+  }
   const uint32_t vb = static_cast<uint32_t>(cdiv(V, 256));
   hipLaunchKernelGGL(k_fill_i32, dim3(static_cast<uint32_t>(cdiv(V, kScanThreads))),
                      dim3(kScanThreads), 0, s, p.flags, V, 0);
