@@ -129,7 +129,7 @@ static vce_status fwd_impl(const void* h, const void* W, const int32_t* targets,
   if (T > 0 && (!ws || ws_bytes < probe.bytes)) return VCE_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return VCE_ERR_ALIGN;
   const vce::FwdPlan p = vce::plan_fwd(T, H, V_real, V_pad, num_shards, shard_rows, ws);
-  return hip_status(vce::run_ce_fwd(h, W, targets, T, H, V_real, V_pad, num_shards, ignore_index,
+  return hip_status(vce::run_ce_fwd(h, W, targets, T, H, V_real, V_pad, ignore_index,
                                     dt == VCE_BF16, lse, loss, loss_sum, n_valid, n_bad_target,
                                     shard_stats, p, static_cast<hipStream_t>(stream)));
 }
@@ -219,7 +219,7 @@ static vce_status argmax_impl(const void* h, const void* W, int64_t T, int64_t H
   if (T > 0 && (!ws || ws_bytes < probe.bytes)) return VCE_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return VCE_ERR_ALIGN;
   const vce::ArgPlan p = vce::plan_argmax(T, H, V_real, V_pad, num_shards, shard_rows, ws);
-  return hip_status(vce::run_argmax(h, W, T, H, V_real, V_pad, num_shards, dt == VCE_BF16, index,
+  return hip_status(vce::run_argmax(h, W, T, H, V_real, V_pad, dt == VCE_BF16, index,
                                     value, shard_value, shard_index, p,
                                     static_cast<hipStream_t>(stream)));
 }

@@ -406,7 +406,7 @@ hipError_t run_fill_scalars(float* f0, int32_t* i0, int32_t* i1, hipStream_t s) 
 }
 
 hipError_t run_ce_fwd(const void* h, const void* W, const int32_t* targets, int64_t T, int64_t H,
-                      int64_t V_real, int64_t V_pad, int32_t n, int32_t ignore_index, bool bf16,
+                      int64_t V_real, int64_t V_pad, int32_t ignore_index, bool bf16,
                       float* lse, float* loss, float* loss_sum, int32_t* n_valid, int32_t* n_bad,
                       float* shard_stats, const FwdPlan& p, hipStream_t s) {
   if (T == 0) return run_fill_scalars(loss_sum, n_valid, n_bad, s);
@@ -442,7 +442,7 @@ hipError_t run_ce_fwd(const void* h, const void* W, const int32_t* targets, int6
 }
 
 hipError_t run_argmax(const void* h, const void* W, int64_t T, int64_t H, int64_t V_real,
-                      int64_t V_pad, int32_t n, bool bf16, int32_t* index, float* value,
+                      int64_t V_pad, bool bf16, int32_t* index, float* value,
                       float* shard_value, int32_t* shard_index, const ArgPlan& p,
                       hipStream_t s) {
   if (T == 0) return hipSuccess;

@@ -211,7 +211,7 @@ CandPlan plan_cand(int64_t T, int64_t V, void* ws);
 
 // Launchers (all enqueue on `s`; return the first launch error).
 hipError_t run_ce_fwd(const void* h, const void* W, const int32_t* targets, int64_t T, int64_t H,
-                      int64_t V_real, int64_t V_pad, int32_t n, int32_t ignore_index, bool bf16,
+                      int64_t V_real, int64_t V_pad, int32_t ignore_index, bool bf16,
                       float* lse, float* loss, float* loss_sum, int32_t* n_valid, int32_t* n_bad,
                       float* shard_stats, const FwdPlan& p, hipStream_t s);
 
@@ -224,7 +224,7 @@ hipError_t run_ce_bwd(const void* h, const void* W, const int32_t* targets, cons
                       void* const* events);
 
 hipError_t run_argmax(const void* h, const void* W, int64_t T, int64_t H, int64_t V_real,
-                      int64_t V_pad, int32_t n, bool bf16, int32_t* index, float* value,
+                      int64_t V_pad, bool bf16, int32_t* index, float* value,
                       float* shard_value, int32_t* shard_index, const ArgPlan& p, hipStream_t s);
 
 hipError_t run_emb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, int64_t V_real,
