@@ -954,12 +954,14 @@ __global__ void k_cand_counts(const int32_t* __restrict__ uidx, int64_t V, int64
 }
 
 // One workgroup builds the candidate list for vocabularies up to kCandMaxV
-// rows, with bit maps in LDS: the targets' flags, then the not-in map of the
-// permutation; word prefixes of their popcounts give every unique target its
-// position and every negative its rank. Same results as the multi-launch
-// path below (unique targets ascending, then the first P - |U| entries of
-// perm that are not unique targets).
+// rows, with the targets' flags as a bit map in LDS: word prefixes of its
+// popcounts give every unique target its position; the permutation is read
+// in order only as far as the P - |U| negatives it must supply, each ranked
+// with wave ballots. Same results as the multi-launch path below (unique
+// targets ascending, then the first P - |U| entries of perm that are not
+// unique targets).
 constexpr int kCandThreads = 1024;
+constexpr int kCandLoads = 8;  // global reads in flight per thread
 constexpr int64_t kCandMaxV = 262144;
 
 // exclusive prefix of popc(bits[w]) over w < nw into pre[w]; returns the total
@@ -1001,18 +1003,25 @@ __global__ __launch_bounds__(kCandThreads) void k_cand_one(const int32_t* __rest
                                                            int32_t* __restrict__ n_unique,
                                                            int32_t* __restrict__ n_cand) {
   constexpr int MAXW = static_cast<int>(kCandMaxV / 32);
-  __shared__ uint32_t fbits[MAXW], fpre[MAXW], nbits[MAXW], npre[MAXW];
+  __shared__ uint32_t fbits[MAXW], fpre[MAXW];
   __shared__ uint32_t wsum[kCandThreads / 64];
+  __shared__ uint32_t wcnt[2][kCandThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nw = static_cast<int>((V + 31) / 32);
-  for (int k = tid; k < nw; k += kCandThreads) {
-    fbits[k] = 0u;
-    nbits[k] = 0u;
-  }
+  for (int k = tid; k < nw; k += kCandThreads) fbits[k] = 0u;
   __syncthreads();
-  for (int64_t t = tid; t < T; t += kCandThreads) {
-    const int64_t y = targets[t];
-    if (y >= 0 && y < V) atomicOr(&fbits[y >> 5], 1u << (y & 31));
+  // every global read below is issued kCandLoads at a time: one workgroup
+  // has too few waves to hide one round trip per element
+  for (int64_t t0 = 0; t0 < T; t0 += kCandThreads * kCandLoads) {
+    int32_t y[kCandLoads];
+#pragma unroll
+    for (int u = 0; u < kCandLoads; ++u) {
+      const int64_t t = t0 + u * kCandThreads + tid;
+      y[u] = t < T ? targets[t] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kCandLoads; ++u)
+      if (y[u] >= 0 && y[u] < V) atomicOr(&fbits[y[u] >> 5], 1u << (y[u] & 31));
   }
   __syncthreads();
   const uint32_t nu = cand_word_scan(fbits, fpre, nw, wsum);
@@ -1026,42 +1035,70 @@ __global__ __launch_bounds__(kCandThreads) void k_cand_one(const int32_t* __rest
     }
   }
   // each target's position among the candidates (other values unchanged)
-  for (int64_t t = tid; t < T; t += kCandThreads) {
-    const int64_t y = targets[t];
-    int32_t pt = static_cast<int32_t>(y);
-    if (y >= 0 && y < V) {
-      const uint32_t b = static_cast<uint32_t>(y & 31);
-      pt = static_cast<int32_t>(fpre[y >> 5] + __popc(fbits[y >> 5] & ((1u << b) - 1u)));
+  for (int64_t t0 = 0; t0 < T; t0 += kCandThreads * kCandLoads) {
+    int32_t y[kCandLoads];
+#pragma unroll
+    for (int u = 0; u < kCandLoads; ++u) {
+      const int64_t t = t0 + u * kCandThreads + tid;
+      y[u] = t < T ? targets[t] : -1;
     }
-    pos[t] = pt;
-  }
-  // not-in map of the permutation, 64 entries per wave step
-  for (int64_t i0 = static_cast<int64_t>(w) * 64; i0 < V; i0 += kCandThreads) {
-    const int64_t i = i0 + lane;
-    bool ni = false;
-    if (i < V) {
-      const int64_t r = perm[i];
-      ni = r >= 0 && r < V && !((fbits[r >> 5] >> (r & 31)) & 1u);
-    }
-    const uint64_t m = __ballot(ni);
-    if (lane == 0) {
-      const int k = static_cast<int>(i0 >> 5);
-      nbits[k] = static_cast<uint32_t>(m);
-      if (k + 1 < nw) nbits[k + 1] = static_cast<uint32_t>(m >> 32);
+#pragma unroll
+    for (int u = 0; u < kCandLoads; ++u) {
+      const int64_t t = t0 + u * kCandThreads + tid;
+      if (t >= T) continue;
+      int32_t pt = y[u];
+      if (y[u] >= 0 && y[u] < V) {
+        const uint32_t b = static_cast<uint32_t>(y[u] & 31);
+        pt = static_cast<int32_t>(fpre[y[u] >> 5] + __popc(fbits[y[u] >> 5] & ((1u << b) - 1u)));
+      }
+      pos[t] = pt;
     }
   }
-  __syncthreads();
-  cand_word_scan(nbits, npre, nw, wsum);
-  // the first P - |U| of them, in permutation order
+  // the first P - |U| permutation entries that are valid rows and not
+  // targets, in permutation order: read in blocks of kCandThreads * kCandLoads
+  // entries (wave w takes kCandLoads groups of 64 in a row), each entry's rank
+  // among them = those before its block + those of earlier waves + those of
+  // earlier groups and lower lanes of its own wave; reading stops once the
+  // ranks reach P - |U|
   const int64_t need = P > nu ? P - nu : 0;
-  for (int k = tid; k < nw; k += kCandThreads) {
-    uint32_t b = nbits[k];
-    int64_t at = npre[k];
-    while (b && at < need) {
-      cand[nu + at] = perm[static_cast<int64_t>(k) * 32 + (__ffs(b) - 1)];
-      ++at;
-      b &= b - 1u;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int64_t found = 0;  // ranks handed out before this block (the same in every thread)
+  for (int64_t base = 0, it = 0; base < V && found < need;
+       base += kCandThreads * kCandLoads, ++it) {
+    int32_t r[kCandLoads];
+#pragma unroll
+    for (int u = 0; u < kCandLoads; ++u) {
+      const int64_t i = base + (static_cast<int64_t>(w) * kCandLoads + u) * 64 + lane;
+      r[u] = i < V ? perm[i] : -1;
     }
+    uint64_t m[kCandLoads];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int u = 0; u < kCandLoads; ++u) {
+      const bool ni = r[u] >= 0 && r[u] < V && !((fbits[r[u] >> 5] >> (r[u] & 31)) & 1u);
+      m[u] = __ballot(ni);
+      cnt += static_cast<uint32_t>(__popcll(m[u]));
+    }
+    // two sets of wave counts, so one barrier per block suffices
+    if (lane == 0) wcnt[it & 1][w] = cnt;
+    __syncthreads();
+    uint32_t wbase = 0, tot = 0;
+#pragma unroll
+    for (int k = 0; k < kCandThreads / 64; ++k) {
+      const uint32_t c = wcnt[it & 1][k];
+      if (k < w) wbase += c;
+      tot += c;
+    }
+    int64_t at = found + wbase;
+#pragma unroll
+    for (int u = 0; u < kCandLoads; ++u) {
+      if ((m[u] >> lane) & 1ull) {
+        const int64_t q = at + __popcll(m[u] & below);
+        if (q < need) cand[nu + q] = r[u];
+      }
+      at += __popcll(m[u]);
+    }
+    found += tot;
   }
   if (tid == 0) {
     *n_unique = static_cast<int32_t>(nu);
