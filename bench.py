@@ -471,8 +471,7 @@ def main():
         perm5 = torch.from_numpy(inp5.perm).to(dev)
         ws5 = V.Workspaces(dev, cand=V.vss_candidates_workspace_bytes(T5, V5),
                            fwd=V.vce_fwd_workspace_bytes(T5, H5, P5, P5, 1, dt_code),
-                           bwd=V.vce_bwd_workspace_bytes(T5, H5, P5, P5, 1, dt_code),
-                           emb=V.vemb_bwd_workspace_bytes(P5, H5, V5, V5))
+                           bwd=V.vce_bwd_workspace_bytes(T5, H5, P5, P5, 1, dt_code))
         dW5 = torch.empty(V5, H5, **f32)
 
         def samp():

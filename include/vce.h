@@ -331,9 +331,9 @@ vce_status vce_remap(const int32_t* in, int64_t T, const int32_t* map, int64_t V
  * unchanged (so ignore_index stays ignored, other values stay invalid).     *
  * In:  targets [T], perm [V] int32.  Out: cand [cand_cap] int32 with        *
  *      cand_cap >= max(P, min(T, V)); pos [T] int32; n_unique [1], n_cand   *
- *      [1] int32. The candidate rows' gather, cross-entropy and scatter-back *
- *      reuse vemb_fwd, vce_fwd/vce_bwd (V_real = V_pad = n_cand, one shard)  *
- *      and vemb_bwd.                                                         *
+ *      [1] int32. The candidate rows' gather and cross-entropy reuse       *
+ *      vemb_fwd and vce_fwd/vce_bwd (V_real = V_pad = n_cand, one shard);    *
+ *      vss_scatter takes the candidate rows' gradient back to the table.     *
  * ------------------------------------------------------------------------ */
 size_t vss_candidates_workspace_bytes(int64_t T, int64_t V);
 
@@ -341,6 +341,25 @@ vce_status vss_candidates(const int32_t* targets, int64_t T, int64_t V, int32_t 
                           const int32_t* perm, int64_t P, int32_t* cand, int64_t cand_cap,
                           int32_t* pos, int32_t* n_unique, int32_t* n_cand,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Sampled-softmax gradient scatter.                                         *
+ *                                                                           *
+ * [SS] Setup: only the candidate rows take part in the loss, so only they   *
+ * receive gradient. For i < P with cand[i] in [0, V): dW[cand[i]] = dWc[i]  *
+ * (accumulate = 0: every other row of dW is set to zero) or dW[cand[i]] +=  *
+ * dWc[i] (accumulate = 1); other entries of cand are skipped. The entries   *
+ * in [0, V) must be distinct, as vss_candidates makes them (with a repeat,  *
+ * which of its rows lands is unspecified; vemb_bwd sums IDs that repeat):   *
+ * this is vemb_bwd's scatter-add for distinct IDs, without its sort and     *
+ * workspace.                                                                *
+ * In:  cand [P] int32, dWc [P, H] f32.  Out: dW [V, H] f32.                 *
+ * Errors: P < 0, V < 1 or H <= 0: VCE_ERR_SHAPE; accumulate not 0 or 1:     *
+ * VCE_ERR_DTYPE; dW NULL, or cand / dWc NULL with P > 0: VCE_ERR_NULL;      *
+ * H % 8 != 0 or a misaligned pointer: VCE_ERR_ALIGN.                        *
+ * ------------------------------------------------------------------------ */
+vce_status vss_scatter(const int32_t* cand, int64_t P, const float* dWc, int64_t H, int64_t V,
+                       float* dW, int32_t accumulate, void* stream);
 
 #ifdef __cplusplus
 }

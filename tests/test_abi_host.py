@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in vce.SIGNATURES, n
@@ -199,6 +199,21 @@ def test_candidates_argument_errors():
     assert args(ign=3) == SHAPE
     assert args(wsb=need - 1) == WORKSPACE
     assert args(ws=NUL) == WORKSPACE
+
+
+def test_scatter_argument_errors():
+    args = lambda cand=A, P=10, src=B, H=64, V=100, dW=C, acc=0: lib.vss_scatter(
+        cand, P, src, H, V, dW, acc, None)
+    assert args(P=-1) == SHAPE
+    assert args(V=0) == SHAPE
+    assert args(H=0) == SHAPE
+    assert args(acc=2) == DTYPE
+    assert args(dW=NUL) == NULL
+    assert args(cand=NUL) == NULL
+    assert args(src=NUL) == NULL
+    assert args(H=60) == ALIGN
+    assert args(dW=MIS) == ALIGN
+    assert args(src=MIS) == ALIGN
 
 
 def test_workspace_queries_are_deterministic_and_reject_bad_shapes():

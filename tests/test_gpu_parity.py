@@ -373,6 +373,28 @@ def test_candidates_bit_exact(V, T, Vc, P):
     assert np.array_equal(c.pos.cpu().numpy(), pos.astype(np.int32))
 
 
+@pytest.mark.parametrize("P,H,Vt,acc", [(0, 64, 50, 0), (1, 8, 3, 1), (777, 264, 5000, 0),
+                                         (2000, 2056, 3000, 1), (4096, 1536, 40000, 0)])
+def test_sampled_scatter_exact(V, P, H, Vt, acc):
+    """vss_scatter against the oracle's scatter-add on distinct rows (some
+    outside [0, V), which are skipped): a single contribution per row, so the
+    result is exact (plus the old row when accumulating)."""
+    say(f"case sampled scatter P={P} H={H} V={Vt} accumulate={acc}")
+    dev = "cuda"
+    rng = np.random.default_rng(P * 7 + H)
+    cand = rng.permutation(Vt + 40)[:P].astype(np.int32) - 20  # distinct; some < 0 or >= V
+    dWc = rng.standard_normal((P, H)).astype(np.float32)
+    dW0 = rng.standard_normal((Vt, H)).astype(np.float32)
+    dW = torch.from_numpy(dW0).to(dev)
+    out = V.vss_scatter(torch.from_numpy(cand).to(dev), torch.from_numpy(dWc).to(dev), Vt, dW=dW,
+                        accumulate=bool(acc))
+    torch.cuda.synchronize()
+    ref, _ = oracle.scatter_add(cand, dWc.astype(np.float64), Vt, Vt)
+    if acc:
+        ref = dW0.astype(np.float64) + ref
+    np.testing.assert_array_equal(out.cpu().numpy(), ref.astype(np.float32))
+
+
 def test_sampled_step_small(V):
     say("case sampled step T=1024 H=128 V=16384 P=2048")
     dev = "cuda"

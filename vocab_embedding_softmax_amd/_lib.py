@@ -62,6 +62,7 @@ SIGNATURES = {
     "vce_remap": (_I32, [_P, _I64, _P, _I64, _P, _P]),
     "vss_candidates_workspace_bytes": (_SZ, [_I64, _I64]),
     "vss_candidates": (_I32, [_P, _I64, _I64, _I32, _P, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "vss_scatter": (_I32, [_P, _I64, _P, _I64, _I64, _P, _I32, _P]),
 }
 
 
@@ -423,3 +424,22 @@ def vss_candidates(targets: torch.Tensor, V: int, perm: torch.Tensor, P: int,
                             _ptr(ws), ws.numel(), _stream(stream, dev))
     _check("vss_candidates", st)
     return out
+
+
+def vss_scatter(cand: torch.Tensor, dWc: torch.Tensor, V: int, *,
+                dW: Optional[torch.Tensor] = None, accumulate: bool = False,
+                stream=None) -> torch.Tensor:
+    """Candidate rows' gradient back to the table: dW[cand[i]] (+)= dWc[i] for
+    cand entries in [0, V), which must be distinct. cand [P] int32, dWc [P, H]
+    float32; dW [V, H] float32 (every other row zeroed unless accumulate)."""
+    P, H = dWc.shape
+    _need(cand, "cand", torch.int32, (P,))
+    _need(dWc, "dWc", torch.float32, (P, H))
+    dev = dWc.device
+    if dW is None:
+        dW = torch.empty(V, H, dtype=torch.float32, device=dev)
+    _need(dW, "dW", torch.float32, (V, H))
+    st = lib.vss_scatter(_ptr(cand), P, _ptr(dWc), H, V, _ptr(dW), 1 if accumulate else 0,
+                         _stream(stream, dev))
+    _check("vss_scatter", st)
+    return dW

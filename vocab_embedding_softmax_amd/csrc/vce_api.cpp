@@ -342,4 +342,16 @@ vce_status vss_candidates(const int32_t* targets, int64_t T, int64_t V, int32_t 
                                         static_cast<hipStream_t>(stream)));
 }
 
+vce_status vss_scatter(const int32_t* cand, int64_t P, const float* dWc, int64_t H, int64_t V,
+                       float* dW, int32_t accumulate, void* stream) {
+  if (P < 0 || V < 1 || H <= 0 || P > kMaxDim || V > kMaxDim || H > kMaxDim) return VCE_ERR_SHAPE;
+  if (accumulate != 0 && accumulate != 1) return VCE_ERR_DTYPE;
+  if (!dW) return VCE_ERR_NULL;
+  if (P > 0 && (!cand || !dWc)) return VCE_ERR_NULL;
+  if (H % 8 != 0 || !aligned16(dW)) return VCE_ERR_ALIGN;
+  if (P > 0 && (!aligned4(cand) || !aligned16(dWc))) return VCE_ERR_ALIGN;
+  return hip_status(
+      vce::run_ss_scatter(cand, P, dWc, H, V, dW, accumulate, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

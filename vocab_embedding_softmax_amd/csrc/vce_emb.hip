@@ -1106,6 +1106,50 @@ __global__ __launch_bounds__(kCandThreads) void k_cand_one(const int32_t* __rest
   }
 }
 
+// Gradient scatter of the sampled softmax ([SS] Setup: only the candidate
+// rows take part in the loss, so only they receive gradient): candidate row
+// i goes to row cand[i] of the table, entries outside [0, V) skipped. The
+// candidates are distinct, so this is the scatter-add without the sort: one
+// wave per candidate row, kScatLoads float4 per lane in flight. ACC adds into
+// the table row; otherwise the row is copied (the launcher zeroes the table
+// first). ACC is a template argument: as a run-time branch inside the row
+// loop it doubled the kernel's time.
+constexpr int kScatLoads = 8;
+template <bool ACC>
+__global__ __launch_bounds__(256) void k_scatter_rows(const int32_t* __restrict__ cand, int64_t P,
+                                                      const float* __restrict__ src, int64_t H,
+                                                      int64_t V, float* __restrict__ dW) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (i >= P) return;
+  const int64_t v = cand[i];
+  if (v < 0 || v >= V) return;
+  const f32x4* s = reinterpret_cast<const f32x4*>(src + i * H);
+  f32x4* d = reinterpret_cast<f32x4*>(dW + v * H);
+  const int64_t n4 = H / 4;
+  for (int64_t j0 = 0; j0 < n4; j0 += 64 * kScatLoads) {
+    f32x4 x[kScatLoads], y[kScatLoads];
+#pragma unroll
+    for (int u = 0; u < kScatLoads; ++u) {
+      const int64_t j = j0 + u * 64 + lane;
+      if (j < n4) {
+        x[u] = s[j];
+        if constexpr (ACC) y[u] = d[j];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kScatLoads; ++u) {
+      const int64_t j = j0 + u * 64 + lane;
+      if (j < n4) {
+        if constexpr (ACC)
+          d[j] = y[u] + x[u];
+        else
+          d[j] = x[u];
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 
 hipError_t run_emb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, int64_t V_real,
@@ -1184,6 +1228,24 @@ hipError_t run_emb_bwd(const int32_t* ids, const void* dout, bool dout_bf16, int
   const dim3 fgrid(static_cast<uint32_t>(p.nchunks), static_cast<uint32_t>(p.nslices));
   hipLaunchKernelGGL(k_seg_fix, fgrid, dim3(64 * kFixWaves), 0, s, p.skey, p.n_sorted,
                      p.chunk_start, H, dW, accumulate, p.partial);
+  return hipGetLastError();
+}
+
+hipError_t run_ss_scatter(const int32_t* cand, int64_t P, const float* dWc, int64_t H, int64_t V,
+                          float* dW, int32_t accumulate, hipStream_t s) {
+  if (!accumulate) {
+    const int64_t n4 = V * H / 4;
+    hipLaunchKernelGGL(k_fill_f4, dim3(static_cast<uint32_t>(cdiv(n4, 256))), dim3(256), 0, s,
+                       reinterpret_cast<float4*>(dW), n4);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (P == 0) return hipSuccess;
+  const dim3 grid(static_cast<uint32_t>(cdiv(P, 4)));
+  if (accumulate)
+    hipLaunchKernelGGL(k_scatter_rows<true>, grid, dim3(256), 0, s, cand, P, dWc, H, V, dW);
+  else
+    hipLaunchKernelGGL(k_scatter_rows<false>, grid, dim3(256), 0, s, cand, P, dWc, H, V, dW);
   return hipGetLastError();
 }
 

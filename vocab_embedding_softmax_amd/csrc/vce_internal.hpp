@@ -243,6 +243,10 @@ hipError_t run_emb_bwd(const int32_t* ids, const void* dout, bool dout_bf16, int
                        int64_t V_real, int64_t V_pad, float* dW, int32_t accumulate,
                        const EmbBwdPlan& p, hipStream_t s);
 
+// dW[cand[i]] (+)= dWc[i] for distinct cand entries in [0, V); the rest of
+// dW zeroed first unless accumulating
+hipError_t run_ss_scatter(const int32_t* cand, int64_t P, const float* dWc, int64_t H, int64_t V,
+                          float* dW, int32_t accumulate, hipStream_t s);
 hipError_t run_candidates(const int32_t* targets, int64_t T, int64_t V, const int32_t* perm,
                           int64_t P, int32_t* cand, int32_t* pos, int32_t* n_unique,
                           int32_t* n_cand, const CandPlan& p, hipStream_t s);

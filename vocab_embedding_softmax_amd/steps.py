@@ -95,8 +95,7 @@ def sampled_step(h, W, targets, perm, P, ignore_index=-100, *, grad_loss=None,
                   stream=stream)
     b = L.vce_bwd(h, Wc, c.pos, f.lse, grad_loss, f.n_valid, P, 1, ignore_index, reduction,
                   ws=None if ws is None else ws["bwd"], stream=stream)
-    dW = L.vemb_bwd(cand, b.dW, V, V, 1, dW=dW, accumulate=False,
-                    ws=None if ws is None else ws["emb"], stream=stream)
+    dW = L.vss_scatter(cand, b.dW, V, dW=dW, accumulate=False, stream=stream)
     return StepOut(f, b.dh, dW, dict(cand=c.cand, pos=c.pos, n_unique=c.n_unique,
                                      n_cand=c.n_cand, Wc=Wc, dWc=b.dW))
 
