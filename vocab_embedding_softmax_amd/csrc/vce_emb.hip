@@ -115,10 +115,22 @@ __global__ __launch_bounds__(256) void k_vemb_fwd(const int32_t* __restrict__ id
   const int lane = threadIdx.x & 63;
   if (blockIdx.x == 0 && n_bad) {
     __shared__ int32_t cnt[4];
+    // 16 reads in flight per lane: with one at a time this workgroup was the
+    // launch's last to finish
+    constexpr int UB = 16;
     int32_t bad = 0;
-    for (int64_t t = threadIdx.x; t < T; t += 256) {
-      const int64_t id = ids[t];
-      bad += (id < 0 || id >= V_real) ? 1 : 0;
+    for (int64_t b0 = 0; b0 < T; b0 += 256 * UB) {
+      int32_t idv[UB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int64_t t = b0 + u * 256 + threadIdx.x;
+        idv[u] = t < T ? ids[t] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int64_t t = b0 + u * 256 + threadIdx.x;
+        bad += (t < T && (idv[u] < 0 || idv[u] >= V_real)) ? 1 : 0;
+      }
     }
     for (int o = 32; o > 0; o >>= 1) bad += __shfl_xor(bad, o);
     if (lane == 0) cnt[threadIdx.x >> 6] = bad;
@@ -244,10 +256,22 @@ __global__ __launch_bounds__(256) void k_ngram_fwd(
   const int lane = threadIdx.x & 63;
   if (blockIdx.x == 0 && n_bad) {
     __shared__ int32_t cnt[4];
+    // 16 reads in flight per lane: with one at a time this workgroup was the
+    // launch's last to finish
+    constexpr int UB = 16;
     int32_t bad = 0;
-    for (int64_t t = threadIdx.x; t < T; t += 256) {
-      const int64_t id = ids[t];
-      bad += (id < 0 || id >= V_real) ? 1 : 0;
+    for (int64_t b0 = 0; b0 < T; b0 += 256 * UB) {
+      int32_t idv[UB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int64_t t = b0 + u * 256 + threadIdx.x;
+        idv[u] = t < T ? ids[t] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int64_t t = b0 + u * 256 + threadIdx.x;
+        bad += (t < T && (idv[u] < 0 || idv[u] >= V_real)) ? 1 : 0;
+      }
     }
     for (int o = 32; o > 0; o >>= 1) bad += __shfl_xor(bad, o);
     if (lane == 0) cnt[threadIdx.x >> 6] = bad;
