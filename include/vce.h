@@ -349,10 +349,9 @@ vce_status vss_candidates(const int32_t* targets, int64_t T, int64_t V, int32_t 
  * receive gradient. For i < P with cand[i] in [0, V): dW[cand[i]] = dWc[i]  *
  * (accumulate = 0: every other row of dW is set to zero) or dW[cand[i]] +=  *
  * dWc[i] (accumulate = 1); other entries of cand are skipped. The entries   *
- * in [0, V) must be distinct, as vss_candidates makes them (with a repeat,  *
- * which of its rows lands is unspecified; vemb_bwd sums IDs that repeat):   *
- * this is vemb_bwd's scatter-add for distinct IDs, without its sort and     *
- * workspace.                                                                *
+ * in [0, V) must be distinct, as vss_candidates makes them (a repeated     *
+ * entry leaves its row undefined; vemb_bwd sums IDs that repeat): this is   *
+ * vemb_bwd's scatter-add for distinct IDs, without its sort and workspace.  *
  * In:  cand [P] int32, dWc [P, H] f32.  Out: dW [V, H] f32.                 *
  * Errors: P < 0, V < 1 or H <= 0: VCE_ERR_SHAPE; accumulate not 0 or 1:     *
  * VCE_ERR_DTYPE; dW NULL, or cand / dWc NULL with P > 0: VCE_ERR_NULL;      *
