@@ -356,6 +356,8 @@ def test_ot_h_step(V, dt, T, H, Vr, Vp, n):
     (3000, 20001, 2048),      # a partial last word of the bit maps
     (500, 1000, 3000),        # P above V: every non-target row is a negative
     (3000, 300000, 4096),     # past the LDS bit maps: flags, scans and emits in several launches
+    (20000, 262144, 16384),   # the largest one-workgroup table; negatives from two read blocks
+    (3000, 262145, 4096),     # one row past it: the several-launch path
 ])
 def test_candidates_bit_exact(V, T, Vc, P):
     say(f"case candidates T={T} V={Vc} P={P}")
