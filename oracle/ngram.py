@@ -23,8 +23,10 @@ Readings where the page is silent (also in the design notes):
   - the n-gram tables are split into the same number of contiguous, equal
     shards as the unigram table (rows_n % num_shards == 0) and looked up by
     owner and local index the same way.
-Pinned by tests/test_oracle_pins.py::test_ngram_* (brute force over positions,
-range and uniformity of the rows, finite differences of the backward).
+Pinned by tests/test_oracle_pins.py::test_mix64_is_the_splitmix64_finaliser
+(the generator's published first outputs from state 0) and test_ngram_* (brute
+force over positions, range and uniformity of the rows, finite differences of
+the backward).
 """
 
 from __future__ import annotations

@@ -604,6 +604,32 @@ def test_ngram_rows_spread_uniformly():
     assert len({oracle.mix64(int(k)) for k in keys}) == len(keys)
 
 
+def test_mix64_is_the_splitmix64_finaliser():
+    """Known answers: the SplitMix64 generator (state advanced by its golden
+    gamma, each output the finaliser of the new state) started from state 0
+    yields the published first outputs (tests/golden/splitmix64_seed0.txt).
+    A changed shift or multiplier of the finaliser changes all three."""
+    gamma = seed = None
+    outs = []
+    with open(os.path.join(GOLDEN, "splitmix64_seed0.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, val = line.split()
+            if key == "gamma":
+                gamma = int(val, 16)
+            elif key == "seed":
+                seed = int(val)
+            elif key == "output":
+                outs.append(int(val, 16))
+    assert gamma is not None and seed is not None and len(outs) == 3
+    state = seed
+    for want in outs:
+        state = (state + gamma) & ((1 << 64) - 1)
+        assert oracle.mix64(state) == want, hex(oracle.mix64(state))
+
+
 def test_ngram_embed_bruteforce():
     rng = np.random.default_rng(21)
     T, H, V_real, V_pad, r2, r3 = 9, 4, 12, 16, 10, 14
