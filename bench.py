@@ -50,7 +50,7 @@ def parse():
                     help="skip the CE-only field on the T=8192 workload")
     ap.add_argument("--no-sampled", action="store_true",
                     help="skip the sampled-softmax field (its own T=16384, H=1536 workload)")
-    ap.add_argument("--cpu-tokens", type=int, default=2048,
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens in the oracle's CPU-baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one elementwise pass over 1 GiB (read 1 GiB, write 1 GiB): "
@@ -96,31 +96,31 @@ def measured_traffic(tag: str):
 
 
 def cpu_baseline(inp, n_tok: int):
-    """The float64 oracle as it stands, on the first n_tok tokens of the same
-    workload, on this host's cores. Returns tokens/s of the oracle step."""
+    """The float64 oracle as it stands (oracle.parallel: its definitions over
+    token and vocabulary chunks on a pool of threads, one BLAS thread each),
+    on the first n_tok tokens of the same workload, on this host's cores
+    (at most 16, the host share of one GPU). Returns tokens/s of the oracle
+    step on that sample."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()
-                     if i.get("user_api") == "blas"] or [os.cpu_count() or 1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    workers = oracle.parallel.default_workers()
     W = oracle.decode(inp.W, inp.dtype)
     t0 = time.perf_counter()
     if inp.h is None:
-        oracle.tied_step(inp.ids[:n_tok], inp.targets[:n_tok], W, inp.V_real, inp.V_pad,
-                         inp.num_shards, inp.ignore_index)
+        oracle.parallel.tied_step(inp.ids[:n_tok], inp.targets[:n_tok], W, inp.V_real, inp.V_pad,
+                                  inp.num_shards, inp.ignore_index, workers=workers)
         what = "tied step (gather, CE fwd+bwd, scatter-add)"
     else:
         h = oracle.decode(inp.h[:n_tok], inp.dtype)
-        oracle.cross_entropy(h, W, inp.targets[:n_tok], inp.V_real, inp.V_pad, inp.num_shards,
-                             inp.ignore_index)
+        oracle.parallel.cross_entropy(h, W, inp.targets[:n_tok], inp.V_real, inp.V_pad,
+                                      inp.num_shards, inp.ignore_index, workers=workers)
         what = "CE fwd+bwd"
     dt = time.perf_counter() - t0
     del W
-    return dict(value=n_tok / dt, unit="tokens/s", cores=int(cores), kind="oracle",
-                sample=f"float64 oracle {what} on the first {n_tok} tokens of the same "
-                       f"workload (full V={inp.V_real}, H={inp.H}); {dt:.1f} s wall")
+    return dict(value=n_tok / dt, unit="tokens/s", cores=int(workers), kind="oracle",
+                cpu_model=oracle.parallel.cpu_model(), host_cpus=os.cpu_count(),
+                sample=f"token sample: float64 oracle {what} on the first {n_tok} of the "
+                       f"workload's {inp.T} tokens (full V={inp.V_real}, H={inp.H}), "
+                       f"{workers} threads; {dt:.1f} s wall")
 
 
 def main():
@@ -178,7 +178,9 @@ def main():
             V.vemb_fwd(ids, W, Vr, n, out=h, n_bad=nbad)
         if ev is not None:
             ev[1].record(stream)
-        V.vce_fwd(h, W, tg, Vr, n, inp.ignore_index, out=fo, ws=ws["fwd"])
+        # bad targets are counted on the device and checked after the timed
+        # steps (a check here would synchronise inside the step)
+        V.vce_fwd(h, W, tg, Vr, n, inp.ignore_index, out=fo, ws=ws["fwd"], allow_bad=True)
         if ev is not None:
             ev[2].record(stream)
         V.vce_bwd(h, W, tg, fo.lse, gl, fo.n_valid, Vr, n, inp.ignore_index, V.REDUCE_MEAN,
@@ -202,6 +204,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / a.steps
+    if int(fo.n_bad.item()):
+        raise SystemExit(f"{int(fo.n_bad.item())} bad targets in the workload")
 
     def span(i, j):
         return float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))
@@ -368,7 +372,7 @@ def main():
         V.vce_fwd(h, W, tg, Vr, n, inp.ignore_index, out=fo, **kw)
         e0.record(stream)
         for _ in range(reps):
-            V.vce_fwd(h, W, tg, Vr, n, inp.ignore_index, out=fo, **kw)
+            V.vce_fwd(h, W, tg, Vr, n, inp.ignore_index, out=fo, allow_bad=True, **kw)
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
@@ -396,7 +400,7 @@ def main():
 
         def oth():
             V.ot_h_step(ids, tg, tg2, W, W2, Vr, n, inp.ignore_index, ws=ws, ws2=ws2, h=h,
-                        dh=dh, dW=dW, dW2=dW2)
+                        dh=dh, dW=dW, dW2=dW2, allow_bad=True)
 
         oth()
         torch.cuda.synchronize()
@@ -471,7 +475,8 @@ def main():
         dW3 = torch.empty(inp3.V_pad, H3, **f32)
 
         def ce3():
-            return V.ce_step(h3, W3, tg3, V3, n3, inp3.ignore_index, ws=ws3, dh=dh3, dW=dW3)
+            return V.ce_step(h3, W3, tg3, V3, n3, inp3.ignore_index, ws=ws3, dh=dh3, dW=dW3,
+                             allow_bad=True)
 
         ce3()
         torch.cuda.synchronize()
@@ -507,12 +512,16 @@ def main():
                            bwd=V.vce_bwd_workspace_bytes(T5, H5, P5, P5, 1, dt_code))
         dW5 = torch.empty(V5, H5, **f32)
 
-        def samp():
-            return V.sampled_step(h5, W5, tg5, perm5, P5, inp5.ignore_index, ws=ws5, dW=dW5)
-
-        r5 = samp()
+        # the first call reads the candidate count from the device; the timed
+        # calls of the same batch pass it (no synchronisation inside the step)
+        r5 = V.sampled_step(h5, W5, tg5, perm5, P5, inp5.ignore_index, ws=ws5, dW=dW5)
         torch.cuda.synchronize()
         n_cand = int(r5.extra["n_cand"].item())
+
+        def samp():
+            return V.sampled_step(h5, W5, tg5, perm5, P5, inp5.ignore_index, ws=ws5, dW=dW5,
+                                  n_cand=n_cand, allow_bad=True)
+
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         reps5 = 5

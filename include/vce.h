@@ -334,6 +334,10 @@ vce_status vce_remap(const int32_t* in, int64_t T, const int32_t* map, int64_t V
  *      [1] int32. The candidate rows' gather and cross-entropy reuse       *
  *      vemb_fwd and vce_fwd/vce_bwd (V_real = V_pad = n_cand, one shard);    *
  *      vss_scatter takes the candidate rows' gradient back to the table.     *
+ * Errors: T < 0, V < 1, P < 1, P > V (the candidates are distinct rows),    *
+ * ignore_index in [0, V) or cand_cap too small: VCE_ERR_SHAPE; a NULL       *
+ * pointer: VCE_ERR_NULL; misaligned: VCE_ERR_ALIGN; workspace too small:    *
+ * VCE_ERR_WORKSPACE.                                                        *
  * ------------------------------------------------------------------------ */
 size_t vss_candidates_workspace_bytes(int64_t T, int64_t V);
 

@@ -30,3 +30,4 @@ from .argmax import shard_argmax, merge_shard_argmax, greedy_argmax  # noqa: F40
 from .tied import tied_step  # noqa: F401
 from .oth import OT_H_WEIGHT, ot_h_step  # noqa: F401
 from .ngram import mix64, ngram_backward, ngram_embed, ngram_ids  # noqa: F401
+from . import parallel  # noqa: F401

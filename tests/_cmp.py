@@ -3,7 +3,8 @@
 Tolerances:
   bf16 inputs, fp32 accumulation: |d loss_sum| / |loss_sum| <= 2e-3,
     max_t |d lse_t| <= 1e-2, rel-L2 <= 1e-2 on dh and dW (and on every
-    embedding-gradient tensor);
+    embedding-gradient tensor), and on every 256-row block of dW on its own
+    (tile_rel_l2);
   fp32 inputs: 1e-5 relative on loss, lse (per element) and the gradients (rel-L2).
   Integer and byte results (gathers, counts, candidate lists): bit-exact.
 
@@ -29,13 +30,55 @@ TOL = {
 }
 
 
-def rel_l2(a, b):
-    a = np.asarray(a, dtype=np.float64)
-    b = np.asarray(b, dtype=np.float64)
-    nb = np.linalg.norm(b)
-    if nb == 0:
-        return float(np.linalg.norm(a))
-    return float(np.linalg.norm(a - b) / nb)
+def rel_l2(a, b, block=1 << 16):
+    """||a - b|| / ||b|| (||a|| when b is 0), in float64, a row block at a time
+    so that full-size tables need no float64 copy of the whole tensor."""
+    a = np.asarray(a)
+    b = np.asarray(b)
+    if a.shape != b.shape:
+        raise ValueError(f"shapes differ: {a.shape} vs {b.shape}")
+    if a.ndim < 2:
+        a = a.reshape(-1, 1)
+        b = b.reshape(-1, 1)
+    dd = bb = aa = 0.0
+    for r0 in range(0, a.shape[0], block):
+        x = a[r0:r0 + block].astype(np.float64)
+        y = b[r0:r0 + block].astype(np.float64)
+        dd += float(np.square(x - y).sum())
+        bb += float(np.square(y).sum())
+        aa += float(np.square(x).sum())
+    if bb == 0:
+        return float(np.sqrt(aa))
+    return float(np.sqrt(dd / bb))
+
+
+def tile_rel_l2(got, ref, rows=256, floor_frac=1e-6):
+    """Relative L2 error of each block of `rows` consecutive rows (one GEMM
+    tile of dW): ||got_j - ref_j|| / max(||ref_j||, floor), with the floor
+    floor_frac * ||ref|| / sqrt(number of blocks) so that a block whose
+    reference is (nearly) zero is held to an absolute bound. Returns the
+    per-block errors. A whole-tensor rel-L2 is dominated by the few rows of
+    frequent targets; this is not."""
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    n = (ref.shape[0] + rows - 1) // rows
+    dn = np.zeros(n)
+    rn = np.zeros(n)
+    for j in range(n):
+        x = got[j * rows:(j + 1) * rows].astype(np.float64)
+        y = ref[j * rows:(j + 1) * rows].astype(np.float64)
+        dn[j] = np.sqrt(np.square(x - y).sum())
+        rn[j] = np.sqrt(np.square(y).sum())
+    floor = floor_frac * np.sqrt(np.square(rn).sum()) / np.sqrt(max(n, 1))
+    return dn / np.maximum(rn, max(floor, 1e-300))
+
+
+def check_dw_tiles(got, ref, dtype, what="dW", rows=256):
+    e = tile_rel_l2(got, ref, rows)
+    j = int(np.argmax(e)) if e.size else 0
+    assert e.size == 0 or e[j] <= TOL[dtype]["grad"], \
+        f"{what}: rows [{j * rows}, {(j + 1) * rows}) rel-L2 {e[j]}"
+    return float(e.max()) if e.size else 0.0
 
 
 def check_ce(gpu: dict, ref: dict, dtype: str, V_real: int, check_grads: bool = True):
@@ -60,6 +103,7 @@ def check_ce(gpu: dict, ref: dict, dtype: str, V_real: int, check_grads: bool = 
         e_dw = rel_l2(gpu["dW"], ref["dW"])
         assert e_dh <= tol["grad"], f"dh rel-L2 {e_dh}"
         assert e_dw <= tol["grad"], f"dW rel-L2 {e_dw}"
+        check_dw_tiles(gpu["dW"][:V_real], ref["dW"][:V_real], dtype)
         assert not gpu["dW"][V_real:].any(), "padded dW rows must be exactly 0"
         assert not gpu["dh"][~valid].any(), "ignored tokens must get dh = 0"
 

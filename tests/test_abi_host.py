@@ -196,6 +196,7 @@ def test_candidates_argument_errors():
         A, 8, 100, ign, B, P, C, cap, A, B, C, ws, wsb, None)
     assert args(P=0) == SHAPE
     assert args(cap=9) == SHAPE          # capacity below max(P, min(T, V))
+    assert args(P=101, cap=101) == SHAPE  # more candidates than rows: they cannot be distinct
     assert args(ign=3) == SHAPE
     assert args(wsb=need - 1) == WORKSPACE
     assert args(ws=NUL) == WORKSPACE

@@ -77,8 +77,9 @@ def test_tied_step_graph_replays(V):
     gb, eb = buffers(), buffers()
 
     def step(b, i, t):
+        # no synchronisation inside a captured step: n_bad is checked by the test
         return V.tied_step(i, t, W, Vr, n, inp.ignore_index, grad_loss=gl, ws=b["ws"], h=b["h"],
-                           dh=b["dh"], dW=b["dW"])
+                           dh=b["dh"], dW=b["dW"], allow_bad=True)
 
     g, out = capture(lambda: step(gb, ids, tg))
 
@@ -90,6 +91,7 @@ def test_tied_step_graph_replays(V):
         same(out.fwd.loss_sum, ref.fwd.loss_sum, "loss_sum")
         same(out.fwd.lse, ref.fwd.lse, "lse")
         same(out.fwd.n_valid, ref.fwd.n_valid, "n_valid")
+        assert int(out.fwd.n_bad.item()) == 0
         same(out.dh, ref.dh, "dh")
         same(out.dW, ref.dW, "dW")
         same(out.extra["h"], ref.extra["h"], "h")
@@ -121,8 +123,9 @@ def test_sampled_step_graph_replays(V):
     gb, eb = buffers(), buffers()
 
     def step(b):
+        # the batch has fewer distinct targets than P, so n_cand = P (checked below)
         return V.sampled_step(h, W, tg, perm, P, inp.ignore_index, grad_loss=gl, ws=b["ws"],
-                              dW=b["dW"])
+                              dW=b["dW"], n_cand=P, allow_bad=True)
 
     g, out = capture(lambda: step(gb))
     for _ in range(3):
@@ -131,6 +134,7 @@ def test_sampled_step_graph_replays(V):
         g.replay()
         torch.cuda.synchronize()
         same(out.extra["cand"][:P], ref.extra["cand"][:P], "cand")
+        assert int(out.extra["n_cand"].item()) == P and int(out.fwd.n_bad.item()) == 0
         same(out.fwd.loss_sum, ref.fwd.loss_sum, "loss_sum")
         same(out.dh, ref.dh, "dh")
         same(out.dW, ref.dW, "dW")

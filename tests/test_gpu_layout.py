@@ -78,10 +78,11 @@ def _gpu_ce(V, inp, rows, n_even=None, W_bits=None, targets=None):
     tg = torch.from_numpy(inp.targets if targets is None else targets).to(dev)
     if n_even is None:
         n = len(rows) - 1
-        f = V.vce_fwd(h, W, tg, inp.V_real, n, inp.ignore_index, shard_stats=True,
+        f = V.vce_fwd(h, W, tg, inp.V_real, n, inp.ignore_index, shard_stats=True, allow_bad=True,
                       shard_rows=[int(x) for x in rows])
     else:
-        f = V.vce_fwd(h, W, tg, inp.V_real, n_even, inp.ignore_index, shard_stats=True)
+        f = V.vce_fwd(h, W, tg, inp.V_real, n_even, inp.ignore_index, shard_stats=True,
+                      allow_bad=True)
     gl = torch.ones(1, dtype=torch.float32, device=dev)
     b = V.vce_bwd(h, W, tg, f.lse, gl, f.n_valid, inp.V_real, 1, inp.ignore_index, MEAN)
     torch.cuda.synchronize()

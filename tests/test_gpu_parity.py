@@ -37,7 +37,7 @@ def gpu_ce(V, inp, grad_loss=1.0, reduction=MEAN, num_shards=None, W_override=No
     tg = torch.from_numpy(inp.targets).to(dev)
     gl = torch.tensor([grad_loss], dtype=torch.float32, device=dev)
     r = V.ce_step(h, W, tg, inp.V_real, n, inp.ignore_index, grad_loss=gl,
-                  reduction=reduction, shard_stats=True)
+                  reduction=reduction, shard_stats=True, allow_bad=True)
     torch.cuda.synchronize()
     f = r.fwd
     return dict(lse=f.lse.cpu().numpy(), loss=f.loss.cpu().numpy(),
@@ -291,7 +291,7 @@ def test_tied_step_small(V):
     dev = "cuda"
     W = V.from_bits(inp.W, "bf16", dev)
     r = V.tied_step(torch.from_numpy(inp.ids).to(dev), torch.from_numpy(inp.targets).to(dev),
-                    W, inp.V_real, inp.num_shards)
+                    W, inp.V_real, inp.num_shards, allow_bad=True)
     torch.cuda.synchronize()
     ref = oracle.tied_step(inp.ids, inp.targets, oracle.decode(inp.W, "bf16"), inp.V_real,
                            inp.V_pad, inp.num_shards)
@@ -319,7 +319,7 @@ def test_ot_h_step(V, dt, T, H, Vr, Vp, n):
     W = V.from_bits(inp.W, dt, dev)
     W2 = V.from_bits(W2b, dt, dev)
     r = V.ot_h_step(torch.from_numpy(inp.ids).to(dev), torch.from_numpy(inp.targets).to(dev),
-                    torch.from_numpy(y2).to(dev), W, W2, Vr, n)
+                    torch.from_numpy(y2).to(dev), W, W2, Vr, n, allow_bad=True)
     torch.cuda.synchronize()
     ref = oracle.ot_h_step(inp.ids, inp.targets, y2, oracle.decode(inp.W, dt),
                            oracle.decode(W2b, dt), Vr, Vp, n)
@@ -341,7 +341,7 @@ def test_ot_h_step(V, dt, T, H, Vr, Vp, n):
     assert not r.extra["dW2"][Vr:].cpu().numpy().any()
     # the second head's share of dh alone: run the first head only and compare
     r1 = V.tied_step(torch.from_numpy(inp.ids).to(dev), torch.from_numpy(inp.targets).to(dev),
-                     W, Vr, n)
+                     W, Vr, n, allow_bad=True)
     d2 = (r.dh - r1.dh).cpu().numpy()
     want2 = ref["dh"] - oracle.tied_step(inp.ids, inp.targets, oracle.decode(inp.W, dt), Vr, Vp,
                                          n)["dh"]
@@ -354,7 +354,9 @@ def test_ot_h_step(V, dt, T, H, Vr, Vp, n):
 @pytest.mark.parametrize("T,Vc,P", [
     (3000, 20000, 2048),      # one workgroup, bit maps in LDS
     (3000, 20001, 2048),      # a partial last word of the bit maps
-    (500, 1000, 3000),        # P above V: every non-target row is a negative
+    (500, 1000, 1000),        # P = V: every non-target row is a negative
+    (3000, 20000, 256),       # more distinct targets than P: the candidates are U alone
+    (3000, 300000, 256),      # the same on the several-launch path
     (3000, 300000, 4096),     # past the LDS bit maps: flags, scans and emits in several launches
     (20000, 262144, 16384),   # the largest one-workgroup table; negatives from two read blocks
     (3000, 262145, 4096),     # one row past it: the several-launch path
@@ -373,6 +375,73 @@ def test_candidates_bit_exact(V, T, Vc, P):
     # with P above V only V - |U| negatives exist: the list holds those
     assert np.array_equal(c.cand.cpu().numpy()[:cand.shape[0]], cand.astype(np.int32))
     assert np.array_equal(c.pos.cpu().numpy(), pos.astype(np.int32))
+
+
+def test_candidates_reject_more_than_the_table(V):
+    dev = "cuda"
+    tg = torch.zeros(8, dtype=torch.int32, device=dev)
+    perm = torch.arange(100, dtype=torch.int32, device=dev)
+    with pytest.raises(V.VceError):
+        V.vss_candidates(tg, 100, perm, 101)
+
+
+def test_sampled_step_more_distinct_targets_than_P(V):
+    """|U| > P: the composite is sized by n_cand = |U| (the candidates are the
+    distinct targets alone, no negatives); every valid target keeps its
+    class, nothing is dropped as a bad target."""
+    say("case sampled step T=2048 H=128 V=8192 P=256 (|U| > P)")
+    dev = "cuda"
+    inp = make_sampled_inputs(2048, 128, 8192, 256, "bf16", seed=31, zipf_s=0.6,
+                              ignore_frac=0.02)
+    h = V.from_bits(inp.h, "bf16", dev)
+    W = V.from_bits(inp.W, "bf16", dev)
+    tg = torch.from_numpy(inp.targets).to(dev)
+    perm = torch.from_numpy(inp.perm).to(dev)
+    ref = oracle.sampled_step(oracle.decode(inp.h, "bf16"), oracle.decode(inp.W, "bf16"),
+                              inp.targets, inp.perm, inp.P)
+    assert ref["n_unique"] > inp.P
+    ws = V.Workspaces(dev, cand=V.vss_candidates_workspace_bytes(2048, 8192),
+                      fwd=V.vce_fwd_workspace_bytes(2048, 128, 256, 256, 1),
+                      bwd=V.vce_bwd_workspace_bytes(2048, 128, 256, 256, 1))
+    r = V.sampled_step(h, W, tg, perm, inp.P, ws=ws)
+    torch.cuda.synchronize()
+    n_cand = int(r.extra["n_cand"].item())
+    assert n_cand == ref["n_unique"] == ref["cand"].shape[0]
+    assert np.array_equal(r.extra["cand"].cpu().numpy()[:n_cand], ref["cand"].astype(np.int32))
+    assert np.array_equal(r.extra["pos"].cpu().numpy(), ref["pos"].astype(np.int32))
+    g = dict(lse=r.fwd.lse.cpu().numpy(), loss=r.fwd.loss.cpu().numpy(),
+             loss_sum=float(r.fwd.loss_sum.item()), n_valid=int(r.fwd.n_valid.item()),
+             n_bad=int(r.fwd.n_bad.item()), dh=r.dh.cpu().numpy(), dW=r.dW.cpu().numpy())
+    assert g["n_bad"] == 0
+    check_ce(g, ref, "bf16", inp.V_real)
+    # sizing by P instead would drop the targets ranked past P: refused as bad targets
+    with pytest.raises(V.BadTargetError):
+        V.sampled_step(h, W, tg, perm, inp.P, n_cand=inp.P)
+
+
+def test_bad_target_policy(V):
+    """A target outside [0, V_real) other than ignore_index: the library
+    counts it and treats it as ignored; the binding raises unless the caller
+    allows it."""
+    say("case bad-target policy")
+    dev = "cuda"
+    inp = make_ce_inputs(64, 64, 1000, 1024, 4, "f32", seed=3)
+    inp.targets[7] = 1010      # a padded class
+    inp.targets[9] = -7        # negative, not ignore_index
+    h = V.from_bits(inp.h, "f32", dev)
+    W = V.from_bits(inp.W, "f32", dev)
+    tg = torch.from_numpy(inp.targets).to(dev)
+    with pytest.raises(V.BadTargetError) as e:
+        V.ce_step(h, W, tg, inp.V_real, inp.num_shards, inp.ignore_index)
+    assert e.value.n_bad == 2
+    r = V.ce_step(h, W, tg, inp.V_real, inp.num_shards, inp.ignore_index, allow_bad=True)
+    torch.cuda.synchronize()
+    ref = oracle_ce(inp)
+    assert int(r.fwd.n_bad.item()) == 2 and ref["n_bad"] == 2
+    g = dict(lse=r.fwd.lse.cpu().numpy(), loss=r.fwd.loss.cpu().numpy(),
+             loss_sum=float(r.fwd.loss_sum.item()), n_valid=int(r.fwd.n_valid.item()),
+             n_bad=int(r.fwd.n_bad.item()), dh=r.dh.cpu().numpy(), dW=r.dW.cpu().numpy())
+    check_ce(g, ref, "f32", inp.V_real)
 
 
 @pytest.mark.parametrize("P,H,Vt,acc", [(0, 64, 50, 0), (1, 8, 3, 1), (777, 264, 5000, 0),

@@ -398,6 +398,39 @@ def test_tied_step_finite_difference():
     assert list(r["count"]) == [0, 0, 2, 0, 0, 1, 0, 0]
 
 
+# ---------------------------------------------------------------- parallel schedule
+
+def test_parallel_schedule_matches_sequential():
+    """oracle.parallel evaluates the same definitions over token and
+    vocabulary chunks on many threads; it must agree with the sequential,
+    pinned oracle to float64 rounding (chunks deliberately ragged)."""
+    inp = config_inputs("c1")
+    h = oracle.decode(inp.h, inp.dtype)
+    W = oracle.decode(inp.W, inp.dtype)
+    y = inp.targets.copy()
+    y[3] = inp.V_real + 5      # a bad target (padded class)
+    y[7] = 5000                # a bad target (past the table)
+    for red, gl in ((MEAN, 1.0), (SUM, 0.5)):
+        ref = oracle.cross_entropy(h, W, y, inp.V_real, inp.V_pad, inp.num_shards,
+                                   inp.ignore_index, gl, red)
+        got = oracle.parallel.cross_entropy(h, W, y, inp.V_real, inp.V_pad, inp.num_shards,
+                                            inp.ignore_index, gl, red, workers=4,
+                                            tok_chunk=7, voc_chunk=97)
+        assert got["n_valid"] == ref["n_valid"] and got["n_bad"] == ref["n_bad"]
+        for k in ("lse", "loss", "zt", "dh", "dW"):
+            np.testing.assert_allclose(got[k], ref[k], rtol=1e-12, atol=1e-15, err_msg=k)
+        assert abs(got["loss_sum"] - ref["loss_sum"]) <= 1e-12 * abs(ref["loss_sum"])
+        assert not got["dW"][inp.V_real:].any()
+    ids = inp.ids.copy()
+    ids[:4] = [-1, inp.V_real, inp.V_pad - 1, 7]
+    ref = oracle.tied_step(ids, y, W, inp.V_real, inp.V_pad, inp.num_shards)
+    got = oracle.parallel.tied_step(ids, y, W, inp.V_real, inp.V_pad, inp.num_shards,
+                                    workers=3)
+    for k in ("lse", "loss", "dh", "dW", "dW_emb"):
+        np.testing.assert_allclose(got[k], ref[k], rtol=1e-12, atol=1e-15, err_msg=k)
+    assert np.array_equal(got["count"], ref["count"])
+
+
 # ---------------------------------------------------------------- sampled softmax
 
 def test_candidates_bruteforce():

@@ -72,6 +72,18 @@ class VceError(RuntimeError):
         super().__init__(f"{fn} returned {STATUS.get(status, status)}: {strerror(status)}")
 
 
+class BadTargetError(ValueError):
+    """Targets outside [0, V_real) other than ignore_index reached the loss.
+    The library treats them as ignored and counts them (n_bad_target); the
+    binding refuses them unless the caller passes allow_bad=True, as
+    PyTorch's cross-entropy refuses an out-of-range class."""
+
+    def __init__(self, n_bad: int):
+        self.n_bad = n_bad
+        super().__init__(f"{n_bad} target(s) outside [0, V_real) that are not ignore_index "
+                         f"(pass allow_bad=True to treat them as ignored)")
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
@@ -141,6 +153,14 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
+def read_scalar(t: torch.Tensor, stream=None) -> int:
+    """A one-element device tensor's value on the host, after the work queued
+    on `stream` (default: the current stream) has finished. Synchronises."""
+    s = torch.cuda.current_stream(t.device) if stream is None else stream
+    s.synchronize()
+    return int(t.cpu().item())
+
+
 # ------------------------------------------------------------------ sizes
 
 def vce_fwd_workspace_bytes(T, H, V_real, V_pad, num_shards, dtype=VCE_BF16,
@@ -184,10 +204,17 @@ FwdOut = namedtuple("FwdOut", "lse loss loss_sum n_valid n_bad shard_stats")
 def vce_fwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, V_real: int,
             num_shards: int, ignore_index: int = -100, *, shard_stats: bool = False,
             shard_rows=None, out: Optional[FwdOut] = None, ws: Optional[torch.Tensor] = None,
-            stream=None) -> FwdOut:
+            allow_bad: bool = False, stream=None) -> FwdOut:
     """Cross-entropy forward. h [T,H], W [V_pad,H] (same dtype), targets [T] int32.
     shard_rows (optional): num_shards + 1 row offsets of an explicit layout
-    (calls vce_fwd_ex)."""
+    (calls vce_fwd_ex).
+
+    Bad targets (outside [0, V_real), not ignore_index): the library counts
+    them in n_bad and treats them as ignored. With allow_bad=False (default)
+    this call then waits for the forward (a stream synchronisation) and raises
+    BadTargetError if any was counted; allow_bad=True skips that check (no
+    synchronisation: use it under graph capture or where the caller reads
+    n_bad itself)."""
     T, H = h.shape
     V_pad = W.shape[0]
     dt = _dt(h)
@@ -214,6 +241,10 @@ def vce_fwd(h: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, V_real: int
         st = lib.vce_fwd_ex(_ptr(h), _ptr(W), _ptr(targets), T, H, V_real, V_pad, num_shards,
                             rows, ignore_index, dt, *outs)
         _check("vce_fwd_ex", st)
+    if not allow_bad:
+        nb = read_scalar(out.n_bad, stream)
+        if nb:
+            raise BadTargetError(nb)
     return out
 
 

@@ -326,6 +326,8 @@ vce_status vss_candidates(const int32_t* targets, int64_t T, int64_t V, int32_t 
                           int32_t* pos, int32_t* n_unique, int32_t* n_cand, void* ws,
                           size_t ws_bytes, void* stream) {
   if (T < 0 || V < 1 || P < 1 || T > kMaxDim || V > kMaxDim || P > kMaxDim) return VCE_ERR_SHAPE;
+  // more candidates than table rows cannot all be distinct rows
+  if (P > V) return VCE_ERR_SHAPE;
   if (check_ignore(ignore_index, V) != VCE_OK) return VCE_ERR_SHAPE;
   const int64_t need_cap = P > (T < V ? T : V) ? P : (T < V ? T : V);
   if (cand_cap < need_cap) return VCE_ERR_SHAPE;

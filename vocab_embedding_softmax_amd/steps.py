@@ -50,12 +50,12 @@ class Workspaces:
 
 def ce_step(h, W, targets, V_real, num_shards, ignore_index=-100, *, grad_loss=None,
             reduction=L.REDUCE_MEAN, ws: Optional[Workspaces] = None, dh=None, dW=None,
-            shard_stats=False, stream=None) -> StepOut:
+            shard_stats=False, allow_bad=False, stream=None) -> StepOut:
     dev = h.device
     if grad_loss is None:
         grad_loss = torch.ones(1, dtype=torch.float32, device=dev)
     f = L.vce_fwd(h, W, targets, V_real, num_shards, ignore_index, shard_stats=shard_stats,
-                  ws=None if ws is None else ws["fwd"], stream=stream)
+                  ws=None if ws is None else ws["fwd"], allow_bad=allow_bad, stream=stream)
     b = L.vce_bwd(h, W, targets, f.lse, grad_loss, f.n_valid, V_real, num_shards, ignore_index,
                   reduction, dh=dh, dW=dW, ws=None if ws is None else ws["bwd"], stream=stream)
     return StepOut(f, b.dh, b.dW, None)
@@ -63,13 +63,13 @@ def ce_step(h, W, targets, V_real, num_shards, ignore_index=-100, *, grad_loss=N
 
 def tied_step(ids, targets, W, V_real, num_shards, ignore_index=-100, *, grad_loss=None,
               reduction=L.REDUCE_MEAN, ws: Optional[Workspaces] = None, h=None, dh=None,
-              dW=None, stream=None) -> StepOut:
+              dW=None, allow_bad=False, stream=None) -> StepOut:
     dev = W.device
     if grad_loss is None:
         grad_loss = torch.ones(1, dtype=torch.float32, device=dev)
     h, n_bad_id = L.vemb_fwd(ids, W, V_real, num_shards, out=h, stream=stream)
     f = L.vce_fwd(h, W, targets, V_real, num_shards, ignore_index,
-                  ws=None if ws is None else ws["fwd"], stream=stream)
+                  ws=None if ws is None else ws["fwd"], allow_bad=allow_bad, stream=stream)
     b = L.vce_bwd(h, W, targets, f.lse, grad_loss, f.n_valid, V_real, num_shards, ignore_index,
                   reduction, dh=dh, dW=dW, accumulate_dW=False,
                   ws=None if ws is None else ws["bwd"], stream=stream)
@@ -80,21 +80,35 @@ def tied_step(ids, targets, W, V_real, num_shards, ignore_index=-100, *, grad_lo
 
 def sampled_step(h, W, targets, perm, P, ignore_index=-100, *, grad_loss=None,
                  reduction=L.REDUCE_MEAN, ws: Optional[Workspaces] = None, dW=None,
-                 stream=None) -> StepOut:
-    """Assumes the batch has at most P distinct targets (then n_cand == P); the
-    caller can check extra['n_cand'] afterwards."""
+                 n_cand: Optional[int] = None, allow_bad=False, stream=None) -> StepOut:
+    """The composite is sized by the number of candidates, n_cand = max(P, |U|)
+    (U = the batch's distinct valid targets): with more distinct targets than
+    P the candidates are U alone and every one of them takes part.
+
+    n_cand=None (default) reads that count from the device after the
+    candidate kernel (a stream synchronisation). A caller that must not
+    synchronise (graph capture) passes n_cand itself; it must equal the
+    device's count (P whenever |U| <= P). A smaller value would leave the
+    targets ranked past it out of the candidates: they are then counted as
+    bad targets (fwd.n_bad), which raises unless allow_bad=True. The
+    workspaces in `ws` are sized for P candidates and are replaced by larger
+    ones when n_cand exceeds P."""
     dev = h.device
     V, H = W.shape
     if grad_loss is None:
         grad_loss = torch.ones(1, dtype=torch.float32, device=dev)
     c = L.vss_candidates(targets, V, perm, P, ignore_index,
                          ws=None if ws is None else ws["cand"], stream=stream)
-    cand = c.cand[:P]
+    Pe = L.read_scalar(c.n_cand, stream) if n_cand is None else int(n_cand)
+    if Pe < 1 or Pe > c.cand.shape[0]:
+        raise ValueError(f"n_cand = {Pe} outside [1, {c.cand.shape[0]}]")
+    fit = ws is not None and Pe <= P
+    cand = c.cand[:Pe]
     Wc, _ = L.vemb_fwd(cand, W, V, 1, count_bad=False, stream=stream)
-    f = L.vce_fwd(h, Wc, c.pos, P, 1, ignore_index, ws=None if ws is None else ws["fwd"],
-                  stream=stream)
-    b = L.vce_bwd(h, Wc, c.pos, f.lse, grad_loss, f.n_valid, P, 1, ignore_index, reduction,
-                  ws=None if ws is None else ws["bwd"], stream=stream)
+    f = L.vce_fwd(h, Wc, c.pos, Pe, 1, ignore_index, ws=ws["fwd"] if fit else None,
+                  allow_bad=allow_bad, stream=stream)
+    b = L.vce_bwd(h, Wc, c.pos, f.lse, grad_loss, f.n_valid, Pe, 1, ignore_index, reduction,
+                  ws=ws["bwd"] if fit else None, stream=stream)
     dW = L.vss_scatter(cand, b.dW, V, dW=dW, accumulate=False, stream=stream)
     return StepOut(f, b.dh, dW, dict(cand=c.cand, pos=c.pos, n_unique=c.n_unique,
                                      n_cand=c.n_cand, Wc=Wc, dWc=b.dW))
@@ -102,7 +116,7 @@ def sampled_step(h, W, targets, perm, P, ignore_index=-100, *, grad_loss=None,
 
 def ot_h_step(ids, targets1, targets2, W, W2, V_real, num_shards, ignore_index=-100, *,
               weight=0.1, ws: Optional[Workspaces] = None, ws2: Optional[Workspaces] = None,
-              h=None, dh=None, dW=None, dW2=None, stream=None) -> StepOut:
+              h=None, dh=None, dW=None, dW2=None, allow_bad=False, stream=None) -> StepOut:
     """ids, targets1 [T]; targets2 [T - 1] (the tokens two positions ahead of
     rows 0..T-2); W the tied table, W2 the second head's table (same shape).
     ws2 sizes the second head's calls (T - 1 rows)."""
@@ -112,10 +126,10 @@ def ot_h_step(ids, targets1, targets2, W, W2, V_real, num_shards, ignore_index=-
     wgt = torch.full((1,), float(weight), dtype=torch.float32, device=dev)
     h, n_bad_id = L.vemb_fwd(ids, W, V_real, num_shards, out=h, stream=stream)
     f1 = L.vce_fwd(h, W, targets1, V_real, num_shards, ignore_index,
-                   ws=None if ws is None else ws["fwd"], stream=stream)
+                   ws=None if ws is None else ws["fwd"], allow_bad=allow_bad, stream=stream)
     h2 = h[:T - 1]
     f2 = L.vce_fwd(h2, W2, targets2, V_real, num_shards, ignore_index,
-                   ws=None if ws2 is None else ws2["fwd"], stream=stream)
+                   ws=None if ws2 is None else ws2["fwd"], allow_bad=allow_bad, stream=stream)
     b1 = L.vce_bwd(h, W, targets1, f1.lse, one, f1.n_valid, V_real, num_shards, ignore_index,
                    L.REDUCE_MEAN, dh=dh, dW=dW, ws=None if ws is None else ws["bwd"],
                    stream=stream)
