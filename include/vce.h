@@ -265,6 +265,27 @@ vce_status vngram_fwd(const int32_t* ids, const void* E, const void* E2, const v
                       int32_t* ids2, int32_t* ids3, int32_t* n_bad_id, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * Greedy argmax without a workspace, for callers that cannot allocate        *
+ * device memory (code under HIP graph capture, tight serving loops).         *
+ *                                                                           *
+ * The same call as vce_argmax (same kernels, arguments, results and errors) *
+ * except that the per-tile reports live in a static device buffer of the    *
+ * library, 16 MiB (VCE_NOALLOC_SCRATCH_BYTES) on each GPU it runs on, held  *
+ * until the process ends. Its address is looked up once per device on the  *
+ * first call with that device current. Allocates nothing.                   *
+ * Errors: as vce_argmax; VCE_ERR_WORKSPACE when vce_argmax_workspace_bytes  *
+ * for the same arguments exceeds VCE_NOALLOC_SCRATCH_BYTES (at V_pad =      *
+ * 201088 over 8 shards: T above 2647). The buffer is shared by every call    *
+ * on one GPU: calls that overlap on one GPU (other streams, other host      *
+ * threads) race on it; calls in one stream are ordered and safe.            *
+ * ------------------------------------------------------------------------ */
+#define VCE_NOALLOC_SCRATCH_BYTES (16u << 20)
+vce_status vce_argmax_noalloc(const void* h, const void* W, int64_t T, int64_t H,
+                              int64_t V_real, int64_t V_pad, int32_t num_shards, vce_dtype dt,
+                              int32_t* index, float* value, float* shard_value,
+                              int32_t* shard_index, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Explicit (uneven) shard layouts and mapped class ownership.               *
  *                                                                           *
  * [VS] paragraph 1 describes the equal split; [SP] paragraph 5 notes that   *

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in vce.SIGNATURES, n
@@ -264,3 +264,19 @@ def test_bwd_accumulate_flags_checked():
     assert call(4) == DTYPE and call(-1) == DTYPE
     for acc in (0, 1, 2, 3):
         assert call(acc) == WORKSPACE
+
+
+def test_argmax_noalloc_argument_errors():
+    """Checked before any HIP call: bad arguments as for vce_argmax, and a
+    call whose per-tile reports would not fit the static scratch."""
+    call = lambda T=4, H=64, Vr=1000, Vp=1024, n=4, dt=1, h=A, W=B, idx=C, val=A: \
+        lib.vce_argmax_noalloc(h, W, T, H, Vr, Vp, n, dt, idx, val, NUL, NUL, None)
+    assert call(dt=7) == DTYPE
+    assert call(Vr=0) == SHAPE
+    assert call(n=3) == SHARD
+    assert call(h=NUL) == NULL
+    assert call(H=60) == ALIGN
+    need = lib.vce_argmax_workspace_bytes(2648, 3072, 201088, 201088, 8, 1)
+    assert need > 16 << 20 >= lib.vce_argmax_workspace_bytes(2647, 3072, 201088, 201088, 8, 1)
+    assert call(T=2648, H=3072, Vr=201088, Vp=201088, n=8) == WORKSPACE
+    assert call(T=0) == OK

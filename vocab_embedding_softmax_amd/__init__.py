@@ -8,7 +8,7 @@ Importing it raises ImportError when the library has not been built.
 from ._lib import (  # noqa: F401
     ACC_DH, ACC_DW, LIB_PATH, REDUCE_MEAN, REDUCE_SUM, VCE_BF16, VCE_F32, BadTargetError, VceError,
     lib, read_scalar, strerror,
-    vce_argmax, vce_argmax_workspace_bytes, vce_bwd, vce_bwd_workspace_bytes, vce_fwd,
+    vce_argmax, vce_argmax_noalloc, vce_argmax_workspace_bytes, vce_bwd, vce_bwd_workspace_bytes, vce_fwd,
     vce_fwd_workspace_bytes, vce_remap, vemb_bwd,
     vemb_bwd_workspace_bytes, vemb_fwd, vngram_fwd, vss_candidates, vss_candidates_workspace_bytes,
     vss_scatter,

@@ -50,6 +50,8 @@ SIGNATURES = {
     "vce_argmax_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32, _I32]),
     "vce_argmax": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _SZ,
                           _P]),
+    "vce_argmax_noalloc": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _P, _P, _P, _P,
+                                  _P]),
     "vngram_fwd": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I32, _I32, _P, _P,
                           _P, _P, _P]),
     "vce_fwd_workspace_bytes_ex": (_SZ, [_I64, _I64, _I64, _I64, _I32, _P, _I32]),
@@ -333,6 +335,30 @@ def vce_argmax(h: torch.Tensor, W: torch.Tensor, V_real: int, num_shards: int, *
         st = lib.vce_argmax_ex(_ptr(h), _ptr(W), T, H, V_real, V_pad, num_shards, rows, dt,
                                *outs)
         _check("vce_argmax_ex", st)
+    return out
+
+
+def vce_argmax_noalloc(h: torch.Tensor, W: torch.Tensor, V_real: int, num_shards: int, *,
+                       shard_reports: bool = False, out: Optional[ArgOut] = None,
+                       stream=None) -> ArgOut:
+    """vce_argmax with the library's static scratch instead of a workspace
+    (nothing is allocated when `out` is given)."""
+    T, H = h.shape
+    V_pad = W.shape[0]
+    dt = _dt(h)
+    _need(h, "h")
+    _need(W, "W", h.dtype, (V_pad, H))
+    dev = h.device
+    if out is None:
+        f = dict(dtype=torch.float32, device=dev)
+        i = dict(dtype=torch.int32, device=dev)
+        out = ArgOut(torch.empty(T, **i), torch.empty(T, **f),
+                     torch.empty(num_shards, T, **f) if shard_reports else None,
+                     torch.empty(num_shards, T, **i) if shard_reports else None)
+    st = lib.vce_argmax_noalloc(_ptr(h), _ptr(W), T, H, V_real, V_pad, num_shards, dt,
+                                _ptr(out.index), _ptr(out.value), _ptr(out.shard_value),
+                                _ptr(out.shard_index), _stream(stream, dev))
+    _check("vce_argmax_noalloc", st)
     return out
 
 

@@ -199,11 +199,13 @@ vce_status vce_bwd_timed(const void* h, const void* W, const int32_t* targets, c
                                     p, static_cast<hipStream_t>(stream), events));
 }
 
-static vce_status argmax_impl(const void* h, const void* W, int64_t T, int64_t H,
-                              int64_t V_real, int64_t V_pad, int32_t num_shards,
-                              const int64_t* shard_rows, vce_dtype dt, int32_t* index,
-                              float* value, float* shard_value, int32_t* shard_index, void* ws,
-                              size_t ws_bytes, void* stream) {
+// Argument checks of the argmax entry points; on success `need` is the
+// workspace the call takes.
+static vce_status argmax_check(const void* h, const void* W, int64_t T, int64_t H,
+                               int64_t V_real, int64_t V_pad, int32_t num_shards,
+                               const int64_t* shard_rows, vce_dtype dt, const int32_t* index,
+                               const float* value, const float* shard_value,
+                               const int32_t* shard_index, size_t* need) {
   if (!dtype_ok(dt)) return VCE_ERR_DTYPE;
   vce_status st = shard_rows ? check_layout(T, H, V_real, V_pad, num_shards, shard_rows)
                              : check_table(T, H, V_real, V_pad, num_shards);
@@ -214,9 +216,20 @@ static vce_status argmax_impl(const void* h, const void* W, int64_t T, int64_t H
                 (shard_value && !aligned4(shard_value)) ||
                 (shard_index && !aligned4(shard_index))))
     return VCE_ERR_ALIGN;
-  const vce::ArgPlan probe =
-      vce::plan_argmax(T, H, V_real, V_pad, num_shards, shard_rows, nullptr);
-  if (T > 0 && (!ws || ws_bytes < probe.bytes)) return VCE_ERR_WORKSPACE;
+  *need = vce::plan_argmax(T, H, V_real, V_pad, num_shards, shard_rows, nullptr).bytes;
+  return VCE_OK;
+}
+
+static vce_status argmax_impl(const void* h, const void* W, int64_t T, int64_t H,
+                              int64_t V_real, int64_t V_pad, int32_t num_shards,
+                              const int64_t* shard_rows, vce_dtype dt, int32_t* index,
+                              float* value, float* shard_value, int32_t* shard_index, void* ws,
+                              size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  const vce_status st = argmax_check(h, W, T, H, V_real, V_pad, num_shards, shard_rows, dt,
+                                     index, value, shard_value, shard_index, &need);
+  if (st != VCE_OK) return st;
+  if (T > 0 && (!ws || ws_bytes < need)) return VCE_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return VCE_ERR_ALIGN;
   const vce::ArgPlan p = vce::plan_argmax(T, H, V_real, V_pad, num_shards, shard_rows, ws);
   return hip_status(vce::run_argmax(h, W, T, H, V_real, V_pad, dt == VCE_BF16, index,
@@ -230,6 +243,22 @@ vce_status vce_argmax(const void* h, const void* W, int64_t T, int64_t H, int64_
                       size_t ws_bytes, void* stream) {
   return argmax_impl(h, W, T, H, V_real, V_pad, num_shards, nullptr, dt, index, value,
                      shard_value, shard_index, ws, ws_bytes, stream);
+}
+
+vce_status vce_argmax_noalloc(const void* h, const void* W, int64_t T, int64_t H,
+                              int64_t V_real, int64_t V_pad, int32_t num_shards, vce_dtype dt,
+                              int32_t* index, float* value, float* shard_value,
+                              int32_t* shard_index, void* stream) {
+  size_t need = 0;
+  const vce_status st = argmax_check(h, W, T, H, V_real, V_pad, num_shards, nullptr, dt, index,
+                                     value, shard_value, shard_index, &need);
+  if (st != VCE_OK) return st;
+  if (need > vce::kNoAllocScratchBytes) return VCE_ERR_WORKSPACE;
+  if (T == 0) return VCE_OK;
+  void* ws = nullptr;
+  if (vce::noalloc_scratch(&ws) != hipSuccess) return VCE_ERR_HIP;
+  return argmax_impl(h, W, T, H, V_real, V_pad, num_shards, nullptr, dt, index, value,
+                     shard_value, shard_index, ws, vce::kNoAllocScratchBytes, stream);
 }
 
 vce_status vce_argmax_ex(const void* h, const void* W, int64_t T, int64_t H, int64_t V_real,

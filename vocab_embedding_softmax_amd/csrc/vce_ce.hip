@@ -16,10 +16,41 @@
 //   partial a vocabulary rank would contribute to the all-reduce) and
 //   dW_chunk = G^T h, both MFMA GEMMs that read G, W and h in place (the
 //   K-major operands through transposing LDS reads).
+#include <mutex>
+
 #include "gemm_tn.hpp"
 #include "vce_internal.hpp"
 
 namespace vce {
+
+// ------------------------------------------------------------ static scratch
+
+// Device memory of the allocation-free argmax (the per-tile reports that
+// vce_argmax keeps in the caller's workspace). Each GPU the library runs on
+// holds its own copy until the process ends. In host code `scratch` is only a
+// host-side stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with `dev` current
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 // ------------------------------------------------------------------ planning
 

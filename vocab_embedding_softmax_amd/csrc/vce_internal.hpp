@@ -253,6 +253,11 @@ hipError_t run_candidates(const int32_t* targets, int64_t T, int64_t V, const in
 
 hipError_t run_fill_scalars(float* f0, int32_t* i0, int32_t* i1, hipStream_t s);
 
+// Static device scratch of the allocation-free argmax: size, and its device
+// address on the current device (looked up once per device, then cached).
+constexpr size_t kNoAllocScratchBytes = size_t{16} << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Exclusive scan of n int32 values: y[i] = sum x[0..i), y[n] = total.
 // tmp holds scan_blocks(n) + 1 ints.
 int64_t scan_blocks(int64_t n);
