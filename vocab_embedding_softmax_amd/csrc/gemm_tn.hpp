@@ -45,6 +45,11 @@
 
 #include "vce_device.hpp"
 
+// A second copy of the K loop for whole tiles, free of per-load tests
+#ifndef VCE_KLOOP_SPLIT
+#define VCE_KLOOP_SPLIT 1
+#endif
+
 namespace vce {
 
 enum EpiMode { EPI_FWD = 0, EPI_GRAD = 1, EPI_STORE = 2, EPI_ARGMAX = 3 };
@@ -630,10 +635,14 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
     //   WAIT_ALL: wait for every load (near the end, fewer slices are younger)
     //   ISSUE:    queue slice kt + NS
     //   LAST:     the tile's last slice (no barrier, nothing more to read)
-    auto kstep = [&](int kt, auto wait_all, auto issue_next, auto last) {
+    //   AF:       every slice of the tile is whole (all positions valid, K a
+    //             multiple of the slice): the loads take the fast form with
+    //             no run-time test
+    auto kstep = [&](int kt, auto wait_all, auto issue_next, auto last, auto all_fast) {
       constexpr bool WAIT_ALL = decltype(wait_all)::value;
       constexpr bool ISSUE = decltype(issue_next)::value;
       constexpr bool LAST = decltype(last)::value;
+      constexpr bool AF = decltype(all_fast)::value;
       const char* st = smem + (kt % NS) * STAGE;
       if constexpr (SPREAD && ISSUE) {
         // slice kt+NS-1 goes into the stage slice kt-1 used (free since the
@@ -645,7 +654,7 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
         const int64_t kleft = klen - kofs;
         const char* pa = Ab + kofs * (AKM ? g.lda : 1) * ES;
         const char* pb = Bb + kofs * (BKM ? g.ldb : 1) * ES;
-        const bool fast_a = sa.fast(kleft), fast_b = sb.fast(kleft);
+        const bool fast_a = AF || sa.fast(kleft), fast_b = AF || sb.fast(kleft);
         constexpr int NT = MI * NI;
         constexpr int SLOTS = (SS - 1) * NT;  // MFMAs before the barrier
         static_for<0, SS - 1>([&](auto ss) {
@@ -655,6 +664,7 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
             constexpr int k = decltype(kk)::value;
             constexpr int slot = sub * NT + k;
             // loads l with l * SLOTS / LOADS == slot go right before this MFMA
+            bool loaded = false;
             static_for<0, LOADS>([&](auto ll) {
               constexpr int l = decltype(ll)::value;
               if constexpr ((l * SLOTS) / LOADS == slot) {
@@ -662,9 +672,12 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
                   sa.issue_q(l, stl, pa, kleft, wave, fast_a);
                 else
                   sb.issue_q(l - SA::Q, stl + A_BYTES, pb, kleft, wave, fast_b);
+                loaded = true;
               }
             });
             mma_chunk<E>(acc[k / NI][k % NI], fa[sub & 1][k / NI], fb[sub & 1][k % NI]);
+            // as below: keep the loads where they were placed
+            if (AF && loaded) __builtin_amdgcn_sched_barrier(0);
           });
         });
       } else {
@@ -699,8 +712,8 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
           kleft = klen - kofs;
           pa = Ab + kofs * (AKM ? g.lda : 1) * ES;
           pb = Bb + kofs * (BKM ? g.ldb : 1) * ES;
-          fast_a = sa.fast(kleft);
-          fast_b = sb.fast(kleft);
+          fast_a = AF || sa.fast(kleft);
+          fast_b = AF || sb.fast(kleft);
         }
         constexpr int NT = MI * NI;
         static_for<0, (NT > LOADS ? NT : LOADS)>([&](auto kk) {
@@ -716,6 +729,9 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
             fa[0][k] = sa.frag(stn, k, 0, lane);
           else if constexpr (k < MI + NI)
             fb[0][k - MI] = sb.frag(stn + A_BYTES, k - MI, 0, lane);
+          // keep one load per MFMA: without run-time tests around the loads
+          // the scheduler would otherwise hoist them all ahead of the MFMAs
+          if constexpr (AF && ISSUE) __builtin_amdgcn_sched_barrier(0);
         });
         if constexpr (NT < MI + NI) {
 #pragma unroll
@@ -743,25 +759,34 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       load_epi();
       asm volatile("" ::"r"(smem) : "memory");
       read_frags(smem, 0, fa[0], fb[0]);
-      int kt = 0;
-      if constexpr (SPREAD) {
-        // kstep(kt) queues slice kt+NS-1; at its barrier the slices after
-        // kt+1 that are in flight are kt+2 .. kt+NS-1
-        for (; kt + NS - 1 < nk; ++kt)
-          kstep(kt, std::false_type{}, std::true_type{}, std::false_type{});
-        for (; kt + 1 < nk; ++kt)
-          kstep(kt, std::true_type{}, std::false_type{}, std::false_type{});
-      } else {
-        for (; kt + NS < nk; ++kt)
-          kstep(kt, std::false_type{}, std::true_type{}, std::false_type{});
-        if (kt + NS == nk && kt + 1 < nk) {
-          kstep(kt, std::false_type{}, std::false_type{}, std::false_type{});
-          ++kt;
+      using F_ = std::false_type;
+      using T_ = std::true_type;
+      auto kloop = [&](auto af) {
+        int kt = 0;
+        if constexpr (SPREAD) {
+          // kstep(kt) queues slice kt+NS-1; at its barrier the slices after
+          // kt+1 that are in flight are kt+2 .. kt+NS-1
+          for (; kt + NS - 1 < nk; ++kt) kstep(kt, F_{}, T_{}, F_{}, af);
+          for (; kt + 1 < nk; ++kt) kstep(kt, T_{}, F_{}, F_{}, af);
+        } else {
+          for (; kt + NS < nk; ++kt) kstep(kt, F_{}, T_{}, F_{}, af);
+          if (kt + NS == nk && kt + 1 < nk) {
+            kstep(kt, F_{}, F_{}, F_{}, af);
+            ++kt;
+          }
+          for (; kt + 1 < nk; ++kt) kstep(kt, T_{}, F_{}, F_{}, af);
         }
-        for (; kt + 1 < nk; ++kt)
-          kstep(kt, std::true_type{}, std::false_type{}, std::false_type{});
-      }
-      kstep(kt, std::true_type{}, std::false_type{}, std::true_type{});
+        kstep(kt, T_{}, F_{}, T_{}, af);
+      };
+#if VCE_KLOOP_SPLIT
+      // whole tiles (the common case) run a K loop without per-load tests
+      if (sa.fast(klen) && sb.fast(klen) && klen % BK == 0)
+        kloop(std::true_type{});
+      else
+        kloop(std::false_type{});
+#else
+      kloop(std::false_type{});
+#endif
     } else {
       load_epi();
     }
