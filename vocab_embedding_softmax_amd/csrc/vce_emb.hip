@@ -13,12 +13,13 @@
 //      into runs of 1024 that workgroups radix-sort by ID in LDS, then each
 //      workgroup places its run by ranking its IDs in all runs (two launches);
 //      larger inputs use block-local LDS sorts, per-block ID counts and scans;
-//   2. the sorted list is cut into chunks of kSegC positions; each chunk sums
-//      the dout rows of its runs (tokens of one ID) in sorted order and writes
-//      the sum of every run that lies wholly inside it into its row of dW;
-//      a run cut by a chunk end leaves a partial sum instead;
-//   3. the chunk where such an ID's run ends adds the ID's partial sums in
-//      chunk order and writes the row.
+//   2. one launch sums the dout rows of each ID (a run of the sorted list)
+//      and writes its row of dW once: an ID with fewer than kSegLong tokens
+//      belongs to the chunk of kSegC sorted positions where its run starts,
+//      and that chunk's wave sums it in sorted (= token) order; an ID with
+//      more is split by columns over many workgroups, each of which sums its
+//      column slice over the whole run in a fixed order. No partial sums leave
+//      a workgroup.
 #include "vce_device.hpp"
 #include "vce_internal.hpp"
 
@@ -35,6 +36,10 @@ constexpr int kRunMaxRuns = 32;                            // runs the merge hol
 constexpr int kPlanDigit = 6;                              // ID bits per radix pass
 constexpr int kSortBlock = 1024;                           // tokens per local sort
 constexpr int kSortThreads = 512;
+constexpr int kSegLong = 32;     // tokens of an ID from which its sum is split by columns
+constexpr int kLongCols = 64;    // columns per long-ID item (16 lanes x 4)
+constexpr int kLongBatch = 16;   // dout rows in flight per lane of a long-ID item
+constexpr int kLongWGs = 512;    // workgroups that take the long-ID items
 
 // ------------------------------------------------------------------ planning
 
@@ -78,8 +83,13 @@ EmbBwdPlan plan_emb_bwd(int64_t T, int64_t H, int64_t V_real, void* ws) {
   p.sorted = c.take<int32_t>(static_cast<size_t>(Tp));
   p.skey = c.take<int32_t>(static_cast<size_t>(Tp));
   p.chunk_start = c.take<int32_t>(static_cast<size_t>(p.nchunks));
-  p.partial = c.take<float>(static_cast<size_t>(p.nchunks * 2 * H));
+  p.chunk_end = c.take<int32_t>(static_cast<size_t>(p.nchunks));
+  p.long_runs = c.take<int32_t>(static_cast<size_t>(p.nchunks * 2));
+  p.n_long = c.take<int32_t>(1);
   if (p.offs) p.n_sorted = p.offs + V_real;
+  // long IDs: at most Tp / kSegLong of them, each cut into cdiv(H, kLongCols) items
+  const int64_t long_items = (Tp / kSegLong) * cdiv(H, kLongCols);
+  p.long_wgs = long_items < kLongWGs ? long_items : kLongWGs;
   p.bytes = c.used;
   return p;
 }
@@ -477,10 +487,12 @@ __global__ __launch_bounds__(kSortThreads) void k_block_sort(const int32_t* __re
                                                              int64_t T, int64_t V_real,
                                                              uint64_t* __restrict__ lkey,
                                                              int32_t* __restrict__ lrank,
-                                                             int32_t* __restrict__ bcnt) {
+                                                             int32_t* __restrict__ bcnt,
+                                                             int32_t* __restrict__ n_long) {
   __shared__ uint64_t s[kSortBlock];
   const int64_t b = blockIdx.x;
   const int tid = threadIdx.x;
+  if (b == 0 && tid == 0) *n_long = 0;  // k_chunk_starts appends the long IDs
   constexpr uint64_t kNone = ~0ull;
 #pragma unroll
   for (int u = 0; u < kSortBlock / kSortThreads; ++u) {
@@ -596,6 +608,24 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d) {
   return eq;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele steps of
+// 1, 2, 4 and 8 lanes within each row of 16 lanes (DPP row shifts; lanes
+// shifted in from outside the row read 0), then the totals of the lower rows
+// (lanes 15, 31 and 47) are added.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  int v = static_cast<int>(x);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  v += (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+  return static_cast<uint32_t>(v);
+}
+
 // Sort of the tokens of one call by (ID, token), in two steps.
 // k_run_sort: workgroup r sorts the run of tokens [r*kRun, (r+1)*kRun) by ID,
 // stably (least-significant-digit radix passes of kPlanDigit ID bits; within
@@ -606,7 +636,8 @@ __global__ __launch_bounds__(kRun) void k_run_sort(const int32_t* __restrict__ i
                                                    int64_t V_real, int32_t vbits,
                                                    uint32_t* __restrict__ rid,
                                                    int32_t* __restrict__ rtok,
-                                                   int32_t* __restrict__ rvalid) {
+                                                   int32_t* __restrict__ rvalid,
+                                                   int32_t* __restrict__ n_long) {
   constexpr int NW = kRun / 64;
   constexpr int ND = 1 << kPlanDigit;
   static_assert(NW * ND == kRun, "one thread per (wave, digit) count");
@@ -624,6 +655,7 @@ __global__ __launch_bounds__(kRun) void k_run_sort(const int32_t* __restrict__ i
     if (v >= 0 && v < V_real) id = static_cast<uint32_t>(v);
   }
   if (tid == 0) s_n = 0;
+  if (blockIdx.x == 0 && tid == 0) *n_long = 0;  // the merge appends the long IDs
   kid[0][tid] = id;
   ktok[0][tid] = static_cast<int32_t>(t);
   __syncthreads();
@@ -646,16 +678,12 @@ __global__ __launch_bounds__(kRun) void k_run_sort(const int32_t* __restrict__ i
     // digit i / NW, wave i % NW
     const int di = tid / NW, wi = tid % NW;
     const uint32_t v = wrun[wi][di];
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(x, o);
-      if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_incl_scan(v);
     if (lane == 63) wtot[w] = x;
     __syncthreads();
-    uint32_t base = 0;
-    for (int k = 0; k < w; ++k) base += wtot[k];
+    uint32_t base = 0;  // all NW reads issued together (broadcasts)
+#pragma unroll
+    for (int k = 0; k < NW; ++k) base += k < w ? wtot[k] : 0u;
     wrun[wi][di] = base + x - v;  // every thread has read its count above
     __syncthreads();
     const uint32_t pos = wrun[w][d] + below;
@@ -670,48 +698,61 @@ __global__ __launch_bounds__(kRun) void k_run_sort(const int32_t* __restrict__ i
   if (tid == 0) rvalid[blockIdx.x] = s_n;
 }
 
-// Summed over runs k < U (those below nruns, other than skip): the number of
-// the kRun ascending IDs of run k that are below x, or at most x for runs
-// before le_before (x < 2^31, so "at most x" is "below x + 1"). The U binary
-// searches advance together with no branches (a run that does not count
-// searches the last run and adds nothing), so the U LDS reads of a step are
-// in flight at once.
+// Both bounds of x (< 2^31) in every run k < nruns: lt_k = #(IDs < x) and
+// le_k = #(IDs <= x) among the run's kRun ascending IDs. Returns
+//   off = sum_{k < r} le_k + sum_{k > r} lt_k,  lt = sum_k lt_k,  le = sum_k le_k.
+// The 2U binary searches advance together with no branches (a run at or past
+// nruns searches the last run and adds nothing), so the 2U LDS reads of a
+// step are in flight at once.
 template <int U>
-__device__ __forceinline__ int32_t run_ranks(const uint32_t* all, int nruns, int skip,
-                                             int le_before, uint32_t x) {
+__device__ __forceinline__ void run_bounds(const uint32_t* all, int nruns, int r, uint32_t x,
+                                           int32_t& off, int32_t& lt, int32_t& le) {
   const uint32_t* base[U];
-  uint32_t lim[U];
-  int32_t c[U];
+  int32_t a[U], b[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     base[u] = all + (u < nruns ? u : nruns - 1) * kRun;
-    lim[u] = x + (u < le_before ? 1u : 0u);
-    c[u] = 0;
+    a[u] = 0;
+    b[u] = 0;
   }
 #pragma unroll
   for (int step = kRun / 2; step > 0; step >>= 1) {
-    uint32_t y[U];
+    uint32_t ya[U], yb[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) y[u] = base[u][c[u] + step - 1];
+    for (int u = 0; u < U; ++u) {
+      ya[u] = base[u][a[u] + step - 1];
+      yb[u] = base[u][b[u] + step - 1];
+    }
 #pragma unroll
-    for (int u = 0; u < U; ++u) c[u] += y[u] < lim[u] ? step : 0;
+    for (int u = 0; u < U; ++u) {
+      a[u] += ya[u] < x ? step : 0;
+      b[u] += yb[u] <= x ? step : 0;
+    }
   }
-  int32_t sum = 0;
+  off = 0;
+  lt = 0;
+  le = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    // c <= kRun - 1 here: element c is the last one left to test
-    const int32_t r = c[u] + (base[u][c[u]] < lim[u] ? 1 : 0);
-    sum += (u < nruns && u != skip) ? r : 0;
+    // a, b <= kRun - 1 here: element a (b) is the last one left to test
+    const int32_t ra = a[u] + (base[u][a[u]] < x ? 1 : 0);
+    const int32_t rb = b[u] + (base[u][b[u]] <= x ? 1 : 0);
+    if (u < nruns) {
+      lt += ra;
+      le += rb;
+      off += u < r ? rb : (u > r ? ra : 0);
+    }
   }
-  return sum;
 }
 
 // k_run_merge: kMergeSplit workgroups per run place its tokens. With the
 // runs' IDs in LDS, a token at index i of run r with ID v goes to
 //   i + (tokens with ID <= v in runs before r) + (tokens with ID < v in runs after r),
 // which is its rank in (ID, token) order, since run r holds tokens
-// [r*kRun, (r+1)*kRun). A token that starts a chunk of kSegC sorted positions
-// also records where its ID's tokens start (tokens with ID < v in all runs).
+// [r*kRun, (r+1)*kRun). The same searches give where v's tokens start and
+// end in the sorted list: a token at a chunk's first position records them
+// for its chunk, and the first token of an ID with at least kSegLong tokens
+// appends the ID's (start, end) to the long list (in any order).
 constexpr int kMergeSplit = 4;
 constexpr int kMergeThreads = kRun / kMergeSplit;
 static_assert(kRunMaxRuns <= 64, "one wave sums the run counts");
@@ -719,7 +760,8 @@ __global__ __launch_bounds__(kMergeThreads) void k_run_merge(
     const uint32_t* __restrict__ rid, const int32_t* __restrict__ rtok,
     const int32_t* __restrict__ rvalid, int32_t nruns, int32_t* __restrict__ sorted,
     int32_t* __restrict__ skey, int32_t* __restrict__ n_sorted,
-    int32_t* __restrict__ chunk_start) {
+    int32_t* __restrict__ chunk_start, int32_t* __restrict__ chunk_end,
+    int32_t* __restrict__ long_runs, int32_t* __restrict__ n_long, int32_t long_cap) {
   __shared__ __attribute__((aligned(16))) uint32_t all[kRunMaxRuns * kRun];
   const int tid = threadIdx.x;
   const int r = blockIdx.x / kMergeSplit;
@@ -745,78 +787,189 @@ __global__ __launch_bounds__(kMergeThreads) void k_run_merge(
   __syncthreads();
   const uint32_t v = all[r * kRun + i];
   if (v == ~0u) return;
-  const bool small = nruns <= kRunMaxRuns / 2;  // uniform
-  const int32_t pos = i + (small ? run_ranks<kRunMaxRuns / 2>(all, nruns, r, r, v)
-                                 : run_ranks<kRunMaxRuns>(all, nruns, r, r, v));
+  int32_t off, lt, le;
+  if (nruns <= kRunMaxRuns / 2)  // uniform
+    run_bounds<kRunMaxRuns / 2>(all, nruns, r, v, off, lt, le);
+  else
+    run_bounds<kRunMaxRuns>(all, nruns, r, v, off, lt, le);
+  const int32_t pos = i + off;
   sorted[pos] = rtok[r * kRun + i];
   skey[pos] = static_cast<int32_t>(v);
-  if (pos % kSegC == 0)
-    chunk_start[pos / kSegC] = small ? run_ranks<kRunMaxRuns / 2>(all, nruns, -1, 0, v)
-                                     : run_ranks<kRunMaxRuns>(all, nruns, -1, 0, v);
+  if (pos % kSegC == 0) {
+    chunk_start[pos / kSegC] = lt;
+    chunk_end[pos / kSegC] = le;
+  }
+  if (pos == lt && le - lt >= kSegLong) {
+    const int32_t k = atomicAdd(n_long, 1);
+    if (k < long_cap) {  // at most (tokens / kSegLong) long IDs: always true
+      long_runs[2 * k] = lt;
+      long_runs[2 * k + 1] = le;
+    }
+  }
 }
 
-// General sort: the first sorted position of the ID at every chunk's start.
+// General sort: where the tokens of the ID at every chunk's first position
+// start and end in the sorted list; the chunk holding the first chunk start
+// inside a long ID's run appends the ID to the long list.
 __global__ __launch_bounds__(256) void k_chunk_starts(const int32_t* __restrict__ skey,
                                                       const int32_t* __restrict__ offs,
                                                       const int32_t* __restrict__ n_sorted,
                                                       int64_t nchunks,
-                                                      int32_t* __restrict__ chunk_start) {
+                                                      int32_t* __restrict__ chunk_start,
+                                                      int32_t* __restrict__ chunk_end,
+                                                      int32_t* __restrict__ long_runs,
+                                                      int32_t* __restrict__ n_long) {
   const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t n = *n_sorted;
   if (c >= nchunks || c * kSegC >= n) return;
-  chunk_start[c] = offs[skey[c * kSegC]];
+  const int64_t id = skey[c * kSegC];
+  const int32_t lt = offs[id], le = offs[id + 1];
+  chunk_start[c] = lt;
+  chunk_end[c] = le;
+  if (le - lt >= kSegLong && lt > c * kSegC - kSegC) {
+    const int32_t k = atomicAdd(n_long, 1);
+    if (k < nchunks) {  // at most (tokens / kSegLong) long IDs: always true
+      long_runs[2 * k] = lt;
+      long_runs[2 * k + 1] = le;
+    }
+  }
 }
 
 // ------------------------------------------------------------------ segment sums
 
-// One wave per (chunk of kSegC sorted positions, 256-column slice of dW).
-// The chunk's runs (positions with one ID) are summed in sorted (= token)
-// order. A run that lies wholly in the chunk is added into (or stored to)
-// its row of dW. A run cut by a chunk end is stored as a partial sum: slot 0
-// for the run that continues from the previous chunk, slot 1 for the run
-// that starts here and continues into the next one. Run boundaries depend
-// on the sorted IDs only, so every branch is uniform across the wave; the
-// dout rows of a batch and the dW rows its closed runs update are all in
-// flight before the first add.
+// Long IDs: item j = (long ID j / nls, column slice j % nls) of kLongCols
+// columns; the workgroups [0, long_wgs) take items wg, wg + long_wgs, ...
+// Sixteen row lanes (4 waves x 4 groups of 16 lanes, 4 columns per lane)
+// each sum every 16th token of the run in sorted order, kLongBatch rows in
+// flight, the next batch's token indices loading behind them; the row lanes'
+// sums are added in row-lane order through LDS and the slice of the ID's row
+// is written (added to when accumulating) once.
 template <typename D>
-__global__ __launch_bounds__(256) void k_seg_chunks(const int32_t* __restrict__ skey,
-                                                    const int32_t* __restrict__ sorted,
-                                                    const int32_t* __restrict__ n_sorted,
-                                                    const D* __restrict__ dout, int64_t H,
-                                                    int64_t nslices, float* __restrict__ dW,
-                                                    int32_t accumulate,
-                                                    float* __restrict__ partial) {
+__device__ __forceinline__ void seg_long(int64_t wg, int64_t nwg, const int32_t* skey,
+                                         const int32_t* sorted, const int32_t* long_runs,
+                                         int32_t n_long, int32_t N, const D* dout, int64_t H,
+                                         float* dW, int32_t accumulate, f32x4 (*red)[16]) {
   const int lane = threadIdx.x & 63;
-  const int64_t slice = static_cast<int64_t>(blockIdx.y) * 4 + (threadIdx.x >> 6);
-  const int64_t c = blockIdx.x;
+  const int rl = (threadIdx.x >> 6) * 4 + (lane >> 4);  // row lane 0..15
+  const int cl = lane & 15;                              // column lane
+  const int64_t nls = (H + kLongCols - 1) / kLongCols;
+  const int64_t items = static_cast<int64_t>(n_long) * nls;
+  constexpr int STEP = 16 * kLongBatch;  // positions per batch of the workgroup
+  for (int64_t j = wg; j < items; j += nwg) {
+    const int64_t k = j / nls;
+    // (first, end) lie in [0, N] with first < end; clamped all the same, so
+    // that no read can leave the sorted list
+    const int32_t end = min(long_runs[2 * k + 1], N);
+    const int32_t first = max(0, min(long_runs[2 * k], end - 1));
+    const int64_t col = (j % nls) * kLongCols + cl * 4;
+    const bool active = col < H;
+    const int64_t colc = active ? col : H - 4;  // a readable column; its sum is dropped
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    int32_t tok[kLongBatch];
+#pragma unroll
+    for (int u = 0; u < kLongBatch; ++u) tok[u] = sorted[min(first + u * 16 + rl, end - 1)];
+    for (int32_t b0 = first; b0 < end; b0 += STEP) {
+      f32x4 row[kLongBatch];
+#pragma unroll
+      for (int u = 0; u < kLongBatch; ++u)
+        row[u] = load_row4<D>(dout + static_cast<int64_t>(tok[u]) * H, colc);
+      if (b0 + STEP < end) {
+#pragma unroll
+        for (int u = 0; u < kLongBatch; ++u)
+          tok[u] = sorted[min(b0 + STEP + u * 16 + rl, end - 1)];
+      }
+#pragma unroll
+      for (int u = 0; u < kLongBatch; ++u)
+        if (b0 + u * 16 + rl < end) acc += row[u];
+    }
+    red[rl][cl] = acc;
+    __syncthreads();
+    if (threadIdx.x < 16 && active) {  // row group 0 of wave 0: cl == threadIdx.x
+      f32x4 tot = red[0][cl];
+#pragma unroll
+      for (int q = 1; q < 16; ++q) tot += red[q][cl];
+      f32x4* dst = reinterpret_cast<f32x4*>(dW + static_cast<int64_t>(skey[first]) * H + col);
+      *dst = accumulate ? *dst + tot : tot;
+    }
+    __syncthreads();  // red is reused by the next item
+  }
+}
+
+// The segment sums of every ID, one launch. Workgroups below long_wgs take
+// the long IDs (seg_long); each other workgroup is a chunk of kSegC sorted
+// positions and four 256-column slices of dW, one per wave. A chunk owns the
+// IDs with fewer than kSegLong tokens whose run starts inside it, whole: from
+// its first position (or the end of a run that came from before or is long)
+// to the end of the last such run, which may reach past the chunk. Its wave
+// sums each run in sorted (= token) order and writes (or adds into) the ID's
+// row; run boundaries depend on the sorted IDs only, so every branch is
+// uniform across the wave, and the dout rows of a batch and the dW rows its
+// runs update are all in flight before the first add.
+template <typename D>
+__global__ __launch_bounds__(256) void k_seg_sums(const int32_t* __restrict__ skey,
+                                                  const int32_t* __restrict__ sorted,
+                                                  const int32_t* __restrict__ n_sorted,
+                                                  const int32_t* __restrict__ chunk_start,
+                                                  const int32_t* __restrict__ chunk_end,
+                                                  const int32_t* __restrict__ long_runs,
+                                                  const int32_t* __restrict__ n_long,
+                                                  const D* __restrict__ dout, int64_t H,
+                                                  int64_t nslices, int64_t nchunks,
+                                                  int64_t long_wgs, float* __restrict__ dW,
+                                                  int32_t accumulate) {
+  __shared__ f32x4 red[16][16];
+  if (static_cast<int64_t>(blockIdx.x) < long_wgs) {
+    const int32_t nl = min(*n_long, static_cast<int32_t>(nchunks));
+    seg_long<D>(blockIdx.x, long_wgs, skey, sorted, long_runs, nl, *n_sorted, dout, H, dW,
+                accumulate, red);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int64_t ngroups = (nslices + 3) / 4;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) - long_wgs;
+  const int64_t c = item / ngroups;
+  const int64_t slice = (item % ngroups) * 4 + (threadIdx.x >> 6);
   const int64_t N = *n_sorted;
   const int64_t p0 = c * kSegC;
   if (slice >= nslices || p0 >= N) return;
-  const int64_t p1 = min(p0 + kSegC, N);
+  // [pb, pe): whole runs of short IDs that start in this chunk
+  const int32_t cs = chunk_start[c], ce = chunk_end[c];
+  const int64_t pb = (cs == p0 && ce - cs < kSegLong) ? p0 : ce;
+  int64_t pe;
+  const int64_t q = p0 + kSegC;
+  if (q >= N) {
+    pe = N;
+  } else {
+    const int32_t cs2 = chunk_start[c + 1], ce2 = chunk_end[c + 1];
+    if (cs2 == q)
+      pe = q;
+    else if (cs2 < p0)
+      pe = pb;  // one run covers the whole chunk: its owner is elsewhere
+    else
+      pe = (ce2 - cs2 < kSegLong) ? ce2 : cs2;
+  }
+  pe = min(pe, N);  // [pb, pe) lies in [0, N) already; kept so by the clamps
+  if (pe <= pb || pb < 0) return;
   const int64_t col = slice * kSegCols + lane * 4;
   const bool active = col < H;
-  const int32_t v_first = skey[p0];
-  const bool cont_before = p0 > 0 && skey[p0 - 1] == v_first;
-  const int32_t v_after = p1 < N ? skey[p1] : -1;
-  bool first_run = true;  // the run being summed is the chunk's first
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int64_t colc = active ? col : H - 4;  // a readable column; its results are dropped
-  for (int64_t b0 = p0; b0 < p1; b0 += kSegBatch) {
-    // every index is clamped into the chunk so that all loads of a batch are
-    // issued back to back; entries past the chunk are masked afterwards
-    // (loaded into vector registers: as scalars, the 33 values and 16 row
-    // addresses exhaust the scalar registers and the loads serialise)
+  for (int64_t b0 = pb; b0 < pe; b0 += kSegBatch) {
+    // every index is clamped into [pb, pe) so that all loads of a batch are
+    // issued back to back; entries past pe are masked afterwards (loaded into
+    // vector registers: as scalars, the 33 values and 16 row addresses
+    // exhaust the scalar registers and the loads serialise)
     int32_t key[kSegBatch + 1], tok[kSegBatch];
 #pragma unroll
     for (int i = 0; i <= kSegBatch; ++i) {
-      int32_t p = static_cast<int32_t>(min(b0 + i, p1 - 1));
+      int32_t p = static_cast<int32_t>(min(b0 + i, pe - 1));
       asm volatile("v_mov_b32 %0, %0" : "+v"(p));
       key[i] = skey[p];
       if (i < kSegBatch) tok[i] = sorted[p];
     }
 #pragma unroll
     for (int i = 0; i <= kSegBatch; ++i)
-      if (b0 + i >= p1) key[i] = v_after;
+      if (b0 + i >= pe) key[i] = -1;  // pe ends a run
     f32x4 row[kSegBatch], cur[kSegBatch];
 #pragma unroll
     for (int i = 0; i < kSegBatch; ++i) {
@@ -825,98 +978,33 @@ __global__ __launch_bounds__(256) void k_seg_chunks(const int32_t* __restrict__ 
     }
 #pragma unroll
     for (int i = 0; i < kSegBatch; ++i)
-      if (b0 + i >= p1 || !active) row[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // dW rows of runs that close in this batch and lie wholly in the chunk
-    if (accumulate) {
-      bool fr = first_run;
+      if (b0 + i >= pe || !active) row[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // dW rows of the runs that end in this batch
+    if (accumulate && active) {
 #pragma unroll
-      for (int i = 0; i < kSegBatch; ++i) {
-        const int64_t p = b0 + i;
-        if (p < p1 && key[i + 1] != key[i]) {
-          const bool closed = !(fr && cont_before) && !(p + 1 == p1 && v_after == key[i]);
-          if (closed && active)
-            cur[i] = *reinterpret_cast<const f32x4*>(dW + static_cast<int64_t>(key[i]) * H + col);
-          fr = false;
-        }
-      }
+      for (int i = 0; i < kSegBatch; ++i)
+        if (b0 + i < pe && key[i + 1] != key[i])
+          cur[i] = *reinterpret_cast<const f32x4*>(dW + static_cast<int64_t>(key[i]) * H + col);
     }
     // sums first (every load of the batch is waited for once), stores after:
     // on this GPU stores count in the same counter as loads, so a store
     // between two uses would make the second wait for the store as well
-    int dest[kSegBatch];  // 0 none, 1 the ID's row of dW, 2 partial slot 0, 3 slot 1
+    bool last[kSegBatch];
 #pragma unroll
     for (int i = 0; i < kSegBatch; ++i) {
-      const int64_t p = b0 + i;
-      dest[i] = 0;
-      if (p < p1) acc += row[i];
-      if (p < p1 && (p + 1 == p1 || key[i + 1] != key[i])) {  // last position of a run here
-        const bool from_before = first_run && cont_before;
-        const bool into_next = p + 1 == p1 && v_after == key[i];
-        dest[i] = (!from_before && !into_next) ? 1 : (from_before ? 2 : 3);
-        row[i] = (dest[i] == 1 && accumulate) ? cur[i] + acc : acc;
+      last[i] = b0 + i < pe && key[i + 1] != key[i];
+      if (b0 + i < pe) acc += row[i];
+      if (last[i]) {
+        row[i] = accumulate ? cur[i] + acc : acc;
         acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        first_run = false;
       }
     }
     if (active) {
 #pragma unroll
-      for (int i = 0; i < kSegBatch; ++i) {
-        if (dest[i] == 1)
-          *reinterpret_cast<f32x4*>(dW + static_cast<int64_t>(key[i]) * H + col) = row[i];
-        else if (dest[i] > 1)
-          *reinterpret_cast<f32x4*>(partial + (c * 2 + (dest[i] - 2)) * H + col) = row[i];
-      }
+      for (int i = 0; i < kSegBatch; ++i)
+        if (last[i]) *reinterpret_cast<f32x4*>(dW + static_cast<int64_t>(key[i]) * H + col) = row[i];
     }
   }
-}
-
-// One workgroup per (chunk, 256-column slice): if the chunk's first run
-// continues from the previous chunk and ends in this one, the workgroup
-// closes that ID: slot 1 of the chunk where the ID's run starts, then slot 0
-// of every later chunk up to this one. Wave w sums every kFixWaves-th of
-// those slots in chunk order, with kSegBatch loads in flight; the wave sums
-// are added in wave order.
-constexpr int kFixWaves = 4;
-__global__ __launch_bounds__(64 * kFixWaves) void k_seg_fix(const int32_t* __restrict__ skey,
-                                                            const int32_t* __restrict__ n_sorted,
-                                                            const int32_t* __restrict__ chunk_start,
-                                                            int64_t H, float* __restrict__ dW,
-                                                            int32_t accumulate,
-                                                            const float* __restrict__ partial) {
-  __shared__ f32x4 red[kFixWaves][64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t c = blockIdx.x;
-  const int64_t N = *n_sorted;
-  const int64_t p0 = c * kSegC;
-  if (c == 0 || p0 >= N) return;
-  const int32_t v = skey[p0];
-  if (skey[p0 - 1] != v) return;  // the first run starts here
-  const int64_t p1 = min(p0 + kSegC, N);
-  if (p1 < N && skey[p1 - 1] == v && skey[p1] == v) return;  // ... and goes on past this chunk
-  const int64_t col = static_cast<int64_t>(blockIdx.y) * kSegCols + lane * 4;
-  const int64_t colc = col < H ? col : H - 4;
-  const int64_t ca = chunk_start[c] / kSegC;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int STEP = kFixWaves * kSegBatch;
-  for (int64_t c0 = ca + 1 + w; c0 <= c; c0 += STEP) {
-    f32x4 part[kSegBatch];
-#pragma unroll
-    for (int u = 0; u < kSegBatch; ++u) {
-      const int64_t cc = min(c0 + static_cast<int64_t>(u) * kFixWaves, c);
-      part[u] = *reinterpret_cast<const f32x4*>(partial + (cc * 2 + 0) * H + colc);
-    }
-#pragma unroll
-    for (int u = 0; u < kSegBatch; ++u)
-      if (c0 + static_cast<int64_t>(u) * kFixWaves <= c) acc += part[u];
-  }
-  red[w][lane] = acc;
-  __syncthreads();
-  if (w != 0 || col >= H) return;
-  f32x4 tot = *reinterpret_cast<const f32x4*>(partial + (ca * 2 + 1) * H + col);
-#pragma unroll
-  for (int k = 0; k < kFixWaves; ++k) tot += red[k][lane];
-  f32x4* dst = reinterpret_cast<f32x4*>(dW + static_cast<int64_t>(v) * H + col);
-  *dst = accumulate ? *dst + tot : tot;
 }
 
 // ------------------------------------------------------------------ candidates
@@ -1206,12 +1294,13 @@ hipError_t run_emb_bwd(const int32_t* ids, const void* dout, bool dout_bf16, int
   // 1. stable sort of the tokens by ID
   if (p.runs) {
     hipLaunchKernelGGL(k_run_sort, dim3(static_cast<uint32_t>(p.nruns)), dim3(kRun), 0, s, ids, T,
-                       V_real, p.vbits, p.rid, p.rtok, p.rvalid);
+                       V_real, p.vbits, p.rid, p.rtok, p.rvalid, p.n_long);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(k_run_merge, dim3(static_cast<uint32_t>(p.nruns * kMergeSplit)),
                        dim3(kMergeThreads), 0, s, p.rid,
                        p.rtok, p.rvalid, static_cast<int32_t>(p.nruns), p.sorted, p.skey,
-                       p.n_sorted, p.chunk_start);
+                       p.n_sorted, p.chunk_start, p.chunk_end, p.long_runs, p.n_long,
+                       static_cast<int32_t>(p.nchunks));
     if ((err = hipGetLastError()) != hipSuccess) return err;
   } else {
     const int64_t ncnt = p.nblocks * V_real;
@@ -1224,7 +1313,7 @@ hipError_t run_emb_bwd(const int32_t* ids, const void* dout, bool dout_bf16, int
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(k_block_sort, dim3(static_cast<uint32_t>(p.nblocks)), dim3(kSortThreads), 0,
-                       s, ids, T, V_real, p.lkey, p.lrank, p.bcnt);
+                       s, ids, T, V_real, p.lkey, p.lrank, p.bcnt, p.n_long);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(k_col_scan, dim3(static_cast<uint32_t>(cdiv(V_real, 256))), dim3(256), 0, s,
                        p.bcnt, p.nblocks, V_real, p.counts);
@@ -1236,22 +1325,23 @@ hipError_t run_emb_bwd(const int32_t* ids, const void* dout, bool dout_bf16, int
                        s, p.lkey, p.lrank, p.bcnt, p.offs, nkeys, V_real, p.sorted, p.skey);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(k_chunk_starts, dim3(static_cast<uint32_t>(cdiv(p.nchunks, 256))),
-                       dim3(256), 0, s, p.skey, p.offs, p.n_sorted, p.nchunks, p.chunk_start);
+                       dim3(256), 0, s, p.skey, p.offs, p.n_sorted, p.nchunks, p.chunk_start,
+                       p.chunk_end, p.long_runs, p.n_long);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  // 2. chunk sums, then the IDs that cross chunk ends
-  const dim3 grid(static_cast<uint32_t>(p.nchunks), static_cast<uint32_t>(cdiv(p.nslices, 4)));
+  // 2. segment sums: long IDs by column slices, the others by chunks
+  const int64_t nwg = p.long_wgs + p.nchunks * cdiv(p.nslices, 4);
+  const dim3 grid(static_cast<uint32_t>(nwg));
   if (dout_bf16)
-    hipLaunchKernelGGL(k_seg_chunks<uint16_t>, grid, dim3(256), 0, s, p.skey, p.sorted, p.n_sorted,
-                       static_cast<const uint16_t*>(dout), H, p.nslices, dW, accumulate,
-                       p.partial);
+    hipLaunchKernelGGL(k_seg_sums<uint16_t>, grid, dim3(256), 0, s, p.skey, p.sorted, p.n_sorted,
+                       p.chunk_start, p.chunk_end, p.long_runs, p.n_long,
+                       static_cast<const uint16_t*>(dout), H, p.nslices, p.nchunks, p.long_wgs,
+                       dW, accumulate);
   else
-    hipLaunchKernelGGL(k_seg_chunks<float>, grid, dim3(256), 0, s, p.skey, p.sorted, p.n_sorted,
-                       static_cast<const float*>(dout), H, p.nslices, dW, accumulate, p.partial);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  const dim3 fgrid(static_cast<uint32_t>(p.nchunks), static_cast<uint32_t>(p.nslices));
-  hipLaunchKernelGGL(k_seg_fix, fgrid, dim3(64 * kFixWaves), 0, s, p.skey, p.n_sorted,
-                     p.chunk_start, H, dW, accumulate, p.partial);
+    hipLaunchKernelGGL(k_seg_sums<float>, grid, dim3(256), 0, s, p.skey, p.sorted, p.n_sorted,
+                       p.chunk_start, p.chunk_end, p.long_runs, p.n_long,
+                       static_cast<const float*>(dout), H, p.nslices, p.nchunks, p.long_wgs, dW,
+                       accumulate);
   return hipGetLastError();
 }
 
