@@ -36,10 +36,10 @@ constexpr int kRunMaxRuns = 32;                            // runs the merge hol
 constexpr int kPlanDigit = 6;                              // ID bits per radix pass
 constexpr int kSortBlock = 1024;                           // tokens per local sort
 constexpr int kSortThreads = 512;
-constexpr int kSegLong = 32;     // tokens of an ID from which its sum is split by columns
+constexpr int kSegLong = 64;     // tokens of an ID from which its sum is split by columns
 constexpr int kLongCols = 64;    // columns per long-ID item (16 lanes x 4)
 constexpr int kLongBatch = 16;   // dout rows in flight per lane of a long-ID item
-constexpr int kLongWGs = 512;    // workgroups that take the long-ID items
+constexpr int kLongWGs = 1024;   // workgroups that take the long-ID items
 
 // ------------------------------------------------------------------ planning
 
@@ -84,7 +84,7 @@ EmbBwdPlan plan_emb_bwd(int64_t T, int64_t H, int64_t V_real, void* ws) {
   p.skey = c.take<int32_t>(static_cast<size_t>(Tp));
   p.chunk_start = c.take<int32_t>(static_cast<size_t>(p.nchunks));
   p.chunk_end = c.take<int32_t>(static_cast<size_t>(p.nchunks));
-  p.long_runs = c.take<int32_t>(static_cast<size_t>(p.nchunks * 2));
+  p.long_runs = c.take<int32_t>(static_cast<size_t>(p.nchunks * 4));
   p.n_long = c.take<int32_t>(1);
   if (p.offs) p.n_sorted = p.offs + V_real;
   // long IDs: at most Tp / kSegLong of them, each cut into cdiv(H, kLongCols) items
@@ -698,20 +698,21 @@ __global__ __launch_bounds__(kRun) void k_run_sort(const int32_t* __restrict__ i
   if (tid == 0) rvalid[blockIdx.x] = s_n;
 }
 
-// Both bounds of x (< 2^31) in every run k < nruns: lt_k = #(IDs < x) and
-// le_k = #(IDs <= x) among the run's kRun ascending IDs. Returns
-//   off = sum_{k < r} le_k + sum_{k > r} lt_k,  lt = sum_k lt_k,  le = sum_k le_k.
-// The 2U binary searches advance together with no branches (a run at or past
+// Both bounds of x (< 2^31) in the runs k = q, q + 4, q + 8, ... below
+// nruns (U slots): lt_k = #(IDs < x) and le_k = #(IDs <= x) among the run's
+// kRun ascending IDs. Adds to off (le_k for k < r, lt_k for k > r), lt and le.
+// The 2U binary searches advance together with no branches (a slot past
 // nruns searches the last run and adds nothing), so the 2U LDS reads of a
 // step are in flight at once.
 template <int U>
-__device__ __forceinline__ void run_bounds(const uint32_t* all, int nruns, int r, uint32_t x,
-                                           int32_t& off, int32_t& lt, int32_t& le) {
+__device__ __forceinline__ void run_bounds(const uint32_t* all, int nruns, int q, int r,
+                                           uint32_t x, int32_t& off, int32_t& lt, int32_t& le) {
   const uint32_t* base[U];
   int32_t a[U], b[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    base[u] = all + (u < nruns ? u : nruns - 1) * kRun;
+    const int k = q + 4 * u;
+    base[u] = all + (k < nruns ? k : nruns - 1) * kRun;
     a[u] = 0;
     b[u] = 0;
   }
@@ -729,54 +730,59 @@ __device__ __forceinline__ void run_bounds(const uint32_t* all, int nruns, int r
       b[u] += yb[u] <= x ? step : 0;
     }
   }
-  off = 0;
-  lt = 0;
-  le = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     // a, b <= kRun - 1 here: element a (b) is the last one left to test
+    const int k = q + 4 * u;
     const int32_t ra = a[u] + (base[u][a[u]] < x ? 1 : 0);
     const int32_t rb = b[u] + (base[u][b[u]] <= x ? 1 : 0);
-    if (u < nruns) {
+    if (k < nruns) {
       lt += ra;
       le += rb;
-      off += u < r ? rb : (u > r ? ra : 0);
+      off += k < r ? rb : (k > r ? ra : 0);
     }
   }
 }
 
-// k_run_merge: kMergeSplit workgroups per run place its tokens. With the
-// runs' IDs in LDS, a token at index i of run r with ID v goes to
+// k_run_merge: a workgroup places kRankTok tokens of one run, four threads
+// per token, each searching a quarter of the runs. With the runs' IDs in
+// LDS, a token at index i of run r with ID v goes to
 //   i + (tokens with ID <= v in runs before r) + (tokens with ID < v in runs after r),
 // which is its rank in (ID, token) order, since run r holds tokens
 // [r*kRun, (r+1)*kRun). The same searches give where v's tokens start and
 // end in the sorted list: a token at a chunk's first position records them
 // for its chunk, and the first token of an ID with at least kSegLong tokens
 // appends the ID's (start, end) to the long list (in any order).
-constexpr int kMergeSplit = 4;
-constexpr int kMergeThreads = kRun / kMergeSplit;
+constexpr int kRankTok = 64;
+constexpr int kMergeSplit = kRun / kRankTok;  // workgroups per run
 static_assert(kRunMaxRuns <= 64, "one wave sums the run counts");
-__global__ __launch_bounds__(kMergeThreads) void k_run_merge(
+static_assert(kRunMaxRuns % 4 == 0, "four threads per token split the runs");
+__global__ __launch_bounds__(4 * kRankTok) void k_run_merge(
     const uint32_t* __restrict__ rid, const int32_t* __restrict__ rtok,
     const int32_t* __restrict__ rvalid, int32_t nruns, int32_t* __restrict__ sorted,
     int32_t* __restrict__ skey, int32_t* __restrict__ n_sorted,
     int32_t* __restrict__ chunk_start, int32_t* __restrict__ chunk_end,
     int32_t* __restrict__ long_runs, int32_t* __restrict__ n_long, int32_t long_cap) {
   __shared__ __attribute__((aligned(16))) uint32_t all[kRunMaxRuns * kRun];
+  constexpr int NT = 4 * kRankTok;
   const int tid = threadIdx.x;
   const int r = blockIdx.x / kMergeSplit;
-  const int i = (blockIdx.x % kMergeSplit) * kMergeThreads + tid;  // index in run r
-  // nruns * kRun IDs = nruns 16-byte pieces per thread, eight loads in flight
+  const int i = (blockIdx.x % kMergeSplit) * kRankTok + tid / 4;  // index in run r
+  const int q = tid % 4;                                           // runs q, q+4, ...
+  // nruns * kRun IDs: nruns * kRun / (4 * NT) 16-byte pieces per thread,
+  // sixteen loads in flight
+  const int32_t tk = rtok[r * kRun + i];  // loaded with the IDs, used at the end
   const u32x4* src = reinterpret_cast<const u32x4*>(rid);
   u32x4* dst = reinterpret_cast<u32x4*>(all);
-  for (int j0 = 0; j0 < nruns; j0 += 8) {
-    u32x4 x[8];
+  const int npieces = nruns * (kRun / 4);
+  for (int p0 = 0; p0 < npieces; p0 += 16 * NT) {
+    u32x4 x[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (j0 + u < nruns) x[u] = src[(j0 + u) * kMergeThreads + tid];
+    for (int u = 0; u < 16; ++u)
+      if (p0 + u * NT + tid < npieces) x[u] = src[p0 + u * NT + tid];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (j0 + u < nruns) dst[(j0 + u) * kMergeThreads + tid] = x[u];
+    for (int u = 0; u < 16; ++u)
+      if (p0 + u * NT + tid < npieces) dst[p0 + u * NT + tid] = x[u];
   }
   if (blockIdx.x == 0 && tid < 64) {  // nruns <= 64: one load per lane, one wave sum
     int32_t n = tid < nruns ? rvalid[tid] : 0;
@@ -786,14 +792,22 @@ __global__ __launch_bounds__(kMergeThreads) void k_run_merge(
   }
   __syncthreads();
   const uint32_t v = all[r * kRun + i];
-  if (v == ~0u) return;
-  int32_t off, lt, le;
+  if (v == ~0u) return;  // the same for the four threads of a token
+  int32_t off = 0, lt = 0, le = 0;
   if (nruns <= kRunMaxRuns / 2)  // uniform
-    run_bounds<kRunMaxRuns / 2>(all, nruns, r, v, off, lt, le);
+    run_bounds<kRunMaxRuns / 8>(all, nruns, q, r, v, off, lt, le);
   else
-    run_bounds<kRunMaxRuns>(all, nruns, r, v, off, lt, le);
+    run_bounds<kRunMaxRuns / 4>(all, nruns, q, r, v, off, lt, le);
+  // sums over the four threads of the token (adjacent lanes)
+#pragma unroll
+  for (int o = 1; o < 4; o <<= 1) {
+    off += __shfl_xor(off, o);
+    lt += __shfl_xor(lt, o);
+    le += __shfl_xor(le, o);
+  }
+  if (q != 0) return;
   const int32_t pos = i + off;
-  sorted[pos] = rtok[r * kRun + i];
+  sorted[pos] = tk;
   skey[pos] = static_cast<int32_t>(v);
   if (pos % kSegC == 0) {
     chunk_start[pos / kSegC] = lt;
@@ -801,10 +815,8 @@ __global__ __launch_bounds__(kMergeThreads) void k_run_merge(
   }
   if (pos == lt && le - lt >= kSegLong) {
     const int32_t k = atomicAdd(n_long, 1);
-    if (k < long_cap) {  // at most (tokens / kSegLong) long IDs: always true
-      long_runs[2 * k] = lt;
-      long_runs[2 * k + 1] = le;
-    }
+    if (k < long_cap)  // at most (tokens / kSegLong) long IDs: always true
+      reinterpret_cast<i32x4*>(long_runs)[k] = i32x4{lt, le, static_cast<int32_t>(v), 0};
   }
 }
 
@@ -828,10 +840,8 @@ __global__ __launch_bounds__(256) void k_chunk_starts(const int32_t* __restrict_
   chunk_end[c] = le;
   if (le - lt >= kSegLong && lt > c * kSegC - kSegC) {
     const int32_t k = atomicAdd(n_long, 1);
-    if (k < nchunks) {  // at most (tokens / kSegLong) long IDs: always true
-      long_runs[2 * k] = lt;
-      long_runs[2 * k + 1] = le;
-    }
+    if (k < nchunks)  // at most (tokens / kSegLong) long IDs: always true
+      reinterpret_cast<i32x4*>(long_runs)[k] = i32x4{lt, le, static_cast<int32_t>(id), 0};
   }
 }
 
@@ -839,35 +849,43 @@ __global__ __launch_bounds__(256) void k_chunk_starts(const int32_t* __restrict_
 
 // Long IDs: item j = (long ID j / nls, column slice j % nls) of kLongCols
 // columns; the workgroups [0, long_wgs) take items wg, wg + long_wgs, ...
-// Sixteen row lanes (4 waves x 4 groups of 16 lanes, 4 columns per lane)
-// each sum every 16th token of the run in sorted order, kLongBatch rows in
-// flight, the next batch's token indices loading behind them; the row lanes'
-// sums are added in row-lane order through LDS and the slice of the ID's row
-// is written (added to when accumulating) once.
+// kLongRowLanes row lanes (groups of kLongCols / 4 lanes, 4 columns per
+// lane) each sum every kLongRowLanes-th token of the run in sorted order,
+// kLongBatch rows in flight, the next batch's token indices loading behind
+// them; the row lanes' sums are added in row-lane order through LDS and the
+// slice of the ID's row is written (added to when accumulating) once.
+constexpr int kLongLanesPerRow = kLongCols / 4;
+constexpr int kLongRowLanes = 256 / kLongLanesPerRow;
 template <typename D>
 __device__ __forceinline__ void seg_long(int64_t wg, int64_t nwg, const int32_t* skey,
                                          const int32_t* sorted, const int32_t* long_runs,
                                          int32_t n_long, int32_t N, const D* dout, int64_t H,
-                                         float* dW, int32_t accumulate, f32x4 (*red)[16]) {
-  const int lane = threadIdx.x & 63;
-  const int rl = (threadIdx.x >> 6) * 4 + (lane >> 4);  // row lane 0..15
-  const int cl = lane & 15;                              // column lane
+                                         float* dW, int32_t accumulate,
+                                         f32x4 (*red)[kLongLanesPerRow]) {
+  const int rl = threadIdx.x / kLongLanesPerRow;  // row lane
+  const int cl = threadIdx.x % kLongLanesPerRow;  // column lane
   const int64_t nls = (H + kLongCols - 1) / kLongCols;
   const int64_t items = static_cast<int64_t>(n_long) * nls;
-  constexpr int STEP = 16 * kLongBatch;  // positions per batch of the workgroup
+  constexpr int STEP = kLongRowLanes * kLongBatch;  // positions per batch of the workgroup
   for (int64_t j = wg; j < items; j += nwg) {
     const int64_t k = j / nls;
     // (first, end) lie in [0, N] with first < end; clamped all the same, so
     // that no read can leave the sorted list
-    const int32_t end = min(long_runs[2 * k + 1], N);
-    const int32_t first = max(0, min(long_runs[2 * k], end - 1));
+    const i32x4 e = reinterpret_cast<const i32x4*>(long_runs)[k];
+    const int32_t end = min(e.y, N);
+    const int32_t first = max(0, min(e.x, end - 1));
     const int64_t col = (j % nls) * kLongCols + cl * 4;
     const bool active = col < H;
     const int64_t colc = active ? col : H - 4;  // a readable column; its sum is dropped
+    // the row slice this item adds into, loaded now and used at the end
+    f32x4* dst = reinterpret_cast<f32x4*>(dW + static_cast<int64_t>(e.z) * H + colc);
+    f32x4 old = {0.f, 0.f, 0.f, 0.f};
+    if (accumulate && threadIdx.x < kLongLanesPerRow) old = *dst;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     int32_t tok[kLongBatch];
 #pragma unroll
-    for (int u = 0; u < kLongBatch; ++u) tok[u] = sorted[min(first + u * 16 + rl, end - 1)];
+    for (int u = 0; u < kLongBatch; ++u)
+      tok[u] = sorted[min(first + u * kLongRowLanes + rl, end - 1)];
     for (int32_t b0 = first; b0 < end; b0 += STEP) {
       f32x4 row[kLongBatch];
 #pragma unroll
@@ -876,20 +894,19 @@ __device__ __forceinline__ void seg_long(int64_t wg, int64_t nwg, const int32_t*
       if (b0 + STEP < end) {
 #pragma unroll
         for (int u = 0; u < kLongBatch; ++u)
-          tok[u] = sorted[min(b0 + STEP + u * 16 + rl, end - 1)];
+          tok[u] = sorted[min(b0 + STEP + u * kLongRowLanes + rl, end - 1)];
       }
 #pragma unroll
       for (int u = 0; u < kLongBatch; ++u)
-        if (b0 + u * 16 + rl < end) acc += row[u];
+        if (b0 + u * kLongRowLanes + rl < end) acc += row[u];
     }
     red[rl][cl] = acc;
     __syncthreads();
-    if (threadIdx.x < 16 && active) {  // row group 0 of wave 0: cl == threadIdx.x
+    if (threadIdx.x < kLongLanesPerRow && active) {  // row lane 0: cl == threadIdx.x
       f32x4 tot = red[0][cl];
 #pragma unroll
-      for (int q = 1; q < 16; ++q) tot += red[q][cl];
-      f32x4* dst = reinterpret_cast<f32x4*>(dW + static_cast<int64_t>(skey[first]) * H + col);
-      *dst = accumulate ? *dst + tot : tot;
+      for (int q = 1; q < kLongRowLanes; ++q) tot += red[q][cl];
+      *dst = accumulate ? old + tot : tot;
     }
     __syncthreads();  // red is reused by the next item
   }
@@ -917,7 +934,7 @@ __global__ __launch_bounds__(256) void k_seg_sums(const int32_t* __restrict__ sk
                                                   int64_t nslices, int64_t nchunks,
                                                   int64_t long_wgs, float* __restrict__ dW,
                                                   int32_t accumulate) {
-  __shared__ f32x4 red[16][16];
+  __shared__ f32x4 red[kLongRowLanes][kLongLanesPerRow];
   if (static_cast<int64_t>(blockIdx.x) < long_wgs) {
     const int32_t nl = min(*n_long, static_cast<int32_t>(nchunks));
     seg_long<D>(blockIdx.x, long_wgs, skey, sorted, long_runs, nl, *n_sorted, dout, H, dW,
@@ -933,14 +950,15 @@ __global__ __launch_bounds__(256) void k_seg_sums(const int32_t* __restrict__ sk
   const int64_t p0 = c * kSegC;
   if (slice >= nslices || p0 >= N) return;
   // [pb, pe): whole runs of short IDs that start in this chunk
+  const int64_t cn = min(c + 1, nchunks - 1);  // read only when position p0 + kSegC exists
   const int32_t cs = chunk_start[c], ce = chunk_end[c];
+  const int32_t cs2 = chunk_start[cn], ce2 = chunk_end[cn];
   const int64_t pb = (cs == p0 && ce - cs < kSegLong) ? p0 : ce;
   int64_t pe;
   const int64_t q = p0 + kSegC;
   if (q >= N) {
     pe = N;
   } else {
-    const int32_t cs2 = chunk_start[c + 1], ce2 = chunk_end[c + 1];
     if (cs2 == q)
       pe = q;
     else if (cs2 < p0)
@@ -955,7 +973,7 @@ __global__ __launch_bounds__(256) void k_seg_sums(const int32_t* __restrict__ sk
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int64_t colc = active ? col : H - 4;  // a readable column; its results are dropped
   for (int64_t b0 = pb; b0 < pe; b0 += kSegBatch) {
-    // every index is clamped into [pb, pe) so that all loads of a batch are
+    // every index is clamped into [b0, pe) so that all loads of a batch are
     // issued back to back; entries past pe are masked afterwards (loaded into
     // vector registers: as scalars, the 33 values and 16 row addresses
     // exhaust the scalar registers and the loads serialise)
@@ -1297,7 +1315,7 @@ hipError_t run_emb_bwd(const int32_t* ids, const void* dout, bool dout_bf16, int
                        V_real, p.vbits, p.rid, p.rtok, p.rvalid, p.n_long);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(k_run_merge, dim3(static_cast<uint32_t>(p.nruns * kMergeSplit)),
-                       dim3(kMergeThreads), 0, s, p.rid,
+                       dim3(4 * kRankTok), 0, s, p.rid,
                        p.rtok, p.rvalid, static_cast<int32_t>(p.nruns), p.sorted, p.skey,
                        p.n_sorted, p.chunk_start, p.chunk_end, p.long_runs, p.n_long,
                        static_cast<int32_t>(p.nchunks));

@@ -194,7 +194,7 @@ struct EmbBwdPlan {
   int32_t* n_sorted;   // [1] number of valid tokens (runs; general: offs + V_real)
   int32_t* chunk_start;// [nchunks] first sorted position of the ID at each chunk's first position
   int32_t* chunk_end;  // [nchunks] one past its last sorted position
-  int32_t* long_runs;  // [nchunks][2] (first, end) of every ID with at least kSegLong tokens
+  int32_t* long_runs;  // [nchunks][4] (first, end, ID, 0) of every ID with at least kSegLong tokens
   int32_t* n_long;     // [1] number of such IDs
   int64_t long_wgs;    // workgroups of the segment-sum launch that take the long IDs
   size_t bytes;
