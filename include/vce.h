@@ -385,6 +385,29 @@ vce_status vss_candidates(const int32_t* targets, int64_t T, int64_t V, int32_t 
 vce_status vss_scatter(const int32_t* cand, int64_t P, const float* dWc, int64_t H, int64_t V,
                        float* dW, int32_t accumulate, void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * Sampled-softmax gradient scatter into a table kept across steps.          *
+ *                                                                           *
+ * [SS] Setup: a step's gradient lives in its candidate rows only. A caller  *
+ * that keeps one dW table from step to step, zero except at the rows the    *
+ * previous call wrote (prev [P_prev]), gets the table that vss_scatter with *
+ * accumulate = 0 writes while clearing only those rows: every prev[j] in    *
+ * [0, V) is set to zero, then dW[cand[i]] = dWc[i] for cand[i] in [0, V)    *
+ * (distinct, as for vss_scatter). P_prev*H*4 bytes are cleared instead of   *
+ * V*H*4. Precondition: every row of dW not listed in prev is zero (the      *
+ * caller zeroes the table once, before its first call, with P_prev = 0).    *
+ * On such a table the result has the same bits as vss_scatter(cand, P, dWc, *
+ * H, V, dW, 0). prev may repeat rows, share rows with cand and hold values  *
+ * outside [0, V) (skipped). The two steps run in order on the stream.       *
+ * In:  prev [P_prev] int32, cand [P] int32, dWc [P, H] f32.                 *
+ * Out: dW [V, H] f32.                                                       *
+ * Errors: P_prev < 0 or as vss_scatter: VCE_ERR_SHAPE; prev NULL with       *
+ * P_prev > 0, or as vss_scatter: VCE_ERR_NULL; misaligned prev, or as       *
+ * vss_scatter: VCE_ERR_ALIGN.                                               *
+ * ------------------------------------------------------------------------ */
+vce_status vss_scatter_replace(const int32_t* prev, int64_t P_prev, const int32_t* cand, int64_t P,
+                               const float* dWc, int64_t H, int64_t V, float* dW, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in vce.SIGNATURES, n
@@ -209,6 +209,22 @@ def test_scatter_argument_errors():
     assert args(V=0) == SHAPE
     assert args(H=0) == SHAPE
     assert args(acc=2) == DTYPE
+    assert args(dW=NUL) == NULL
+    assert args(cand=NUL) == NULL
+    assert args(src=NUL) == NULL
+    assert args(H=60) == ALIGN
+    assert args(dW=MIS) == ALIGN
+    assert args(src=MIS) == ALIGN
+
+
+def test_scatter_replace_argument_errors():
+    args = lambda prev=A, Pp=5, cand=A, P=10, src=B, H=64, V=100, dW=C: lib.vss_scatter_replace(
+        prev, Pp, cand, P, src, H, V, dW, None)
+    assert args(Pp=-1) == SHAPE
+    assert args(P=-1) == SHAPE
+    assert args(V=0) == SHAPE
+    assert args(H=0) == SHAPE
+    assert args(prev=NUL) == NULL
     assert args(dW=NUL) == NULL
     assert args(cand=NUL) == NULL
     assert args(src=NUL) == NULL

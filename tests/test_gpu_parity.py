@@ -466,6 +466,52 @@ def test_sampled_scatter_exact(V, P, H, Vt, acc):
     np.testing.assert_array_equal(out.cpu().numpy(), ref.astype(np.float32))
 
 
+def test_sampled_scatter_replace_keeps_only_the_last_rows(V):
+    """vss_scatter_replace over a run of calls on one table (zeroed once):
+    after each call the table equals the oracle's scatter of that call's rows
+    into zeros, whatever rows the earlier calls wrote (overlapping sets,
+    repeated and out-of-range entries in the previous list)."""
+    say("case sampled scatter replace, four calls")
+    dev = "cuda"
+    rng = np.random.default_rng(77)
+    Vt, H = 3000, 264
+    dW = torch.zeros(Vt, H, dtype=torch.float32, device=dev)
+    prev = None
+    for k, P in enumerate([500, 1200, 0, 800]):
+        cand = rng.permutation(Vt + 40)[:P].astype(np.int32) - 20  # distinct; some outside
+        dWc = rng.standard_normal((P, H)).astype(np.float32)
+        cand_t = torch.from_numpy(cand).to(dev)
+        if prev is not None and prev.numel():
+            prev = torch.cat([prev, prev[:3]])  # repeats are harmless
+        V.vss_scatter_replace(prev, cand_t, torch.from_numpy(dWc).to(dev), dW)
+        torch.cuda.synchronize()
+        ref, _ = oracle.scatter_add(cand, dWc.astype(np.float64), Vt, Vt)
+        np.testing.assert_array_equal(dW.cpu().numpy(), ref.astype(np.float32), err_msg=f"call {k}")
+        prev = cand_t
+
+
+def test_sampled_step_replace_is_bitwise_the_full_fill(V):
+    """Consecutive sampled steps with different batches: the table kept across
+    steps (only the previous step's rows cleared) holds the same bits as the
+    whole-table fill of every step."""
+    say("case sampled step replace vs full fill, three steps")
+    dev = "cuda"
+    Vt = 16384
+    dW_keep = torch.zeros(Vt, 128, dtype=torch.float32, device=dev)
+    rows = torch.empty(0, dtype=torch.int32, device=dev)
+    for seed in (21, 22, 23):
+        inp = make_sampled_inputs(1024, 128, Vt, 2048, "bf16", seed=seed)
+        h = V.from_bits(inp.h, "bf16", dev)
+        W = V.from_bits(inp.W, "bf16", dev)
+        tg = torch.from_numpy(inp.targets).to(dev)
+        pm = torch.from_numpy(inp.perm).to(dev)
+        full = V.sampled_step(h, W, tg, pm, inp.P)
+        kept = V.sampled_step(h, W, tg, pm, inp.P, dW=dW_keep, prev_rows=rows)
+        torch.cuda.synchronize()
+        assert torch.equal(full.dW.view(torch.int32), kept.dW.view(torch.int32)), seed
+        rows = kept.extra["rows"]
+
+
 def test_sampled_step_small(V):
     say("case sampled step T=1024 H=128 V=16384 P=2048")
     dev = "cuda"

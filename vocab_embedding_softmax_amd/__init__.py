@@ -11,7 +11,7 @@ from ._lib import (  # noqa: F401
     vce_argmax, vce_argmax_noalloc, vce_argmax_workspace_bytes, vce_bwd, vce_bwd_workspace_bytes, vce_fwd,
     vce_fwd_workspace_bytes, vce_remap, vemb_bwd,
     vemb_bwd_workspace_bytes, vemb_fwd, vngram_fwd, vss_candidates, vss_candidates_workspace_bytes,
-    vss_scatter,
+    vss_scatter, vss_scatter_replace,
 )
 from .steps import (  # noqa: F401
     Workspaces, ce_step, from_bits, ngram_bwd, ot_h_step, sampled_step, tied_step,

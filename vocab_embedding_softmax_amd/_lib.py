@@ -65,6 +65,7 @@ SIGNATURES = {
     "vss_candidates_workspace_bytes": (_SZ, [_I64, _I64]),
     "vss_candidates": (_I32, [_P, _I64, _I64, _I32, _P, _I64, _P, _I64, _P, _P, _P, _P, _SZ, _P]),
     "vss_scatter": (_I32, [_P, _I64, _P, _I64, _I64, _P, _I32, _P]),
+    "vss_scatter_replace": (_I32, [_P, _I64, _P, _I64, _P, _I64, _I64, _P, _P]),
 }
 
 
@@ -499,4 +500,24 @@ def vss_scatter(cand: torch.Tensor, dWc: torch.Tensor, V: int, *,
     st = lib.vss_scatter(_ptr(cand), P, _ptr(dWc), H, V, _ptr(dW), 1 if accumulate else 0,
                          _stream(stream, dev))
     _check("vss_scatter", st)
+    return dW
+
+
+def vss_scatter_replace(prev: Optional[torch.Tensor], cand: torch.Tensor, dWc: torch.Tensor,
+                        dW: torch.Tensor, *, stream=None) -> torch.Tensor:
+    """dW [V, H] float32 holds nonzero values only in the rows listed in prev
+    (the previous call's candidates; None or empty for a zero table): those
+    rows are cleared, then dW[cand[i]] = dWc[i]. Same table as
+    vss_scatter(cand, dWc, V, dW=dW) with accumulate=False."""
+    P, H = dWc.shape
+    _need(cand, "cand", torch.int32, (P,))
+    _need(dWc, "dWc", torch.float32, (P, H))
+    V = dW.shape[0]
+    _need(dW, "dW", torch.float32, (V, H))
+    n_prev = 0 if prev is None else prev.shape[0]
+    if n_prev:
+        _need(prev, "prev", torch.int32, (n_prev,))
+    st = lib.vss_scatter_replace(_ptr(prev) if n_prev else None, n_prev, _ptr(cand), P,
+                                 _ptr(dWc), H, V, _ptr(dW), _stream(stream, dWc.device))
+    _check("vss_scatter_replace", st)
     return dW

@@ -385,4 +385,18 @@ vce_status vss_scatter(const int32_t* cand, int64_t P, const float* dWc, int64_t
       vce::run_ss_scatter(cand, P, dWc, H, V, dW, accumulate, static_cast<hipStream_t>(stream)));
 }
 
+vce_status vss_scatter_replace(const int32_t* prev, int64_t P_prev, const int32_t* cand, int64_t P,
+                               const float* dWc, int64_t H, int64_t V, float* dW, void* stream) {
+  if (P_prev < 0 || P_prev > kMaxDim) return VCE_ERR_SHAPE;
+  if (P < 0 || V < 1 || H <= 0 || P > kMaxDim || V > kMaxDim || H > kMaxDim) return VCE_ERR_SHAPE;
+  if (!dW) return VCE_ERR_NULL;
+  if (P_prev > 0 && !prev) return VCE_ERR_NULL;
+  if (P > 0 && (!cand || !dWc)) return VCE_ERR_NULL;
+  if (H % 8 != 0 || !aligned16(dW)) return VCE_ERR_ALIGN;
+  if (P_prev > 0 && !aligned4(prev)) return VCE_ERR_ALIGN;
+  if (P > 0 && (!aligned4(cand) || !aligned16(dWc))) return VCE_ERR_ALIGN;
+  return hip_status(vce::run_ss_scatter_replace(prev, P_prev, cand, P, dWc, H, V, dW,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -1280,6 +1280,20 @@ __global__ __launch_bounds__(256) void k_scatter_rows(const int32_t* __restrict_
   }
 }
 
+// dW[rows[i]] = 0 for rows[i] in [0, V): one wave per row, 8 float4 stores
+// per lane in flight.
+__global__ __launch_bounds__(256) void k_zero_rows(const int32_t* __restrict__ rows, int64_t n,
+                                                   int64_t H, int64_t V, float* __restrict__ dW) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (i >= n) return;
+  const int64_t v = rows[i];
+  if (v < 0 || v >= V) return;
+  f32x4* d = reinterpret_cast<f32x4*>(dW + v * H);
+  const int64_t n4 = H / 4;
+  for (int64_t j = lane; j < n4; j += 64) d[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
 // ------------------------------------------------------------------ launchers
 
 hipError_t run_emb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H, int64_t V_real,
@@ -1363,6 +1377,18 @@ hipError_t run_emb_bwd(const int32_t* ids, const void* dout, bool dout_bf16, int
   return hipGetLastError();
 }
 
+// The candidate rows' copy (add = false) or add into dW, no fill.
+static hipError_t scatter_rows(const int32_t* cand, int64_t P, const float* dWc, int64_t H,
+                               int64_t V, float* dW, bool add, hipStream_t s) {
+  if (P == 0) return hipSuccess;
+  const dim3 grid(static_cast<uint32_t>(cdiv(P, 4)));
+  if (add)
+    hipLaunchKernelGGL(k_scatter_rows<true>, grid, dim3(256), 0, s, cand, P, dWc, H, V, dW);
+  else
+    hipLaunchKernelGGL(k_scatter_rows<false>, grid, dim3(256), 0, s, cand, P, dWc, H, V, dW);
+  return hipGetLastError();
+}
+
 hipError_t run_ss_scatter(const int32_t* cand, int64_t P, const float* dWc, int64_t H, int64_t V,
                           float* dW, int32_t accumulate, hipStream_t s) {
   if (!accumulate) {
@@ -1372,13 +1398,19 @@ hipError_t run_ss_scatter(const int32_t* cand, int64_t P, const float* dWc, int6
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  if (P == 0) return hipSuccess;
-  const dim3 grid(static_cast<uint32_t>(cdiv(P, 4)));
-  if (accumulate)
-    hipLaunchKernelGGL(k_scatter_rows<true>, grid, dim3(256), 0, s, cand, P, dWc, H, V, dW);
-  else
-    hipLaunchKernelGGL(k_scatter_rows<false>, grid, dim3(256), 0, s, cand, P, dWc, H, V, dW);
-  return hipGetLastError();
+  return scatter_rows(cand, P, dWc, H, V, dW, accumulate != 0, s);
+}
+
+hipError_t run_ss_scatter_replace(const int32_t* prev, int64_t P_prev, const int32_t* cand,
+                                  int64_t P, const float* dWc, int64_t H, int64_t V, float* dW,
+                                  hipStream_t s) {
+  if (P_prev > 0) {
+    hipLaunchKernelGGL(k_zero_rows, dim3(static_cast<uint32_t>(cdiv(P_prev, 4))), dim3(256), 0, s,
+                       prev, P_prev, H, V, dW);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return scatter_rows(cand, P, dWc, H, V, dW, false, s);  // rows of a zero table: copy
 }
 
 hipError_t run_candidates(const int32_t* targets, int64_t T, int64_t V, const int32_t* perm,

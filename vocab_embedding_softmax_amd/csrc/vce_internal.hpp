@@ -250,6 +250,9 @@ hipError_t run_emb_bwd(const int32_t* ids, const void* dout, bool dout_bf16, int
 // dW zeroed first unless accumulating
 hipError_t run_ss_scatter(const int32_t* cand, int64_t P, const float* dWc, int64_t H, int64_t V,
                           float* dW, int32_t accumulate, hipStream_t s);
+hipError_t run_ss_scatter_replace(const int32_t* prev, int64_t P_prev, const int32_t* cand,
+                                  int64_t P, const float* dWc, int64_t H, int64_t V, float* dW,
+                                  hipStream_t s);
 hipError_t run_candidates(const int32_t* targets, int64_t T, int64_t V, const int32_t* perm,
                           int64_t P, int32_t* cand, int32_t* pos, int32_t* n_unique,
                           int32_t* n_cand, const CandPlan& p, hipStream_t s);

@@ -80,7 +80,8 @@ def tied_step(ids, targets, W, V_real, num_shards, ignore_index=-100, *, grad_lo
 
 def sampled_step(h, W, targets, perm, P, ignore_index=-100, *, grad_loss=None,
                  reduction=L.REDUCE_MEAN, ws: Optional[Workspaces] = None, dW=None,
-                 n_cand: Optional[int] = None, allow_bad=False, stream=None) -> StepOut:
+                 prev_rows=None, n_cand: Optional[int] = None, allow_bad=False,
+                 stream=None) -> StepOut:
     """The composite is sized by the number of candidates, n_cand = max(P, |U|)
     (U = the batch's distinct valid targets): with more distinct targets than
     P the candidates are U alone and every one of them takes part.
@@ -92,7 +93,13 @@ def sampled_step(h, W, targets, perm, P, ignore_index=-100, *, grad_loss=None,
     targets ranked past it out of the candidates: they are then counted as
     bad targets (fwd.n_bad), which raises unless allow_bad=True. The
     workspaces in `ws` are sized for P candidates and are replaced by larger
-    ones when n_cand exceeds P."""
+    ones when n_cand exceeds P.
+
+    dW [V, H] receives the table gradient: zero except the candidate rows.
+    With prev_rows (int32, possibly empty) the caller keeps dW from step to
+    step: it must be zero except at prev_rows, the previous step's
+    extra["rows"] (empty for a zeroed table), and only those rows are cleared
+    (vss_scatter_replace) instead of the whole table."""
     dev = h.device
     V, H = W.shape
     if grad_loss is None:
@@ -109,9 +116,14 @@ def sampled_step(h, W, targets, perm, P, ignore_index=-100, *, grad_loss=None,
                   allow_bad=allow_bad, stream=stream)
     b = L.vce_bwd(h, Wc, c.pos, f.lse, grad_loss, f.n_valid, Pe, 1, ignore_index, reduction,
                   ws=ws["bwd"] if fit else None, stream=stream)
-    dW = L.vss_scatter(cand, b.dW, V, dW=dW, accumulate=False, stream=stream)
+    if prev_rows is None:
+        dW = L.vss_scatter(cand, b.dW, V, dW=dW, accumulate=False, stream=stream)
+    else:
+        if dW is None:
+            raise ValueError("prev_rows needs the caller's dW table")
+        dW = L.vss_scatter_replace(prev_rows, cand, b.dW, dW, stream=stream)
     return StepOut(f, b.dh, dW, dict(cand=c.cand, pos=c.pos, n_unique=c.n_unique,
-                                     n_cand=c.n_cand, Wc=Wc, dWc=b.dW))
+                                     n_cand=c.n_cand, Wc=Wc, dWc=b.dW, rows=cand))
 
 
 def ot_h_step(ids, targets1, targets2, W, W2, V_real, num_shards, ignore_index=-100, *,
