@@ -52,6 +52,9 @@ def parse():
                     help="skip the sampled-softmax field (its own T=16384, H=1536 workload)")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens in the oracle's CPU-baseline sample")
+    ap.add_argument("--emb-only", action="store_true",
+                    help="time only the lookup and scatter-add of the tied workload (warm and "
+                         "cold) and print their rooflines; for the traffic-counter runs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one elementwise pass over 1 GiB (read 1 GiB, write 1 GiB): "
                          "the reference kernel that calibrates FETCH_SIZE / WRITE_SIZE")
@@ -191,6 +194,133 @@ def main():
         if ev is not None:
             ev[n_ev - 1].record(stream)
 
+    def emb_rooflines(ms_g_step, ms_s_step):
+        """Lookup and scatter-add of the tied table, repeated back to back
+        (warm) and after a cache-evicting read (cold), against 8 TB/s."""
+        # algorithmic HBM bytes (unique rows read once, outputs written once)
+        uniq = int(np.unique(inp.ids[(inp.ids >= 0) & (inp.ids < Vr)]).shape[0])
+        gather_bytes = uniq * H * 2 + T * H * 2 + 4 * T
+        scatter_bytes = T * H * 4 + 8 * T + 2 * uniq * H * 4
+        # The in-step spans above hold one short call each, so event overhead
+        # weighs on them; here each call is repeated back to back (same
+        # inputs, after the timed steps) and the mean per call is taken.
+        reps = 20
+
+        def per_call(fn):
+            fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        # Cold: a 512 MB read (twice the MALL) before every call evicts the
+        # table rows and dout from the caches and leaves clean lines (a write
+        # would leave dirty ones for the timed call to write back); it stays
+        # queued ahead of the call, so the host's launch latency is not inside
+        # the span.
+        flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        sink = torch.empty(1, dtype=torch.float32, device=dev)
+
+        def cold_call(fn, n_rep=10):
+            fn()
+            ts = []
+            for _ in range(n_rep):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.amax(flush, dim=0, out=sink[0])
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            return float(np.median(ts))
+
+        gather = lambda: V.vemb_fwd(ids, W, Vr, n, out=h, n_bad=nbad)
+        scatter = lambda: V.vemb_bwd(ids, dh, Vr, Vp, n, dW=dW, accumulate=True, ws=ws["emb"])
+        ms_g, ms_s = per_call(gather), per_call(scatter)
+        ms_gc, ms_sc = cold_call(gather), cold_call(scatter)
+        del flush, sink
+        occ_bytes = 2 * T * H * 2 + 4 * T  # every token's row read and written
+
+        def roof(nbytes, ms, ms_cold, ms_step_phase):
+            return {"bytes": nbytes, "ms": ms, "ms_cold": ms_cold, "ms_in_step": ms_step_phase,
+                    "GB_s": nbytes / (ms * 1e-3) / 1e9,
+                    "frac": nbytes / (ms * 1e-3) / PEAK_HBM,
+                    "frac_cold": nbytes / (ms_cold * 1e-3) / PEAK_HBM}
+
+        return {
+            "vemb_fwd": dict(roof(gather_bytes, ms_g, ms_gc, ms_g_step),
+                             bytes_per_occurrence=occ_bytes,
+                             frac_per_occurrence=occ_bytes / (ms_g * 1e-3) / PEAK_HBM),
+            "vemb_bwd": roof(scatter_bytes, ms_s, ms_sc, ms_s_step),
+        }
+
+    def copy_probe():
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        return (1 << 28) * 4
+
+    def copy_reference():
+        """Plain device copies of the lookup's output and the scatter's dout
+        sizes, timed like the calls (warm: back to back; cold: after a 512 MB
+        read), bytes counted in both directions."""
+        flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        sink = torch.empty(1, dtype=torch.float32, device=dev)
+        out = {}
+        for name, dt in (("bf16_TxH", torch.bfloat16), ("f32_TxH", torch.float32)):
+            x = torch.ones(T, H, dtype=dt, device=dev)
+            y = torch.empty_like(x)
+            fn = lambda: y.copy_(x)
+            fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(20):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            warm = e0.elapsed_time(e1) / 20
+            ts = []
+            for _ in range(10):
+                torch.amax(flush, dim=0, out=sink[0])
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            cold = float(np.median(ts))
+            nb = 2 * x.numel() * x.element_size()
+            out[name] = {"bytes": nb, "ms": warm, "ms_cold": cold,
+                         "frac": nb / (warm * 1e-3) / PEAK_HBM,
+                         "frac_cold": nb / (cold * 1e-3) / PEAK_HBM}
+            del x, y
+        del flush, sink
+        return out
+
+    if a.emb_only:
+        if not tied:
+            raise SystemExit("--emb-only times the tied workload's lookup and scatter (c4)")
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(5)
+        dh.normal_(generator=gen)
+        dW.zero_()
+        res = {"workload": f"lookup and scatter-add of the tied step: T={T}, H={H}, "
+                           f"V_real={Vr}, {n} shards, bf16 table, float32 dout",
+               "hbm_rooflines": emb_rooflines(None, None),
+               "copy_reference": copy_reference()}
+        if a.copy_probe:
+            res["copy_probe_bytes"] = copy_probe()
+        print(json.dumps(res), flush=True)
+        return
+
     log(f"[bench] warmup {a.warmup}")
     for _ in range(a.warmup):
         step(new_events())
@@ -279,67 +409,7 @@ def main():
         "phases_ms": phase,
     }
     if tied:
-        # algorithmic HBM bytes (unique rows read once, outputs written once)
-        uniq = int(np.unique(inp.ids[(inp.ids >= 0) & (inp.ids < Vr)]).shape[0])
-        gather_bytes = uniq * H * 2 + T * H * 2 + 4 * T
-        scatter_bytes = T * H * 4 + 8 * T + 2 * uniq * H * 4
-        # The in-step spans above hold one short call each, so event overhead
-        # weighs on them; here each call is repeated back to back (same
-        # inputs, after the timed steps) and the mean per call is taken.
-        reps = 20
-
-        def per_call(fn):
-            fn()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / reps
-
-        # Cold: a 512 MB read (twice the MALL) before every call evicts the
-        # table rows and dout from the caches and leaves clean lines (a write
-        # would leave dirty ones for the timed call to write back); it stays
-        # queued ahead of the call, so the host's launch latency is not inside
-        # the span.
-        flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-        sink = torch.empty(1, dtype=torch.float32, device=dev)
-
-        def cold_call(fn, n_rep=10):
-            fn()
-            ts = []
-            for _ in range(n_rep):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                torch.amax(flush, dim=0, out=sink[0])
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1))
-            return float(np.median(ts))
-
-        gather = lambda: V.vemb_fwd(ids, W, Vr, n, out=h, n_bad=nbad)
-        scatter = lambda: V.vemb_bwd(ids, dh, Vr, Vp, n, dW=dW, accumulate=True, ws=ws["emb"])
-        ms_g, ms_s = per_call(gather), per_call(scatter)
-        ms_gc, ms_sc = cold_call(gather), cold_call(scatter)
-        del flush, sink
-        occ_bytes = 2 * T * H * 2 + 4 * T  # every token's row read and written
-
-        def roof(nbytes, ms, ms_cold, ms_step_phase):
-            return {"bytes": nbytes, "ms": ms, "ms_cold": ms_cold, "ms_in_step": ms_step_phase,
-                    "GB_s": nbytes / (ms * 1e-3) / 1e9,
-                    "frac": nbytes / (ms * 1e-3) / PEAK_HBM,
-                    "frac_cold": nbytes / (ms_cold * 1e-3) / PEAK_HBM}
-
-        res["hbm_rooflines"] = {
-            "vemb_fwd": dict(roof(gather_bytes, ms_g, ms_gc, phase["vemb_fwd"]),
-                             bytes_per_occurrence=occ_bytes,
-                             frac_per_occurrence=occ_bytes / (ms_g * 1e-3) / PEAK_HBM),
-            "vemb_bwd": roof(scatter_bytes, ms_s, ms_sc, phase["vemb_bwd"]),
-        }
+        res["hbm_rooflines"] = emb_rooflines(phase["vemb_fwd"], phase["vemb_bwd"])
     # Greedy argmax over the same table and hidden rows (the decoding twin of
     # the forward: same logits GEMM, (max, lowest index) epilogue), timed on
     # its own after the step: flops per call = 2*T*H*V_real.
@@ -451,13 +521,7 @@ def main():
         log(f"[bench] n-gram embedding fwd {ms_ng * 1e3:.1f} us, bwd {ms_ngb * 1e3:.1f} us")
         del E2, E3, dE2, dE3, ws_ng, ng
     if a.copy_probe:
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        res["copy_probe_bytes"] = src.numel() * 4
-        del src, dst
+        res["copy_probe_bytes"] = copy_probe()
     del ws, dh, dW, W, h, ws_arg, out_arg
     torch.cuda.empty_cache()
     if tied and not a.no_c3:
