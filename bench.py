@@ -162,14 +162,16 @@ def sampled_field(V, dev, stream):
     n_cand = int(r5.extra["n_cand"].item())
     kept = [r5.extra["rows"]]
 
+    gl5 = torch.ones(1, **f32)
+
     def samp():
-        r = V.sampled_step(h5, W5, tg5, perm5, P5, inp5.ignore_index, ws=ws5, dW=dW5,
-                           prev_rows=kept[0], n_cand=n_cand, allow_bad=True)
+        r = V.sampled_step(h5, W5, tg5, perm5, P5, inp5.ignore_index, grad_loss=gl5, ws=ws5,
+                           dW=dW5, prev_rows=kept[0], n_cand=n_cand, allow_bad=True)
         kept[0] = r.extra["rows"]
 
     def samp_full():
-        V.sampled_step(h5, W5, tg5, perm5, P5, inp5.ignore_index, ws=ws5, dW=dW5,
-                       n_cand=n_cand, allow_bad=True)
+        V.sampled_step(h5, W5, tg5, perm5, P5, inp5.ignore_index, grad_loss=gl5, ws=ws5,
+                       dW=dW5, n_cand=n_cand, allow_bad=True)
 
     def timed(fn, reps5=5):
         e0 = torch.cuda.Event(enable_timing=True)
