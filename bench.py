@@ -639,7 +639,42 @@ def main():
             "ms": ms3, "tokens_s": T3 / (ms3 * 1e-3),
             "mfma_frac": 8.0 * T3 * H3 * V3 / (ms3 * 1e-3) / PEAK_BF16}
         log(f"[bench] CE fwd+bwd at T={T3}: {ms3:.3f} ms")
-        del h3, W3, ws3, dh3, dW3
+
+        def timed(fn, reps=3):
+            fn()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        # One rank's share of this workload if its 8 shards sat on 8 GPUs: the
+        # same calls on shard 0's 25136 rows alone (targets folded into the
+        # shard), the per-GPU kernel shape of the sharded design.
+        S3 = inp3.V_pad // n3
+        Wk = W3[:S3]
+        tgk = torch.where(tg3 >= 0, tg3 % S3, tg3)
+        wsk = V.Workspaces(dev, fwd=V.vce_fwd_workspace_bytes(T3, H3, S3, S3, 1, dt_code),
+                           bwd=V.vce_bwd_workspace_bytes(T3, H3, S3, S3, 1, dt_code))
+        dWk = torch.empty(S3, H3, **f32)
+        msk = timed(lambda: V.ce_step(h3, Wk, tgk, S3, 1, inp3.ignore_index, ws=wsk, dh=dh3,
+                                      dW=dWk, allow_bad=True))
+        res["ce_fwd_bwd_T8192_one_shard"] = {
+            "workload": f"T={T3}, H={H3}, V_real={S3} (one shard of {n3}), bf16",
+            "ms": msk, "tokens_s": T3 / (msk * 1e-3),
+            "mfma_frac": 8.0 * T3 * H3 * S3 / (msk * 1e-3) / PEAK_BF16}
+        # Context only (never on the path): torch's bf16 GEMM (the vendor
+        # library) on the forward's shapes, logits written out
+        ms_tg = timed(lambda: torch.matmul(h3, W3.t()))
+        ms_tgk = timed(lambda: torch.matmul(h3, Wk.t()))
+        res["context_torch_gemm"] = {
+            "what": "torch.matmul(h, W^T) in bf16 (hipBLASLt), the [T, V] logits written out",
+            "full_V": {"ms": ms_tg, "TFLOP_s": 2.0 * T3 * H3 * inp3.V_pad / (ms_tg * 1e-3) / 1e12},
+            "one_shard": {"ms": ms_tgk, "TFLOP_s": 2.0 * T3 * H3 * S3 / (ms_tgk * 1e-3) / 1e12}}
+        log(f"[bench] one shard {msk:.3f} ms; torch GEMM {ms_tg:.3f} / {ms_tgk:.3f} ms")
+        del h3, W3, ws3, dh3, dW3, Wk, wsk, dWk
         torch.cuda.empty_cache()
     if not a.no_sampled:
         res["sampled_softmax"] = sampled_field(V, dev, stream)

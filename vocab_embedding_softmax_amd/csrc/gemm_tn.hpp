@@ -95,9 +95,10 @@ struct GradArgs {
 struct StoreArgs {
   float* C;
   int64_t ldc;
-  float* P;             // K splits 1, 2, ...: partial planes [k_splits - 1][M][ldc], overwritten
+  float* P;             // K splits 1, 2, ...: partial planes [k_splits - 1][M][ldc]
   int64_t split_stride; // elements between partial planes
   int32_t accumulate;   // split 0: 1: C += result, 0: C = result
+  int32_t planes_held;  // planes below this index already hold a sum: added to, the others overwritten
   int64_t m_zero_from;  // rows at or past this receive 0 (or are left alone when accumulating)
 };
 
@@ -1081,12 +1082,13 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       }
     } else {  // EPI_STORE
       const StoreArgs& st = e.store;
-      // split 0 writes (or adds into) C; every later K split overwrites its
-      // own partial plane, which a fixed-order pass adds into C afterwards
+      // split 0 writes (or adds into) C; every later K split writes (or adds
+      // into, when an earlier launch left a sum there) its own partial
+      // plane, which a fixed-order pass adds into C afterwards
       const bool first = t.ks == 0;
       float* Cp = first ? st.C : st.P + (t.ks - 1) * st.split_stride;
       const int64_t ldc = st.ldc;
-      const bool accum = first && st.accumulate;
+      const bool accum = first ? st.accumulate != 0 : (t.ks - 1) < st.planes_held;
       // element (i, r) of this lane: row vb + i*32 + 8*(r/4) + r%4
       const int64_t vb = vbase + 4 * half;
       auto rel = [&](int64_t x) {

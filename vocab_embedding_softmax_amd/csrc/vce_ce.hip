@@ -539,6 +539,13 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
   const E* Wp = static_cast<const E*>(W);
   E* Gc = static_cast<E*>(p.G);
   bool dh_written = false;
+  int32_t dh_planes = 0;    // partial planes of dh that hold sums of earlier chunks
+  int64_t last_real = 0;    // the last chunk with a real class: it adds the planes into dh
+  for (int64_t c = 0; c < p.n_chunks; ++c) {
+    int64_t c0, c1;
+    p.chunk(c, c0, c1);
+    if (c0 < V_real) last_real = c;
+  }
   for (int64_t c = 0; c < p.n_chunks; ++c) {
     int64_t c0, c1;
     p.chunk(c, c0, c1);
@@ -612,9 +619,13 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       e.store.P = p.Pdh;
       e.store.split_stride = T * H;
       e.store.accumulate = (dh_written || acc_dh) ? 1 : 0;
+      e.store.planes_held = dh_planes;  // later chunks add into the planes of earlier ones
       e.store.m_zero_from = T;
       if ((err = launch_gemm<E, EPI_STORE, false, true>(g, e, s)) != hipSuccess) return err;
-      if ((err = split_add(dh, p.Pdh, ks, T, T)) != hipSuccess) return err;
+      dh_planes = max(dh_planes, ks - 1);
+      // the planes are added into dh once, after the last real chunk's dh
+      if (c == last_real && (err = split_add(dh, p.Pdh, dh_planes + 1, T, T)) != hipSuccess)
+        return err;
       dh_written = true;
     }
     if ((err = mark()) != hipSuccess) return err;
