@@ -113,23 +113,30 @@ ArgPlan plan_argmax(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t
   return p;
 }
 
-int32_t k_splits_for(int64_t tiles, int64_t K) {
+int32_t k_splits_for(int64_t tiles, int64_t K, int64_t out_elems) {
   constexpr int64_t kCUs = 256;
   constexpr int32_t kMaxSplit = 8;
   if (tiles <= 0) return 1;
-  auto busy = [&](int64_t s) {  // fraction of CU-rounds that hold a tile
-    const int64_t t = tiles * s;
-    return static_cast<double>(t) / static_cast<double>(cdiv(t, kCUs) * kCUs);
+  // Estimated time in units of one 64-K slice of one tile on one CU
+  // (≈ 1.65 µs at the GEMMs' rate): rounds of tiles over the CUs, each tile
+  // its share of K plus ≈ 4 slices of fixed cost (prologue, epilogue); a
+  // split also writes s - 1 float32 planes and a pass reads them and the
+  // output and writes the output (≈ 5 TB/s, i.e. ≈ 8.25 MB per slice time).
+  auto cost = [&](int64_t s) {
+    const double rounds = static_cast<double>(cdiv(tiles * s, kCUs));
+    const double gemm = rounds * static_cast<double>(cdiv(K, s * 64) + 4);
+    if (s == 1) return gemm;
+    const double bytes = static_cast<double>(out_elems) * 4.0 * static_cast<double>(2 * (s - 1) + 2);
+    return gemm + bytes / 8.25e6 + 3.0;
   };
-  if (busy(1) >= 0.85) return 1;
   int32_t best = 1;
-  double best_busy = busy(1);
+  double best_cost = cost(1);
   for (int32_t s = 2; s <= kMaxSplit; ++s) {
     if (cdiv(K, s) < 1024) break;
-    const double b = busy(s);
-    if (b > best_busy + 1e-9) {
+    const double c = cost(s);
+    if (c < best_cost * 0.98) {  // a split must save at least 2 %
       best = s;
-      best_busy = b;
+      best_cost = c;
     }
   }
   return best;
@@ -165,8 +172,8 @@ BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
   // K splits: dh has cdiv(T, 256) x cdiv(H, 256) tiles over the chunk's
   // classes, dW cdiv(chunk, 256) x cdiv(H, 256) tiles over the tokens
   const int64_t tiles_h = cdiv(H, kTileN);
-  p.split_dh = k_splits_for(cdiv(T, kTileM) * tiles_h, p.chunk_rows);
-  p.split_dw = k_splits_for(cdiv(p.chunk_rows, kTileM) * tiles_h, T);
+  p.split_dh = k_splits_for(cdiv(T, kTileM) * tiles_h, p.chunk_rows, T * H);
+  p.split_dw = k_splits_for(cdiv(p.chunk_rows, kTileM) * tiles_h, T, p.chunk_rows * H);
   Carve c(ws);
   p.G = c.take<char>(static_cast<size_t>(T * p.ldC) * esize);
   p.Pdh = c.take<float>(static_cast<size_t>((p.split_dh - 1) * T * H));
@@ -608,7 +615,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       g.m_load_end = T;
       g.n_total = H;
       g.tiles_n = static_cast<int32_t>(cdiv(H, kTileN));
-      const int32_t ks = min(k_splits_for(cdiv(T, kTileM) * g.tiles_n, kreal), p.split_dh);
+      const int32_t ks = min(k_splits_for(cdiv(T, kTileM) * g.tiles_n, kreal, T * H), p.split_dh);
       g.k_splits = ks;
       g.k_total = kreal;
       g.k_per_split = round_up(cdiv(kreal, ks), kPadK);
@@ -642,7 +649,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       g.m_load_end = Vc;
       g.n_total = H;
       g.tiles_n = static_cast<int32_t>(cdiv(H, kTileN));
-      const int32_t ks = min(k_splits_for(cdiv(Vc, kTileM) * g.tiles_n, T), p.split_dw);
+      const int32_t ks = min(k_splits_for(cdiv(Vc, kTileM) * g.tiles_n, T, Vc * H), p.split_dw);
       g.k_splits = ks;
       g.k_total = T;
       g.k_per_split = round_up(cdiv(T, ks), kPadK);

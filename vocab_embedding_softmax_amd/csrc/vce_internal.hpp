@@ -160,11 +160,11 @@ struct BwdPlan {
     c1 = (k + 1) * S < c0 + piece_rows ? (k + 1) * S : c0 + piece_rows;
   }
 };
-// K splits for a GEMM of `tiles` output tiles over K positions: 1 while one
-// pass of tiles keeps at least 85 % of the GPU's 256 CUs busy through its
-// rounds, else the count in 2..8 (each split >= 1024 K positions) that does
-// best, the smallest on ties.
-int32_t k_splits_for(int64_t tiles, int64_t K);
+// K splits for a GEMM of `tiles` output tiles (out_elems float32 outputs)
+// over K positions: the count in 1..8 (each split >= 1024 K positions) with
+// the least estimated time, rounds of tiles over the GPU's 256 CUs plus the
+// partial planes' writes and their addition; a split must save 2 %.
+int32_t k_splits_for(int64_t tiles, int64_t K, int64_t out_elems);
 BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, size_t esize,
                  void* ws);
 
