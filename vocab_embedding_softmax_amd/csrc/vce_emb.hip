@@ -17,9 +17,9 @@
 //      and writes its row of dW once: an ID with fewer than kSegLong tokens
 //      belongs to the chunk of kSegC sorted positions where its run starts,
 //      and that chunk's wave sums it in sorted (= token) order; an ID with
-//      more is split by columns over many workgroups, each of which sums its
-//      column slice over the whole run in a fixed order. No partial sums leave
-//      a workgroup.
+//      kSegLong tokens or more is split by columns over many workgroups, each
+//      of which sums its column slice over the whole run in a fixed order. No
+//      partial sums leave a workgroup.
 #include "vce_device.hpp"
 #include "vce_internal.hpp"
 
