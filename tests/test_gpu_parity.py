@@ -104,6 +104,11 @@ RAGGED = [
     (513, 136, 2500, 2560, 10, "bf16"),
     (64, 64, 1000, 1024, 4, "bf16"),
     (40, 1024, 300, 300, 3, "f32"),
+    # dh's K split in four in the first vocabulary chunk, not at all in the
+    # second (few real classes): the second chunk's result lands in dh while
+    # the first chunk's planes wait for the one addition after it
+    (512, 256, 4200, 8192, 2, "bf16"),
+    (300, 128, 6000, 8192, 2, "f32"),
 ]
 
 
