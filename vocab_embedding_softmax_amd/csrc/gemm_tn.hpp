@@ -1029,28 +1029,24 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
             // the 32-row block lies inside the tile for both lanes of the pair
             if (gr.vec_store && tin && i * 32 + 32 <= end_l + 4 * half) {
               // lane pairs (l, l^32) trade quarter-blocks so that each lane
-              // holds 8 consecutive rows twice: 16-byte stores
+              // holds 8 consecutive rows twice: 16-byte stores. A half-swap
+              // (v_permlane32_swap: lanes 32-63 of its first operand trade
+              // places with lanes 0-31 of its second) of quarter-blocks 0 and
+              // 1 leaves {0 of l, 0 of l^32} in the lower lanes and {1 of l^32,
+              // 1 of l} in the upper ones: rows 8*half .. 8*half+7 of the
+              // 16-row group in both; likewise 2 and 3.
               u32x2 P[4];
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
                 P[q].x = pack_bf16x2(gv[4 * q], gv[4 * q + 1]);
                 P[q].y = pack_bf16x2(gv[4 * q + 2], gv[4 * q + 3]);
               }
-              const u32x2 sa = half ? P[0] : P[1];
-              const u32x2 sb = half ? P[2] : P[3];
-              u32x2 ra, rb;
-              ra.x = __shfl_xor(sa.x, 32);
-              ra.y = __shfl_xor(sa.y, 32);
-              rb.x = __shfl_xor(sb.x, 32);
-              rb.y = __shfl_xor(sb.y, 32);
-              u32x4 p0, p1;
-              if (half) {
-                p0 = u32x4{ra.x, ra.y, P[1].x, P[1].y};
-                p1 = u32x4{rb.x, rb.y, P[3].x, P[3].y};
-              } else {
-                p0 = u32x4{P[0].x, P[0].y, ra.x, ra.y};
-                p1 = u32x4{P[2].x, P[2].y, rb.x, rb.y};
-              }
+              const auto s0x = __builtin_amdgcn_permlane32_swap(P[0].x, P[1].x, false, false);
+              const auto s0y = __builtin_amdgcn_permlane32_swap(P[0].y, P[1].y, false, false);
+              const auto s1x = __builtin_amdgcn_permlane32_swap(P[2].x, P[3].x, false, false);
+              const auto s1y = __builtin_amdgcn_permlane32_swap(P[2].y, P[3].y, false, false);
+              const u32x4 p0 = {s0x[0], s0y[0], s0x[1], s0y[1]};
+              const u32x4 p1 = {s1x[0], s1y[0], s1x[1], s1y[1]};
               E* base = Gp + tt * gr.ldG + vbase + i * 32 + 8 * half;
               *reinterpret_cast<u32x4*>(base) = p0;
               *reinterpret_cast<u32x4*>(base + 16) = p1;
