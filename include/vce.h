@@ -221,8 +221,10 @@ vce_status vemb_fwd(const int32_t* ids, const void* W, int64_t T, int64_t H,
  * [VS] paragraph 2: repeated occurrences of one token add their gradients   *
  * into the one row that owns it; with a tied table every contribution lands *
  * in the same tensor. dW[v,:] (+)= sum of dout[t,:] over t with ids[t] == v, *
- * for v < V_real, summed in float32 in increasing t (deterministic: one     *
- * writer per row, fixed order). IDs outside [0, V_real) are dropped.        *
+ * for v < V_real, summed in float32 in a fixed order (deterministic, one   *
+ * writer per row): in increasing t, or, for an ID with 64 or more tokens,   *
+ * 16 running sums over every 16th token added in order. IDs outside         *
+ * [0, V_real) are dropped.                                                  *
  * accumulate = 1: add into the touched rows only (e.g. after vce_bwd wrote  *
  * the LM-head part of a tied dW); accumulate = 0: the whole table is        *
  * overwritten (untouched rows become 0).                                    *

@@ -168,11 +168,11 @@ int32_t k_splits_for(int64_t tiles, int64_t K, int64_t out_elems);
 BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, size_t esize,
                  void* ws);
 
-// Embedding backward plan: a stable sort of the tokens by ID, then segment
-// sums over fixed-size chunks of the sorted list and a fix-up for the IDs
-// whose tokens span several chunks. Two ways to sort:
-//   one-workgroup: up to 16384 tokens whose (ID, token) pairs pack into 32
-//     bits are radix-sorted in one workgroup's LDS (one launch);
+// Embedding backward plan: a stable sort of the tokens by ID, then one launch
+// of segment sums (short IDs by the chunk of the sorted list where their run
+// starts, long IDs by column slices; see vce_emb.hip). Two ways to sort:
+//   runs: up to 32768 tokens, runs of 1024 radix-sorted in LDS, then placed
+//     by their ranks in every run (two launches);
 //   general: block-local LDS sorts + per-block counts + scans (any size).
 struct EmbBwdPlan {
   bool runs;           // sorted runs + merge (T <= 32 runs of 1024 tokens), else general
