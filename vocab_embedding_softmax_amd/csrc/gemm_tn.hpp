@@ -11,7 +11,10 @@
 //             holding it) over the tile's real vocabulary rows
 //
 // Workgroup: WAVES_M x WAVES_N waves over a BM x BN tile; each wave owns a
-// (BM/WAVES_M) x (BN/WAVES_N) sub-tile made of 32 x 32 MFMA blocks. K
+// (BM/WAVES_M) x (BN/WAVES_N) sub-tile made of 32 x 32 MFMA blocks (the bf16
+// logit GEMMs compute each as four 16x16x32 blocks and rearrange the
+// accumulators into the 32x32 layout before the epilogue; their sums have
+// come out bit-identical to the 32x32x16 ones, in less time per flop). K
 // advances in slices of RB bytes per operand position (RB = 64: 32 bf16 or
 // 16 float), staged in LDS by direct global->LDS loads
 // (global_load_lds_dwordx4), NS stages deep; both layouts fill one stage with
@@ -48,6 +51,10 @@
 // A second copy of the K loop for whole tiles, free of per-load tests
 #ifndef VCE_KLOOP_SPLIT
 #define VCE_KLOOP_SPLIT 1
+#endif
+// bf16 logit GEMMs (forward, G, argmax) on 16x16x32 MFMA blocks
+#ifndef VCE_MFMA16
+#define VCE_MFMA16 1
 #endif
 
 namespace vce {
@@ -153,6 +160,40 @@ template <>
 __device__ __forceinline__ void mma_chunk<uint16_t>(f32x16& acc, const u32x4& a, const u32x4& b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+// bf16 on 16x16x32 blocks (16x16 layout: lane l holds column l % 16, rows
+// 4 (l / 16) .. +3 of the block)
+__device__ __forceinline__ void mma16(f32x4& c, const u32x4& a, const u32x4& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                              __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Four 16x16 blocks b[ra][cb] (rows 16 ra + .., columns 16 cb + ..) -> one
+// 32 x 32 block in the 32x32 layout (lane l: column l % 32, register 4q + r:
+// row 8q + 4 (l / 32) + r). That element sits in block (q / 2, l / 16 % 2) at
+// row 8 (q % 2) + 4 (l / 32) + r, i.e. in register r of lane
+// l % 16 + 16 (2 (q % 2) + l / 32). For fixed ra and r, with P, Q the
+// registers of blocks (ra, 0) and (ra, 1) and rows counted in 16-lane groups,
+// the outputs q = 2 ra and 2 ra + 1 are [P0 Q0 P1 Q1] and [P2 Q2 P3 Q3]: a
+// 16-lane swap (odd groups of the first operand with even groups of the
+// second: [P0 Q0 P2 Q2], [P1 Q1 P3 Q3]) followed by a 32-lane swap (upper half
+// of the first with lower half of the second).
+__device__ __forceinline__ void rows32_layout(f32x16& out, const f32x4& b00, const f32x4& b01,
+                                              const f32x4& b10, const f32x4& b11) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const auto p0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(b00[r]), __float_as_uint(b01[r]),
+                                                     false, false);
+    const auto q0 = __builtin_amdgcn_permlane32_swap(p0[0], p0[1], false, false);
+    out[r] = __uint_as_float(q0[0]);
+    out[4 + r] = __uint_as_float(q0[1]);
+    const auto p1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(b10[r]), __float_as_uint(b11[r]),
+                                                     false, false);
+    const auto q1 = __builtin_amdgcn_permlane32_swap(p1[0], p1[1], false, false);
+    out[8 + r] = __uint_as_float(q1[0]);
+    out[12 + r] = __uint_as_float(q1[1]);
+  }
 }
 
 // float32: the lane's 4 floats are 4 K positions; one 32x32x2 MFMA per
@@ -613,13 +654,38 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
 
   f32x16 acc[MI][NI];
   u32x4 fa[2][MI], fb[2][NI];
+
+  // 16x16x32 form (bf16 logit GEMMs): A in groups of 16 rows, B in groups of
+  // 16 columns, K = 32 per sub-step (two per 128-byte slice). A fragment:
+  // row (lane % 16) of its group, logical 16-byte chunk 4 s + lane / 16 of
+  // the slice (the stage permutation depends on the row's position in its 16).
+  constexpr bool M16 = VCE_MFMA16 && sizeof(E) == 2 && RB == 128 && !AKM && !BKM && !SPREAD;
+  constexpr int MA = 2 * MI, NB = 2 * NI, SS16 = RB / 64;
+  const uint32_t fa16 = static_cast<uint32_t>((wm * WM + (lane & 15)) * RB);
+  const uint32_t fb16 = static_cast<uint32_t>(A_BYTES + (wn * WN + (lane & 15)) * RB);
+  const int sw16 = ((lane & 15) >> 1) & 7;
+  auto frag16 = [&](const char* st, uint32_t f0, int grp, int sub) {
+    const int ch = ((4 * sub + (lane >> 4)) ^ sw16) * 16;
+    return *reinterpret_cast<const u32x4*>(st + f0 + grp * 16 * RB + ch);
+  };
+  u32x4 Ar[4], B16[M16 ? NB : 1];
+  f32x4 acc16[M16 ? MA : 1][M16 ? NB : 1];
+  static_assert(!M16 || (SS16 == 2 && MA % 4 == 0 && LOADS <= 2 * NB), "16x16x32 slice geometry");
+
   while (true) {
+    if constexpr (M16) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+      for (int a = 0; a < MA; ++a)
 #pragma unroll
-      for (int j = 0; j < NI; ++j)
+        for (int b = 0; b < NB; ++b) acc16[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    }
     auto mfmas = [&](const u32x4 (&a)[MI], const u32x4 (&b)[NI]) {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
@@ -748,6 +814,97 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       }
     };
 
+    // The same pipeline on 16x16x32 blocks. A sub-step runs A group by A
+    // group; the A fragments live in a ring of four, group a+2's read before
+    // group a's MFMAs (from this sub-step's source, or from the next
+    // sub-step's once a+2 passes the last group), and each B fragment is read
+    // again for the next sub-step right after its last MFMA (in the last
+    // group). In a slice's second sub-step the reads of the next slice start
+    // at group MA-2, so slice kt+1's wait and barrier sit there (mid), and the
+    // copies of slice kt+NS go out among the last two groups' MFMAs (dma).
+    auto sub16 = [&](const char* stc, int sc, const char* stx, int sx, auto next, auto mid,
+                     auto dma) {
+      constexpr bool NX = decltype(next)::value;
+      static_for<0, MA>([&](auto aa) {
+        constexpr int a = decltype(aa)::value;
+        if constexpr (a == MA - 2) mid();
+        if constexpr (a + 2 < MA)
+          Ar[(a + 2) % 4] = frag16(stc, fa16, a + 2, sc);
+        else if constexpr (NX)
+          Ar[(a + 2) % 4] = frag16(stx, fa16, a + 2 - MA, sx);
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, NB>([&](auto bb) {
+          constexpr int b = decltype(bb)::value;
+          dma(std::integral_constant<int, a * NB + b>{});
+          mma16(acc16[a][b], Ar[a % 4], B16[b]);
+          if constexpr (NX && a == MA - 1) B16[b] = frag16(stx, fb16, b, sx);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      });
+    };
+    auto read16 = [&](const char* st) {
+      Ar[0] = frag16(st, fa16, 0, 0);
+      Ar[1] = frag16(st, fa16, 1, 0);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) B16[b] = frag16(st, fb16, b, 0);
+    };
+    auto kstep16 = [&](int kt, auto wait_all, auto issue_next, auto last, auto all_fast) {
+      constexpr bool WAIT_ALL = decltype(wait_all)::value;
+      constexpr bool ISSUE = decltype(issue_next)::value;
+      constexpr bool LAST = decltype(last)::value;
+      constexpr bool AF = decltype(all_fast)::value;
+      const char* st = smem + (kt % NS) * STAGE;
+      auto none = [] {};
+      auto nodma = [](auto) {};
+      // first sub-step; its last groups read the second's first fragments
+      sub16(st, 0, st, 1, std::true_type{}, none, nodma);
+      if constexpr (!LAST) {
+        const char* stn = smem + ((kt + 1) % NS) * STAGE;
+        const char *pa = nullptr, *pb = nullptr;
+        uint32_t stl = 0;
+        int64_t kleft = 0;
+        bool fast_a = true, fast_b = true;
+        if constexpr (ISSUE) {
+          const int kn = kt + NS;
+          const int64_t kofs = static_cast<int64_t>(kn) * BK;
+          stl = smem_lds + (kn % NS) * STAGE;
+          kleft = klen - kofs;
+          pa = Ab + kofs * ES;
+          pb = Bb + kofs * ES;
+          fast_a = AF || sa.fast(kleft);
+          fast_b = AF || sb.fast(kleft);
+        }
+        auto mid = [&] {
+          // this wave's reads of slice kt are complete, its part of slice kt+1 is in
+          __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+          if constexpr (WAIT_ALL)
+            wait_vmcnt<0>();
+          else
+            wait_vmcnt<(NS - 2) * LOADS>();
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::"r"(smem) : "memory");
+        };
+        auto dma = [&](auto slot) {
+          constexpr int k = decltype(slot)::value - (MA - 2) * NB;
+          if constexpr (ISSUE && k >= 0 && k < LOADS) {
+            if constexpr (k < SA::Q)
+              sa.issue_q(k, stl, pa, kleft, wave, fast_a);
+            else
+              sb.issue_q(k - SA::Q, stl + A_BYTES, pb, kleft, wave, fast_b);
+          }
+        };
+        sub16(st, 1, stn, 0, std::true_type{}, mid, dma);
+      } else {
+        sub16(st, 1, st, 0, std::false_type{}, none, nodma);
+      }
+    };
+    auto step = [&](int kt, auto wait_all, auto issue_next, auto last, auto all_fast) {
+      if constexpr (M16)
+        kstep16(kt, wait_all, issue_next, last, all_fast);
+      else
+        kstep(kt, wait_all, issue_next, last, all_fast);
+    };
+
     if (nk > 0) {
       // slice 0 in; queue slice NS-1; first fragments
       if (nk >= NS - 1)
@@ -759,7 +916,10 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
       if (!SPREAD && NS - 1 < nk) issue(NS - 1);
       load_epi();
       asm volatile("" ::"r"(smem) : "memory");
-      read_frags(smem, 0, fa[0], fb[0]);
+      if constexpr (M16)
+        read16(smem);
+      else
+        read_frags(smem, 0, fa[0], fb[0]);
       using F_ = std::false_type;
       using T_ = std::true_type;
       auto kloop = [&](auto af) {
@@ -767,17 +927,17 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
         if constexpr (SPREAD) {
           // kstep(kt) queues slice kt+NS-1; at its barrier the slices after
           // kt+1 that are in flight are kt+2 .. kt+NS-1
-          for (; kt + NS - 1 < nk; ++kt) kstep(kt, F_{}, T_{}, F_{}, af);
-          for (; kt + 1 < nk; ++kt) kstep(kt, T_{}, F_{}, F_{}, af);
+          for (; kt + NS - 1 < nk; ++kt) step(kt, F_{}, T_{}, F_{}, af);
+          for (; kt + 1 < nk; ++kt) step(kt, T_{}, F_{}, F_{}, af);
         } else {
-          for (; kt + NS < nk; ++kt) kstep(kt, F_{}, T_{}, F_{}, af);
+          for (; kt + NS < nk; ++kt) step(kt, F_{}, T_{}, F_{}, af);
           if (kt + NS == nk && kt + 1 < nk) {
-            kstep(kt, F_{}, F_{}, F_{}, af);
+            step(kt, F_{}, F_{}, F_{}, af);
             ++kt;
           }
-          for (; kt + 1 < nk; ++kt) kstep(kt, T_{}, F_{}, F_{}, af);
+          for (; kt + 1 < nk; ++kt) step(kt, T_{}, F_{}, F_{}, af);
         }
-        kstep(kt, T_{}, F_{}, T_{}, af);
+        step(kt, T_{}, F_{}, T_{}, af);
       };
 #if VCE_KLOOP_SPLIT
       // whole tiles (the common case) run a K loop without per-load tests
@@ -795,6 +955,14 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
     // them); saying so explicitly lets the epilogue use its inputs without a
     // wait that would also cover the next tile's prefetch.
     wait_vmcnt<0>();
+    if constexpr (M16) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          rows32_layout(acc[i][j], acc16[2 * i][2 * j], acc16[2 * i][2 * j + 1],
+                        acc16[2 * i + 1][2 * j], acc16[2 * i + 1][2 * j + 1]);
+    }
 
     // every wave is done with the stage buffers: start the next tile's loads
     lds_barrier();
@@ -808,6 +976,15 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
     }
 
     // ---------------------------------------------------------------- epilogue
+    // Outside the forward, the lane indices are taken afresh here, opaque to
+    // the optimiser, so that nothing the epilogue derives from them is
+    // computed at the top of the kernel and kept live (often in 64-bit form)
+    // across the K loop (the forward's epilogue allocates better without).
+    int lane_ep = lane;
+    if constexpr (MODE != EPI_FWD) asm volatile("" : "+v"(lane_ep));
+    {
+    const int lane = lane_ep;
+    const int half = lane >> 5, l32 = lane & 31;
     // Row of accumulator element r of block i (relative to the wave tile):
     //   i*32 + 8*(r/4) + 4*half + r%4 ;  its column: j*32 + l32.
     const int64_t vbase = t.m0 + wm * WM;
@@ -1113,6 +1290,7 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
               *dst = v;
           }
       }
+    }
     }
 
     if (!has_next) break;
