@@ -11,10 +11,11 @@
 //             holding it) over the tile's real vocabulary rows
 //
 // Workgroup: WAVES_M x WAVES_N waves over a BM x BN tile; each wave owns a
-// (BM/WAVES_M) x (BN/WAVES_N) sub-tile made of 32 x 32 MFMA blocks (the bf16
-// logit GEMMs compute each as four 16x16x32 blocks and rearrange the
-// accumulators into the 32x32 layout before the epilogue; their sums have
-// come out bit-identical to the 32x32x16 ones, in less time per flop). K
+// (BM/WAVES_M) x (BN/WAVES_N) sub-tile made of 32 x 32 MFMA blocks (in bf16
+// with two 128-byte stages, each is computed as four 16x16x32 blocks whose
+// accumulators are rearranged into the 32x32 layout before the epilogue;
+// their sums have come out bit-identical to the 32x32x16 ones, in less time
+// per flop). K
 // advances in slices of RB bytes per operand position (RB = 64: 32 bf16 or
 // 16 float), staged in LDS by direct global->LDS loads
 // (global_load_lds_dwordx4), NS stages deep; both layouts fill one stage with
@@ -31,8 +32,9 @@
 // 8 bytes that lane 4e + i/4 addressed; lane 4e + b of the group addresses
 // row k + e at positions 4b..4b+3, so lane i receives four consecutive K
 // values of position i. The 64-byte blocks of each 256-byte window of a row
-// are permuted by (k & 3), so the four rows one 32-lane pass reads fall on
-// different banks. float fragments are four ds_read_b32; their rows k and
+// are permuted by (k & 3), and its 32-byte halves by bit 3 of k, so the rows
+// one 32-lane pass reads (four, or two sets of four 8 apart in the 16x16x32
+// form) fall on different banks. float fragments are four ds_read_b32; their rows k and
 // k + 4 are separated by permuting 128-byte halves by ((k >> 2) & 1).
 //
 // Operand positions past the valid range read a clamped (valid) position and
@@ -332,6 +334,19 @@ struct StageKC {
     const int ch = ((2 * s + (lane >> 5)) ^ swz(lane & 31)) * 16;
     return *reinterpret_cast<const u32x4*>(st + frag0 + block * 32 * RB + ch);
   }
+
+  // 16x16x32 fragment (RB = 128): row (wbase + 16 grp + lane % 16), logical
+  // chunk 4 sub + lane / 16 (a group starts at a multiple of 16 rows)
+  uint32_t f16;  // this lane's row offset for group 0
+  int32_t s16;   // its row's chunk permutation
+  __device__ __forceinline__ void init16(int wbase, int lane) {
+    f16 = static_cast<uint32_t>((wbase + (lane & 15)) * RB);
+    s16 = swz(lane & 15);
+  }
+  __device__ __forceinline__ u32x4 frag16(const char* st, int grp, int sub, int lane) const {
+    const int ch = ((4 * sub + (lane >> 4)) ^ s16) * 16;
+    return *reinterpret_cast<const u32x4*>(st + f16 + grp * 16 * RB + ch);
+  }
 };
 
 // K-major operand; a slice holds RB / sizeof(E) K rows
@@ -350,7 +365,7 @@ struct StageKM {
   // the chunk permutation repeats every 4 (bf16) / 8 (float) rows: when the
   // rows of consecutive loads step by a multiple of that, a lane's chunk is
   // the same for every load
-  static constexpr bool kQIndep = (RPL * NW) % (ES == 2 ? 4 : 8) == 0;
+  static constexpr bool kQIndep = (RPL * NW) % (ES == 2 ? 16 : 8) == 0;
   uint32_t off0;     // this lane's byte offset for load 0 (chunk included)
   int32_t lk;        // this lane's K row (within the slice) for load 0
   int32_t pch;       // this lane's chunk slot in its LDS row
@@ -362,7 +377,7 @@ struct StageKM {
 
   // permutation of the chunks of K row k
   __device__ __forceinline__ static int swz(int k) {
-    return ES == 2 ? ((k & 3) << 2) : (((k >> 2) & 1) << 3);
+    return ES == 2 ? (((k & 3) << 2) ^ (((k >> 3) & 1) << 1)) : (((k >> 2) & 1) << 3);
   }
 
   template <int NB>
@@ -445,6 +460,35 @@ struct StageKM {
       v.z = *(const lds_u32*)(p + (8 * s + 2) * RBT);
       v.w = *(const lds_u32*)(p + (8 * s + 3) * RBT);
       return v;
+    }
+  }
+
+  // 16x16x32 fragment (bf16): position wbase + 16 grp + lane % 16, K rows
+  // 32 sub + 8 (lane / 16) + 0..7 from two transposing reads of four rows.
+  // Lane 4e + b of each 16-lane group addresses row +e, positions 4b..4b+3;
+  // a 32-lane pass covers rows 8q + 0..3 of two groups q, which the
+  // permutation's bit from row bit 3 puts on other banks.
+  uint32_t f16;  // this lane's row offset (read 0, sub-step 0) plus its element offset
+  int32_t c16;   // its unpermuted chunk for group 0
+  int32_t s16;   // its rows' chunk permutation
+  __device__ __forceinline__ void init16(int wbase, int lane) {
+    const int i = lane & 15, q = lane >> 4;
+    const int krow = 8 * q + (i >> 2);
+    const int pos = wbase + 4 * (i & 3);
+    f16 = static_cast<uint32_t>(krow * RBT + (pos % EPC) * ES);
+    c16 = pos / EPC;
+    s16 = swz(krow);
+  }
+  __device__ __forceinline__ u32x4 frag16(const char* st, int grp, int sub, int lane) const {
+    (void)lane;
+    if constexpr (ES == 2) {
+      const char* p = st + f16 + 32 * sub * RBT + ((c16 + 2 * grp) ^ s16) * 16;
+      const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+      const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * RBT));
+      const u32x2 a = __builtin_bit_cast(u32x2, r0), b = __builtin_bit_cast(u32x2, r1);
+      return u32x4{a.x, a.y, b.x, b.y};
+    } else {
+      return u32x4{0u, 0u, 0u, 0u};  // the 16x16x32 form is bf16 only
     }
   }
 };
@@ -655,19 +699,16 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
   f32x16 acc[MI][NI];
   u32x4 fa[2][MI], fb[2][NI];
 
-  // 16x16x32 form (bf16 logit GEMMs): A in groups of 16 rows, B in groups of
-  // 16 columns, K = 32 per sub-step (two per 128-byte slice). A fragment:
-  // row (lane % 16) of its group, logical 16-byte chunk 4 s + lane / 16 of
-  // the slice (the stage permutation depends on the row's position in its 16).
-  constexpr bool M16 = VCE_MFMA16 && sizeof(E) == 2 && RB == 128 && !AKM && !BKM && !SPREAD;
+  // 16x16x32 form (bf16, two 128-byte stages): A in groups of 16 rows, B in
+  // groups of 16 columns, K = 32 per sub-step (two per slice); a lane's
+  // fragment is position lane % 16 of its group, K values 8 (lane / 16) ..+7
+  // of the sub-step (the stagers' frag16).
+  constexpr bool M16 = VCE_MFMA16 && sizeof(E) == 2 && RB == 128 && NS == 2 && !SPREAD;
   constexpr int MA = 2 * MI, NB = 2 * NI, SS16 = RB / 64;
-  const uint32_t fa16 = static_cast<uint32_t>((wm * WM + (lane & 15)) * RB);
-  const uint32_t fb16 = static_cast<uint32_t>(A_BYTES + (wn * WN + (lane & 15)) * RB);
-  const int sw16 = ((lane & 15) >> 1) & 7;
-  auto frag16 = [&](const char* st, uint32_t f0, int grp, int sub) {
-    const int ch = ((4 * sub + (lane >> 4)) ^ sw16) * 16;
-    return *reinterpret_cast<const u32x4*>(st + f0 + grp * 16 * RB + ch);
-  };
+  if constexpr (M16) {
+    sa.init16(wm * WM, lane);
+    sb.init16(wn * WN, lane);
+  }
   u32x4 Ar[4], B16[M16 ? NB : 1];
   f32x4 acc16[M16 ? MA : 1][M16 ? NB : 1];
   static_assert(!M16 || (SS16 == 2 && MA % 4 == 0 && LOADS <= 2 * NB), "16x16x32 slice geometry");
@@ -829,24 +870,24 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
         constexpr int a = decltype(aa)::value;
         if constexpr (a == MA - 2) mid();
         if constexpr (a + 2 < MA)
-          Ar[(a + 2) % 4] = frag16(stc, fa16, a + 2, sc);
+          Ar[(a + 2) % 4] = sa.frag16(stc, a + 2, sc, lane);
         else if constexpr (NX)
-          Ar[(a + 2) % 4] = frag16(stx, fa16, a + 2 - MA, sx);
+          Ar[(a + 2) % 4] = sa.frag16(stx, a + 2 - MA, sx, lane);
         __builtin_amdgcn_sched_barrier(0);
         static_for<0, NB>([&](auto bb) {
           constexpr int b = decltype(bb)::value;
           dma(std::integral_constant<int, a * NB + b>{});
           mma16(acc16[a][b], Ar[a % 4], B16[b]);
-          if constexpr (NX && a == MA - 1) B16[b] = frag16(stx, fb16, b, sx);
+          if constexpr (NX && a == MA - 1) B16[b] = sb.frag16(stx + A_BYTES, b, sx, lane);
           __builtin_amdgcn_sched_barrier(0);
         });
       });
     };
     auto read16 = [&](const char* st) {
-      Ar[0] = frag16(st, fa16, 0, 0);
-      Ar[1] = frag16(st, fa16, 1, 0);
+      Ar[0] = sa.frag16(st, 0, 0, lane);
+      Ar[1] = sa.frag16(st, 1, 0, lane);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) B16[b] = frag16(st, fb16, b, 0);
+      for (int b = 0; b < NB; ++b) B16[b] = sb.frag16(st + A_BYTES, b, 0, lane);
     };
     auto kstep16 = [&](int kt, auto wait_all, auto issue_next, auto last, auto all_fast) {
       constexpr bool WAIT_ALL = decltype(wait_all)::value;
@@ -869,8 +910,8 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
           const int64_t kofs = static_cast<int64_t>(kn) * BK;
           stl = smem_lds + (kn % NS) * STAGE;
           kleft = klen - kofs;
-          pa = Ab + kofs * ES;
-          pb = Bb + kofs * ES;
+          pa = Ab + kofs * (AKM ? g.lda : 1) * ES;
+          pb = Bb + kofs * (BKM ? g.ldb : 1) * ES;
           fast_a = AF || sa.fast(kleft);
           fast_b = AF || sb.fast(kleft);
         }

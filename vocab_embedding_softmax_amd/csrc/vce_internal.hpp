@@ -31,9 +31,9 @@ constexpr int kOcc = VCE_OCC;       // workgroups resident per CU (waves per SIM
 #define VCE_CHUNK_ROWS 131072
 #endif
 // K staging per GEMM (bytes per position per K slice, LDS stages, spread
-// issue of a slice's loads). Measured on the tied-step shapes: the forward
-// and G GEMMs run fastest with two 128-byte stages, dh and dW with four
-// 64-byte stages (dh with its loads spread over the slice before).
+// issue of a slice's loads). Two 128-byte stages everywhere: the bf16 form
+// on 16x16x32 blocks needs them, and with 32x32x16 blocks dh and dW ran the
+// same with them as with four 64-byte stages.
 #ifndef VCE_FWD_RB
 #define VCE_FWD_RB 128
 #endif
@@ -53,19 +53,19 @@ constexpr int kOcc = VCE_OCC;       // workgroups resident per CU (waves per SIM
 #define VCE_GRAD_SPREAD 0
 #endif
 #ifndef VCE_DH_RB
-#define VCE_DH_RB 64
+#define VCE_DH_RB 128
 #endif
 #ifndef VCE_DH_NS
-#define VCE_DH_NS 4
+#define VCE_DH_NS 2
 #endif
 #ifndef VCE_DH_SPREAD
-#define VCE_DH_SPREAD 1
+#define VCE_DH_SPREAD 0
 #endif
 #ifndef VCE_DW_RB
-#define VCE_DW_RB 64
+#define VCE_DW_RB 128
 #endif
 #ifndef VCE_DW_NS
-#define VCE_DW_NS 4
+#define VCE_DW_NS 2
 #endif
 #ifndef VCE_DW_SPREAD
 #define VCE_DW_SPREAD 0
