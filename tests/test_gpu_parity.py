@@ -109,6 +109,10 @@ RAGGED = [
     # the first chunk's planes wait for the one addition after it
     (512, 256, 4200, 8192, 2, "bf16"),
     (300, 128, 6000, 8192, 2, "f32"),
+    # several tiles and 64-K slices in every GEMM, each with a partial last
+    # one: K tails of 8 (H) and 9 or 12 (T, dW's K) on the 16x16x32 blocks
+    (777, 200, 3000, 3008, 4, "bf16"),
+    (1100, 520, 9000, 9024, 3, "bf16"),
 ]
 
 
