@@ -16,8 +16,8 @@
 // accumulators are rearranged into the 32x32 layout before the epilogue;
 // their sums have come out bit-identical to the 32x32x16 ones, in less time
 // per flop). K
-// advances in slices of RB bytes per operand position (RB = 64: 32 bf16 or
-// 16 float), staged in LDS by direct global->LDS loads
+// advances in slices of RB bytes per operand position (RB = 128: 64 bf16 or
+// 32 float; 64 is supported too), staged in LDS by direct global->LDS loads
 // (global_load_lds_dwordx4), NS stages deep; both layouts fill one stage with
 // ROWS * RB bytes.
 //
@@ -362,7 +362,7 @@ struct StageKM {
   static constexpr int kReads = ES == 2 ? 2 : 4;
   static_assert(1024 % RBT == 0 && RBT >= 256, "row size");
   static_assert(BK % (RPL * NW) == 0 && Q >= 1, "load split");
-  // the chunk permutation repeats every 4 (bf16) / 8 (float) rows: when the
+  // the chunk permutation repeats every 16 (bf16) / 8 (float) rows: when the
   // rows of consecutive loads step by a multiple of that, a lane's chunk is
   // the same for every load
   static constexpr bool kQIndep = (RPL * NW) % (ES == 2 ? 16 : 8) == 0;
