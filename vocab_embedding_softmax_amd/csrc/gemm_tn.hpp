@@ -58,6 +58,17 @@
 #ifndef VCE_MFMA16
 #define VCE_MFMA16 1
 #endif
+// Direct-to-LDS copies of each slice (of 8 per wave) that the logit GEMMs
+// defer into the first MFMAs of the next slice: forward and argmax, G
+#ifndef VCE_DMA_DEFER
+#define VCE_DMA_DEFER 1
+#endif
+#ifndef VCE_DMA_DEFER_FWD
+#define VCE_DMA_DEFER_FWD 6
+#endif
+#ifndef VCE_DMA_DEFER_GRAD
+#define VCE_DMA_DEFER_GRAD 4
+#endif
 
 namespace vce {
 
@@ -889,16 +900,47 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) B16[b] = sb.frag16(st + A_BYTES, b, 0, lane);
     };
-    auto kstep16 = [&](int kt, auto wait_all, auto issue_next, auto last, auto all_fast) {
+    // The copies of one slice: in the logit GEMMs, LH of them go out among
+    // the MFMAs after the barrier that frees their stage (every other one)
+    // and the rest among the first MFMAs of the next slice, so that the
+    // workgroup's copies do not all enter the memory path at once.
+    constexpr int NDEF = !VCE_DMA_DEFER        ? 0
+                         : MODE == EPI_GRAD    ? VCE_DMA_DEFER_GRAD
+                         : MODE == EPI_STORE   ? 0
+                                               : VCE_DMA_DEFER_FWD;
+    constexpr bool DEFER = NDEF > 0;
+    constexpr int LH = LOADS - (NDEF < LOADS ? NDEF : LOADS);
+    static_assert(!DEFER || 2 * (LOADS - LH) <= MA * NB, "deferred copies fit the first sub-step");
+    auto issue_one = [&](auto kk, int kn, auto af) {
+      constexpr int k = decltype(kk)::value;
+      const int64_t kofs = static_cast<int64_t>(kn) * BK;
+      const uint32_t stl = smem_lds + (kn % NS) * STAGE;
+      const int64_t kleft = klen - kofs;
+      if constexpr (k < SA::Q)
+        sa.issue_q(k, stl, Ab + kofs * (AKM ? g.lda : 1) * ES, kleft, wave,
+                   decltype(af)::value || sa.fast(kleft));
+      else
+        sb.issue_q(k - SA::Q, stl + A_BYTES, Bb + kofs * (BKM ? g.ldb : 1) * ES, kleft, wave,
+                   decltype(af)::value || sb.fast(kleft));
+    };
+    auto kstep16 = [&](int kt, auto wait_all, auto issue_next, auto last, auto all_fast,
+                       auto defer_in) {
       constexpr bool WAIT_ALL = decltype(wait_all)::value;
       constexpr bool ISSUE = decltype(issue_next)::value;
       constexpr bool LAST = decltype(last)::value;
       constexpr bool AF = decltype(all_fast)::value;
+      constexpr bool DIN = DEFER && decltype(defer_in)::value;
       const char* st = smem + (kt % NS) * STAGE;
       auto none = [] {};
       auto nodma = [](auto) {};
+      // the second half of slice kt+1's copies, when the previous step left it
+      auto dma0 = [&](auto slot) {
+        constexpr int s = decltype(slot)::value;
+        if constexpr (DIN && s % 2 == 0 && s / 2 < LOADS - LH)  // every other MFMA
+          issue_one(std::integral_constant<int, LH + s / 2>{}, kt + NS - 1, all_fast);
+      };
       // first sub-step; its last groups read the second's first fragments
-      sub16(st, 0, st, 1, std::true_type{}, none, nodma);
+      sub16(st, 0, st, 1, std::true_type{}, none, dma0);
       if constexpr (!LAST) {
         const char* stn = smem + ((kt + 1) % NS) * STAGE;
         const char *pa = nullptr, *pb = nullptr;
@@ -927,7 +969,14 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
         };
         auto dma = [&](auto slot) {
           constexpr int k = decltype(slot)::value - (MA - 2) * NB;
-          if constexpr (ISSUE && k >= 0 && k < LOADS) {
+          if constexpr (DEFER) {
+            // load j before MFMA j * 2 NB / LH of the last two groups
+            static_for<0, LH>([&](auto jj) {
+              constexpr int j = decltype(jj)::value;
+              if constexpr (ISSUE && k == j * 2 * NB / LH)
+                issue_one(std::integral_constant<int, j>{}, kt + NS, all_fast);
+            });
+          } else if constexpr (ISSUE && k >= 0 && k < LOADS) {
             if constexpr (k < SA::Q)
               sa.issue_q(k, stl, pa, kleft, wave, fast_a);
             else
@@ -939,9 +988,10 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
         sub16(st, 1, st, 0, std::false_type{}, none, nodma);
       }
     };
-    auto step = [&](int kt, auto wait_all, auto issue_next, auto last, auto all_fast) {
+    auto step = [&](int kt, auto wait_all, auto issue_next, auto last, auto all_fast,
+                    auto defer_in) {
       if constexpr (M16)
-        kstep16(kt, wait_all, issue_next, last, all_fast);
+        kstep16(kt, wait_all, issue_next, last, all_fast, defer_in);
       else
         kstep(kt, wait_all, issue_next, last, all_fast);
     };
@@ -968,17 +1018,34 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
         if constexpr (SPREAD) {
           // kstep(kt) queues slice kt+NS-1; at its barrier the slices after
           // kt+1 that are in flight are kt+2 .. kt+NS-1
-          for (; kt + NS - 1 < nk; ++kt) step(kt, F_{}, T_{}, F_{}, af);
-          for (; kt + 1 < nk; ++kt) step(kt, T_{}, F_{}, F_{}, af);
-        } else {
-          for (; kt + NS < nk; ++kt) step(kt, F_{}, T_{}, F_{}, af);
-          if (kt + NS == nk && kt + 1 < nk) {
-            step(kt, F_{}, F_{}, F_{}, af);
+          for (; kt + NS - 1 < nk; ++kt) step(kt, F_{}, T_{}, F_{}, af, F_{});
+          for (; kt + 1 < nk; ++kt) step(kt, T_{}, F_{}, F_{}, af, F_{});
+          step(kt, T_{}, F_{}, T_{}, af, F_{});
+        } else if constexpr (M16 && DEFER) {
+          // two stages: a step after one that queued copies issues their
+          // second half (slice 1 was queued whole before the loop)
+          static_assert(NS == 2, "deferred copies assume two stages");
+          if (kt + NS < nk) {
+            step(kt, F_{}, T_{}, F_{}, af, F_{});
+            for (++kt; kt + NS < nk; ++kt) step(kt, F_{}, T_{}, F_{}, af, T_{});
+            if (kt + 1 < nk) {  // kt + NS == nk
+              step(kt, F_{}, F_{}, F_{}, af, T_{});
+              ++kt;
+            }
+          } else if (kt + 1 < nk) {  // nk == 2
+            step(kt, F_{}, F_{}, F_{}, af, F_{});
             ++kt;
           }
-          for (; kt + 1 < nk; ++kt) step(kt, T_{}, F_{}, F_{}, af);
+          step(kt, T_{}, F_{}, T_{}, af, F_{});
+        } else {
+          for (; kt + NS < nk; ++kt) step(kt, F_{}, T_{}, F_{}, af, F_{});
+          if (kt + NS == nk && kt + 1 < nk) {
+            step(kt, F_{}, F_{}, F_{}, af, F_{});
+            ++kt;
+          }
+          for (; kt + 1 < nk; ++kt) step(kt, T_{}, F_{}, F_{}, af, F_{});
+          step(kt, T_{}, F_{}, T_{}, af, F_{});
         }
-        step(kt, T_{}, F_{}, T_{}, af);
       };
 #if VCE_KLOOP_SPLIT
       // whole tiles (the common case) run a K loop without per-load tests
