@@ -238,13 +238,18 @@ def test_workspace_queries_are_deterministic_and_reject_bad_shapes():
     b = lib.vce_bwd_workspace_bytes(8192, 3072, 201088, 201088, 8, 1)
     # one chunk of G (four shards: 100544 columns) is staged, never [T, V]; the dh
     # GEMM's 32 x 12 tiles fill 1.5 rounds of 256 CUs, so its K is split in two
-    # and one float32 partial plane [T, H] is kept
-    assert a == b == 8192 * 100544 * 2 + 8192 * 3072 * 4
-    # one shard of 201088 rows: two tile-aligned pieces of 100608 rows
+    # and one float32 partial plane [T, H] is kept; the dW GEMM's 393 x 12 tiles
+    # fill 18 rounds and 108 tiles: rows past 384 tiles (2240 of them) run as a
+    # second launch with K split in two, and one plane of those rows is kept
+    assert a == b == 8192 * 100544 * 2 + 8192 * 3072 * 4 + 2240 * 3072 * 4
+    # one shard of 201088 rows: two tile-aligned pieces of 100608 rows (393
+    # tiles, a tail of 2304 rows)
     assert lib.vce_bwd_workspace_bytes(8192, 3072, 201088, 201088, 1, 1) == \
-        8192 * 100608 * 2 + 8192 * 3072 * 4
-    # 16384 tokens: 64 x 12 dh tiles are three full rounds, no split, G only
-    assert lib.vce_bwd_workspace_bytes(16384, 3072, 201088, 201088, 8, 1) == 16384 * 100544 * 2
+        8192 * 100608 * 2 + 8192 * 3072 * 4 + 2304 * 3072 * 4
+    # 16384 tokens: 64 x 12 dh tiles are three full rounds, no split; G and the
+    # dW tail's plane
+    assert lib.vce_bwd_workspace_bytes(16384, 3072, 201088, 201088, 8, 1) == \
+        16384 * 100544 * 2 + 2240 * 3072 * 4
     # sampled-softmax shape (P = 16384 rows, H = 1536): chunks of 8192 rows; dh
     # (64 x 6 tiles) split in two; dW (32 x 6 tiles, K = 16384) not split: one
     # round of long tiles costs about what four short rounds plus three planes do

@@ -129,6 +129,38 @@ def test_ragged_shapes(V, T, H, Vr, Vp, n, dt):
     check_ce(g, ref, dt, Vr)
 
 
+def test_dw_tail_split(V):
+    # one shard of 33792 rows in two chunks of 16896 (66 x 4 dW tiles over
+    # K = 2048 tokens: one round of 256 and 8 more): rows past 64 tiles run as
+    # a second launch with K split in two; the second chunk's tail holds the
+    # last 212 real classes and all 300 padding rows
+    T, H, Vr, Vp = 2048, 1024, 33492, 33792
+    say(f"case dW tail split T={T} H={H} V_real={Vr} V_pad={Vp}")
+    inp = make_ce_inputs(T, H, Vr, Vp, 1, "bf16", seed=4242, ignore_frac=0.05,
+                         pad_fill=float("nan"))
+    inp.targets[:64] = np.arange(Vr - 64, Vr)       # targets in the padded tail
+    inp.targets[64:128] = np.arange(16384, 16448)   # and in the first chunk's tail
+    g = gpu_ce(V, inp)
+    ref = oracle_ce(inp)
+    check_ce(g, ref, "bf16", Vr)
+    # accumulating adds the same result (split 0 into dW, split 1 through its
+    # plane) and leaves the padding rows alone
+    dev = "cuda"
+    h = V.from_bits(inp.h, inp.dtype, dev)
+    W = V.from_bits(inp.W, inp.dtype, dev)
+    tg = torch.from_numpy(inp.targets).to(dev)
+    gl = torch.ones(1, dtype=torch.float32, device=dev)
+    f = V.vce_fwd(h, W, tg, Vr, 1, inp.ignore_index, allow_bad=True)
+    dW = torch.from_numpy(g["dW"]).to(dev)
+    dW[Vr:] = 7.0
+    V.vce_bwd(h, W, tg, f.lse, gl, f.n_valid, Vr, 1, inp.ignore_index, V.REDUCE_MEAN, dW=dW,
+              accumulate_dW=True)
+    torch.cuda.synchronize()
+    d2 = dW.cpu().numpy()
+    assert rel_l2(d2[:Vr], 2.0 * g["dW"][:Vr].astype(np.float64)) <= 1e-6
+    assert (d2[Vr:] == 7.0).all()
+
+
 def test_zero_tokens(V):
     say("case T=0")
     inp = make_ce_inputs(0, 64, 100, 128, 2, "bf16", seed=1)

@@ -142,6 +142,30 @@ int32_t k_splits_for(int64_t tiles, int64_t K, int64_t out_elems) {
   return best;
 }
 
+TailSplit tail_split_for(int64_t rows, int64_t tiles_n, int64_t K, int64_t n_cols) {
+  constexpr int64_t kCUs = 256;
+  const int64_t tiles_m = cdiv(rows, kTileM);
+  TailSplit best{rows, 1};
+  if (tiles_m <= 0 || tiles_n <= 0 || (tiles_m * tiles_n) % kCUs == 0) return best;
+  // the most whole rows of tiles that fill whole rounds
+  int64_t m1 = tiles_m;
+  while (m1 > 0 && (m1 * tiles_n) % kCUs != 0) --m1;
+  if (m1 == 0) return best;
+  const int64_t rest = (tiles_m - m1) * tiles_n;  // tiles of the last, partial round
+  // as many parts as fill one round, each at least 1024 K positions
+  const int32_t ks = static_cast<int32_t>(min(kCUs / rest, max(K / 1024, int64_t{1})));
+  if (ks < 2) return best;
+  // units of one 64-K slice of one tile, as in k_splits_for
+  const double slices = static_cast<double>(cdiv(K, 64));
+  const double whole = static_cast<double>(cdiv(tiles_m * tiles_n, kCUs)) * (slices + 4.0);
+  const double tail_rows = static_cast<double>(rows - m1 * kTileM);
+  const double split = static_cast<double>(m1 * tiles_n / kCUs) * (slices + 4.0) +
+                       static_cast<double>(cdiv(K, ks * 64) + 4) +
+                       tail_rows * static_cast<double>(n_cols) * 4.0 * (2.0 * ks) / 8.25e6 + 6.0;
+  if (split < whole * 0.99) best = TailSplit{m1 * kTileM, ks};
+  return best;
+}
+
 BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n, size_t esize,
                  void* ws) {
   (void)V_real;
@@ -178,6 +202,10 @@ BwdPlan plan_bwd(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t n,
   p.G = c.take<char>(static_cast<size_t>(T * p.ldC) * esize);
   p.Pdh = c.take<float>(static_cast<size_t>((p.split_dh - 1) * T * H));
   p.Pdw = c.take<float>(static_cast<size_t>((p.split_dw - 1) * p.chunk_rows * H));
+  p.dw_tail = p.split_dw == 1 ? tail_split_for(p.chunk_rows, tiles_h, T, H)
+                              : TailSplit{p.chunk_rows, 1};
+  p.Pdw_tail = c.take<float>(
+      static_cast<size_t>((p.dw_tail.ks - 1) * (p.chunk_rows - p.dw_tail.m1) * H));
   p.bytes = c.used;
   return p;
 }
@@ -637,32 +665,48 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
     }
     if ((err = mark()) != hipSuccess) return err;
     // 3. dW rows [c0, c1) = G^T h  (K = tokens; G and h read K-major);
-    //    rows of padding classes receive 0 (or are left alone when accumulating)
-    {
+    //    rows of padding classes receive 0 (or are left alone when accumulating).
+    //    Rows [r0, r1) of the chunk in one launch of ks K splits, planes at P.
+    auto dw_rows = [&](int64_t r0, int64_t r1, int32_t ks, float* P) -> hipError_t {
       GemmShape g{};
-      g.A = Gc;
+      g.A = Gc + r0;
       g.lda = p.ldC;
       g.B = h;
       g.ldb = H;
-      g.seg = one_segment(Vc);
-      g.m_total = Vc;
-      g.m_load_end = Vc;
+      g.seg = one_segment(r1 - r0);
+      g.m_total = r1 - r0;
+      g.m_load_end = r1 - r0;
       g.n_total = H;
       g.tiles_n = static_cast<int32_t>(cdiv(H, kTileN));
-      const int32_t ks = min(k_splits_for(cdiv(Vc, kTileM) * g.tiles_n, T, Vc * H), p.split_dw);
       g.k_splits = ks;
       g.k_total = T;
       g.k_per_split = round_up(cdiv(T, ks), kPadK);
       g.group_m = kGroupM;
       EpiArgs e{};
-      e.store.C = dW + c0 * H;
+      e.store.C = dW + (c0 + r0) * H;
       e.store.ldc = H;
-      e.store.P = p.Pdw;
-      e.store.split_stride = Vc * H;
+      e.store.P = P;
+      e.store.split_stride = (r1 - r0) * H;
       e.store.accumulate = acc_dw ? 1 : 0;
-      e.store.m_zero_from = kreal;
-      if ((err = launch_gemm<E, EPI_STORE, true, true>(g, e, s)) != hipSuccess) return err;
-      if ((err = split_add(dW + c0 * H, p.Pdw, ks, Vc, kreal)) != hipSuccess) return err;
+      e.store.m_zero_from = max(kreal - r0, int64_t{0});
+      hipError_t er = launch_gemm<E, EPI_STORE, true, true>(g, e, s);
+      if (er != hipSuccess) return er;
+      return split_add(dW + (c0 + r0) * H, P, ks, r1 - r0, max(kreal - r0, int64_t{0}));
+    };
+    {
+      const int64_t tiles_h = cdiv(H, kTileN);
+      const int32_t ks = min(k_splits_for(cdiv(Vc, kTileM) * tiles_h, T, Vc * H), p.split_dw);
+      // the last partial round of an unsplit launch split in K, when the
+      // plane workspace planned for a whole chunk holds it
+      TailSplit ts{Vc, 1};
+      if (ks == 1 && p.dw_tail.ks > 1) {
+        ts = tail_split_for(Vc, tiles_h, T, H);
+        if (ts.ks > 1 && (ts.ks - 1) * (Vc - ts.m1) >
+                             (p.dw_tail.ks - 1) * (p.chunk_rows - p.dw_tail.m1))
+          ts = TailSplit{Vc, 1};
+      }
+      if ((err = dw_rows(0, ts.m1, ks, p.Pdw)) != hipSuccess) return err;
+      if (ts.m1 < Vc && (err = dw_rows(ts.m1, Vc, ts.ks, p.Pdw_tail)) != hipSuccess) return err;
     }
     if ((err = mark()) != hipSuccess) return err;
   }

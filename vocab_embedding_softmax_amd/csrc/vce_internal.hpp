@@ -133,6 +133,19 @@ ArgPlan plan_argmax(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t
 // Backward plan: the vocabulary is processed in chunks; only one chunk's
 // G = [T][chunk] is staged. A chunk is a group of whole shards, or a piece of
 // one shard when shards are larger than a chunk may be.
+// An unsplit GEMM whose tiles fill their last round of CUs only in part can
+// run as two launches: output rows [0, m1) unsplit, in whole rounds, and rows
+// [m1, rows) with K split in ks parts (planes added afterwards), so that the
+// last round's tiles take a fraction of a tile's time. ks == 1: one launch.
+struct TailSplit {
+  int64_t m1;
+  int32_t ks;
+};
+// The split of a GEMM of `rows` output rows (tiles of kTileM), tiles_n tiles
+// along N and K positions (n_cols float32 outputs per row), by the same
+// estimate as k_splits_for; {rows, 1} when it saves less than 1 %.
+TailSplit tail_split_for(int64_t rows, int64_t tiles_n, int64_t K, int64_t n_cols);
+
 struct BwdPlan {
   int64_t S;                 // rows per shard
   int64_t n;                 // shards
@@ -148,6 +161,8 @@ struct BwdPlan {
   int32_t split_dw;          // most K splits of the dW GEMM
   float* Pdh;                // [split_dh - 1][T][H] partial planes
   float* Pdw;                // [split_dw - 1][chunk_rows][H]
+  TailSplit dw_tail;         // split of the unsplit dW GEMM's last round (chunk_rows rows)
+  float* Pdw_tail;           // [dw_tail.ks - 1][chunk_rows - dw_tail.m1][H]
   size_t bytes;
   void chunk(int64_t c, int64_t& c0, int64_t& c1) const {
     if (group > 0) {
