@@ -246,6 +246,11 @@ def test_workspace_queries_are_deterministic_and_reject_bad_shapes():
     # tiles, a tail of 2304 rows)
     assert lib.vce_bwd_workspace_bytes(8192, 3072, 201088, 201088, 1, 1) == \
         8192 * 100608 * 2 + 8192 * 3072 * 4 + 2304 * 3072 * 4
+    # one shard's rows alone (25136): two pieces of 12800 rows; dW's 50 x 12
+    # tiles: the first 42 tile rows fill two rounds, the last 8 (2048 rows)
+    # run with K split in two
+    assert lib.vce_bwd_workspace_bytes(8192, 3072, 25136, 25136, 1, 1) == \
+        8192 * 12800 * 2 + 8192 * 3072 * 4 + 2048 * 3072 * 4
     # 16384 tokens: 64 x 12 dh tiles are three full rounds, no split; G and the
     # dW tail's plane
     assert lib.vce_bwd_workspace_bytes(16384, 3072, 201088, 201088, 8, 1) == \

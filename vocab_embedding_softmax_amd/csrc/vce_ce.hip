@@ -147,11 +147,10 @@ TailSplit tail_split_for(int64_t rows, int64_t tiles_n, int64_t K, int64_t n_col
   const int64_t tiles_m = cdiv(rows, kTileM);
   TailSplit best{rows, 1};
   if (tiles_m <= 0 || tiles_n <= 0 || (tiles_m * tiles_n) % kCUs == 0) return best;
-  // the most whole rows of tiles that fill whole rounds
-  int64_t m1 = tiles_m;
-  while (m1 > 0 && (m1 * tiles_n) % kCUs != 0) --m1;
-  if (m1 == 0) return best;
-  const int64_t rest = (tiles_m - m1) * tiles_n;  // tiles of the last, partial round
+  // the most whole rows of tiles that fit in the whole rounds
+  const int64_t m1 = (tiles_m * tiles_n / kCUs) * kCUs / tiles_n;
+  if (m1 == 0 || m1 == tiles_m) return best;
+  const int64_t rest = (tiles_m - m1) * tiles_n;  // tiles left for the last round
   // as many parts as fill one round, each at least 1024 K positions
   const int32_t ks = static_cast<int32_t>(min(kCUs / rest, max(K / 1024, int64_t{1})));
   if (ks < 2) return best;
@@ -159,7 +158,7 @@ TailSplit tail_split_for(int64_t rows, int64_t tiles_n, int64_t K, int64_t n_col
   const double slices = static_cast<double>(cdiv(K, 64));
   const double whole = static_cast<double>(cdiv(tiles_m * tiles_n, kCUs)) * (slices + 4.0);
   const double tail_rows = static_cast<double>(rows - m1 * kTileM);
-  const double split = static_cast<double>(m1 * tiles_n / kCUs) * (slices + 4.0) +
+  const double split = static_cast<double>(cdiv(m1 * tiles_n, kCUs)) * (slices + 4.0) +
                        static_cast<double>(cdiv(K, ks * 64) + 4) +
                        tail_rows * static_cast<double>(n_cols) * 4.0 * (2.0 * ks) / 8.25e6 + 6.0;
   if (split < whole * 0.99) best = TailSplit{m1 * kTileM, ks};

@@ -134,9 +134,10 @@ ArgPlan plan_argmax(int64_t T, int64_t H, int64_t V_real, int64_t V_pad, int32_t
 // G = [T][chunk] is staged. A chunk is a group of whole shards, or a piece of
 // one shard when shards are larger than a chunk may be.
 // An unsplit GEMM whose tiles fill their last round of CUs only in part can
-// run as two launches: output rows [0, m1) unsplit, in whole rounds, and rows
-// [m1, rows) with K split in ks parts (planes added afterwards), so that the
-// last round's tiles take a fraction of a tile's time. ks == 1: one launch.
+// run as two launches: output rows [0, m1) unsplit (the most whole rows of
+// tiles that fit in the whole rounds), and rows [m1, rows) with K split in ks
+// parts (planes added afterwards), so that the last round's tiles take a
+// fraction of a tile's time. ks == 1: one launch.
 struct TailSplit {
   int64_t m1;
   int32_t ks;
