@@ -446,7 +446,8 @@ def main():
                  n_chunks),
         "dh": (f"k_gemm_tn<bf16,EPI_STORE,KC,KM> (dh += G_chunk W_chunk, {n_chunks} launches)",
                phase["vce_bwd.dh"], n_chunks),
-        "dw": (f"k_gemm_tn<bf16,EPI_STORE,KM,KM> (dW_chunk = G_chunk^T h, {n_chunks} launches)",
+        "dw": (f"k_gemm_tn<bf16,EPI_STORE,KM,KM> (dW_chunk = G_chunk^T h, {n_chunks} chunks: per "
+               f"chunk the rows of the whole rounds of tiles in one launch, any rest in a K-split one)",
                phase["vce_bwd.dW"], n_chunks),
     }
     dom_tag = max(gemms, key=lambda k: gemms[k][1])
