@@ -69,11 +69,15 @@ GEMM_SOURCES = ("gemm_tn.hpp", "vce_ce.hip", "vce_device.hpp", "vce_internal.hpp
 
 
 def kernel_source_hash() -> str:
+    """Hash of the GEMM kernels' code: comments (from // to the end of a line)
+    and blank lines are left out, so that a comment edit keeps counters taken
+    on the same compiled kernels valid."""
     h = hashlib.sha256()
     for name in GEMM_SOURCES:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            code = [line.split("//", 1)[0].rstrip() for line in f]
+        h.update(name.encode())
+        h.update("\n".join(line for line in code if line).encode())
     return h.hexdigest()[:16]
 
 

@@ -873,7 +873,8 @@ void k_gemm_tn(GemmShape g, EpiArgs e) {
     // again for the next sub-step right after its last MFMA (in the last
     // group). In a slice's second sub-step the reads of the next slice start
     // at group MA-2, so slice kt+1's wait and barrier sit there (mid), and the
-    // copies of slice kt+NS go out among the last two groups' MFMAs (dma).
+    // copies of slice kt+NS go out among the last two groups' MFMAs (dma) or,
+    // those the logit GEMMs defer, among the next slice's first MFMAs (dma0).
     auto sub16 = [&](const char* stc, int sc, const char* stx, int sx, auto next, auto mid,
                      auto dma) {
       constexpr bool NX = decltype(next)::value;
