@@ -129,20 +129,21 @@ def test_ragged_shapes(V, T, H, Vr, Vp, n, dt):
     check_ce(g, ref, dt, Vr)
 
 
-def test_dw_tail_split(V):
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_dw_tail_split(V, dt):
     # one shard of 33792 rows in two chunks of 16896 (66 x 4 dW tiles over
     # K = 2048 tokens: one round of 256 and 8 more): rows past 64 tiles run as
     # a second launch with K split in two; the second chunk's tail holds the
     # last 212 real classes and all 300 padding rows
     T, H, Vr, Vp = 2048, 1024, 33492, 33792
-    say(f"case dW tail split T={T} H={H} V_real={Vr} V_pad={Vp}")
-    inp = make_ce_inputs(T, H, Vr, Vp, 1, "bf16", seed=4242, ignore_frac=0.05,
+    say(f"case dW tail split T={T} H={H} V_real={Vr} V_pad={Vp} {dt}")
+    inp = make_ce_inputs(T, H, Vr, Vp, 1, dt, seed=4242, ignore_frac=0.05,
                          pad_fill=float("nan"))
     inp.targets[:64] = np.arange(Vr - 64, Vr)       # targets in the padded tail
     inp.targets[64:128] = np.arange(16384, 16448)   # and in the first chunk's tail
     g = gpu_ce(V, inp)
     ref = oracle_ce(inp)
-    check_ce(g, ref, "bf16", Vr)
+    check_ce(g, ref, dt, Vr)
     # accumulating adds the same result (split 0 into dW, split 1 through its
     # plane) and leaves the padding rows alone
     dev = "cuda"
