@@ -134,10 +134,13 @@ vce_status vce_fwd(const void* h, const void* W, const int32_t* targets,
  * chunk ([T][chunk], never [T][V]) is staged in the workspace in the input  *
  * element type (bf16 rounded to nearest-even, or float32), then dh receives *
  * G_chunk W_chunk (in chunk order) and the chunk's rows of dW receive       *
- * G_chunk^T h. When the tiles of the dh or dW product would leave CUs idle  *
- * (less than 85 % of 256-CU rounds filled) its K range is split in 2..8     *
- * parts: the later parts go to float32 partial planes in the workspace and  *
- * are added in a fixed order afterwards (results stay deterministic).       *
+ * G_chunk^T h. When the tiles of the dh or dW product would leave CUs idle, *
+ * its K range is split in 2..8 parts where that is estimated to save time   *
+ * (rounds of tiles over 256 CUs against the partial planes' traffic), or,   *
+ * for an unsplit dW, only the rows past its whole rounds of tiles are (a    *
+ * second launch): the later parts go to float32 partial planes in the       *
+ * workspace and are added in a fixed order afterwards (results stay         *
+ * deterministic).                                                           *
  * ------------------------------------------------------------------------ */
 size_t vce_bwd_workspace_bytes(int64_t T, int64_t H, int64_t V_real, int64_t V_pad,
                                int32_t num_shards, vce_dtype dt);
