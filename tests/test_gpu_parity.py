@@ -129,18 +129,24 @@ def test_ragged_shapes(V, T, H, Vr, Vp, n, dt):
     check_ce(g, ref, dt, Vr)
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_dw_tail_split(V, dt):
+@pytest.mark.parametrize("T,H,Vr,Vp,tail0,dt", [
     # one shard of 33792 rows in two chunks of 16896 (66 x 4 dW tiles over
     # K = 2048 tokens: one round of 256 and 8 more): rows past 64 tiles run as
     # a second launch with K split in two; the second chunk's tail holds the
     # last 212 real classes and all 300 padding rows
-    T, H, Vr, Vp = 2048, 1024, 33492, 33792
+    (2048, 1024, 33492, 33792, 16384, "bf16"),
+    (2048, 1024, 33492, 33792, 16384, "f32"),
+    # two chunks of 25600 rows (100 x 3 tiles over K = 4096): the first 85
+    # tile rows fill one round but one CU, the last 15 (3840 rows) run with K
+    # split in four; 200 padding rows at the end
+    (4096, 768, 51000, 51200, 21760, "bf16"),
+])
+def test_dw_tail_split(V, T, H, Vr, Vp, tail0, dt):
     say(f"case dW tail split T={T} H={H} V_real={Vr} V_pad={Vp} {dt}")
-    inp = make_ce_inputs(T, H, Vr, Vp, 1, dt, seed=4242, ignore_frac=0.05,
+    inp = make_ce_inputs(T, H, Vr, Vp, 1, dt, seed=4242 + H, ignore_frac=0.05,
                          pad_fill=float("nan"))
-    inp.targets[:64] = np.arange(Vr - 64, Vr)       # targets in the padded tail
-    inp.targets[64:128] = np.arange(16384, 16448)   # and in the first chunk's tail
+    inp.targets[:64] = np.arange(Vr - 64, Vr)            # targets in the padded tail
+    inp.targets[64:128] = np.arange(tail0, tail0 + 64)   # and in the first chunk's tail
     g = gpu_ce(V, inp)
     ref = oracle_ce(inp)
     check_ce(g, ref, dt, Vr)
