@@ -646,7 +646,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       g.k_splits = ks;
       g.k_total = kreal;
       g.k_per_split = round_up(cdiv(kreal, ks), kPadK);
-      g.group_m = kGroupM;
+      g.group_m = kGroupMdh;
       EpiArgs e{};
       e.store.C = dh;
       e.store.ldc = H;
@@ -680,7 +680,7 @@ static hipError_t ce_bwd_impl(const void* h, const void* W, const int32_t* targe
       g.k_splits = ks;
       g.k_total = T;
       g.k_per_split = round_up(cdiv(T, ks), kPadK);
-      g.group_m = kGroupM;
+      g.group_m = kGroupMdw;
       EpiArgs e{};
       e.store.C = dW + (c0 + r0) * H;
       e.store.ldc = H;

@@ -71,9 +71,22 @@ constexpr int kOcc = VCE_OCC;       // workgroups resident per CU (waves per SIM
 #define VCE_DW_SPREAD 0
 #endif
 constexpr int kChunkRows = VCE_CHUNK_ROWS;  // most vocabulary rows of one backward chunk
-// Tiles along M that one XCD's 32 workgroups walk together (4 x 8 tiles per
-// round): measured 1-2 % faster than 8 x 4 or 2 x 16 on every GEMM of the path.
-constexpr int kGroupM = 4;
+// Tiles along M that one XCD's 32 workgroups walk together: 4 (4 x 8 tiles
+// per round) for the logit GEMMs, 1.5-3 % faster than 2 or 8 there; the dh
+// GEMM (T x H tiles) runs 2 % faster with 1 and the dW GEMM (vocabulary x H)
+// 1 % faster with 2 than with 4.
+#ifndef VCE_GROUP_M
+#define VCE_GROUP_M 4
+#endif
+#ifndef VCE_GROUP_M_DH
+#define VCE_GROUP_M_DH 1
+#endif
+#ifndef VCE_GROUP_M_DW
+#define VCE_GROUP_M_DW 2
+#endif
+constexpr int kGroupM = VCE_GROUP_M;
+constexpr int kGroupMdh = VCE_GROUP_M_DH;
+constexpr int kGroupMdw = VCE_GROUP_M_DW;
 constexpr int kWavesM = VCE_WAVES_M;  // waves per workgroup along M
 constexpr int kWavesN = VCE_WAVES_N;  // waves per workgroup along N
 constexpr int kPadK = 64;     // staged operands are padded to this many K elements
